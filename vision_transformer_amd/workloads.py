@@ -1,0 +1,326 @@
+"""Encoder configurations and seeded synthetic inputs.
+
+This module is shared by the HIP path's tests/benchmark and by the CPU oracle's
+tests.  It holds no step of the encoder's arithmetic: only shapes, random
+draws, the bf16 storage rounding of the drawn weights, and the construction of
+the position *table* that the sincos2d family receives as an input (that table
+is a converter-side product, not a step of the encoder forward; see
+jepa.cpp "GGUF schema (v1)", section "Encoder tensors", and jepa.cpp
+"Converter", section "common.py").
+
+Workload shapes follow the five encoder families described on the pages:
+hfvit ViT-Ti/14 (jepa.cpp "GGUF schema (v1)", family note "hfvit" / "lewm"),
+I-JEPA ViT-L/16 (family "ijepa"), V-JEPA 2 ViT-L video (jepa.cpp
+"Architecture", family matrix "vjepa2"), V-JEPA 2.1 ViT-g video ("vjepa2_1")
+and LeVJEPA ViT-L block-causal video (family note "levjepa").
+
+Draw order for one config (seed = 1000 + config index):
+  1. pixels  [B, C, T, H, W] fp32 ~ N(0, 1)
+  2. patch_w [D, C*t*P*P], patch_b [D]                 ~ N(0, std_w)
+  3. pos table (learned: N(0, std_w); sincos2d: deterministic), cls [D],
+     mod [D], in that order, each only when the config has it
+  4. per block: qkv_w, qkv_b, out_w, out_b, up_w, up_b, down_w, down_b,
+     then ls1, ls2 when layer_scale is set (N(1, 0.1));
+     LayerNorm gamma = 1, beta = 0 (no draw)
+  5. final norm gamma = 1, beta = 0 (no draw)
+Because blocks are drawn in order, a config truncated to its first k layers
+receives exactly the first k blocks of the full config.
+
+Matrices of bf16/f16 configs are rounded to that type with round-to-nearest-
+even; the rounded values (held exactly in fp32) are what both the GPU and the
+oracle consume.  Vectors, norms and tables stay fp32.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+
+DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
+POS_NONE, POS_TABLE = 0, 1
+ROPE_NONE, ROPE_3D = 0, 1
+LAYOUT_TILED, LAYOUT_INTERLEAVED = 0, 1
+ATTN_FULL, ATTN_BLOCK_CAUSAL = 0, 1
+
+
+@dataclass
+class EncoderConfig:
+    """Hyperparameters of one encoder plus the input clip geometry."""
+    name: str
+    embed_dim: int
+    n_layer: int
+    n_head: int
+    ffn_dim: int
+    patch_size: int
+    tubelet_size: int
+    in_chans: int = 3
+    ln_eps: float = 1e-6
+    rope_theta: float = 10000.0
+    pos_type: int = POS_NONE
+    pos_kind: str = ""            # "learned" | "sincos2d" (table contents only)
+    rope: int = ROPE_NONE
+    rope_layout: int = LAYOUT_TILED
+    rope_interpolate: int = 0
+    rope_ref_grid: int = 0
+    cls_token: int = 0
+    modality_embed: int = 0
+    layer_scale: int = 0
+    attn_mode: int = ATTN_FULL
+    dtype: int = DTYPE_BF16
+    # input geometry
+    batch: int = 1
+    frames: int = 1
+    height: int = 224
+    width: int = 224
+    # synthetic-value scales
+    std_w: float = 0.02
+    std_qk: Optional[float] = None   # sensitised variants: std of the q and k rows of qkv_w
+    std_tok: Optional[float] = None  # sensitised variants: std of cls / mod vectors
+    seed: int = 1000
+
+    # ---- derived geometry -------------------------------------------------
+    @property
+    def head_dim(self) -> int:
+        return self.embed_dim // self.n_head
+
+    @property
+    def grid(self):
+        return (self.frames // self.tubelet_size, self.height // self.patch_size,
+                self.width // self.patch_size)
+
+    @property
+    def n_patches(self) -> int:
+        gt, gh, gw = self.grid
+        return gt * gh * gw
+
+    @property
+    def n_prefix(self) -> int:
+        return 1 if self.cls_token else 0
+
+    @property
+    def n_tokens(self) -> int:
+        return self.n_patches + self.n_prefix
+
+    @property
+    def patch_k(self) -> int:
+        return self.in_chans * self.tubelet_size * self.patch_size * self.patch_size
+
+    def replace(self, **kw) -> "EncoderConfig":
+        return dataclasses.replace(self, **kw)
+
+    def hparams(self) -> Dict[str, float]:
+        """The fields that form the library's hyperparameter struct."""
+        keys = ["embed_dim", "n_layer", "n_head", "ffn_dim", "patch_size", "tubelet_size",
+                "in_chans", "ln_eps", "rope_theta", "pos_type", "rope", "rope_layout",
+                "rope_interpolate", "rope_ref_grid", "cls_token", "modality_embed",
+                "layer_scale", "attn_mode", "dtype"]
+        return {k: getattr(self, k) for k in keys}
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs of one forward: 2*M*N*K per GEMM plus 4*D per
+        visible (query, key) pair per layer (softmax, LN, GELU not counted)."""
+        B, N, D, F, L = self.batch, self.n_tokens, self.embed_dim, self.ffn_dim, self.n_layer
+        Np = self.n_patches
+        f = 2.0 * B * Np * self.patch_k * D
+        M = B * N
+        f += L * 2.0 * M * D * (3 * D + D + 2 * F)
+        f += L * 4.0 * D * B * self.visible_pairs()
+        return f
+
+    def visible_pairs(self) -> int:
+        """Visible (query, key) pairs of one item's attention (closed form)."""
+        N = self.n_tokens
+        if self.attn_mode == ATTN_FULL:
+            return N * N
+        p = self.n_prefix
+        gt, gh, gw = self.grid
+        S = gh * gw
+        # prefix rows see all N keys; a patch query of frame f sees (f+1)*S patch keys
+        return p * N + S * S * sum(f + 1 for f in range(gt))
+
+
+def _configs() -> List[EncoderConfig]:
+    c1 = EncoderConfig(name="vit_ti14_hfvit_image", embed_dim=192, n_layer=12, n_head=3, ffn_dim=768,
+                       patch_size=14, tubelet_size=1, pos_type=POS_TABLE, pos_kind="learned",
+                       cls_token=1, dtype=DTYPE_F32, batch=1, frames=1, height=224, width=224,
+                       seed=1000)
+    c2 = EncoderConfig(name="vit_l16_ijepa_image", embed_dim=1024, n_layer=24, n_head=16, ffn_dim=4096,
+                       patch_size=16, tubelet_size=1, pos_type=POS_TABLE, pos_kind="sincos2d",
+                       dtype=DTYPE_BF16, batch=8, frames=1, height=224, width=224, seed=1001)
+    c3 = EncoderConfig(name="vjepa2_vit_l_video", embed_dim=1024, n_layer=24, n_head=16, ffn_dim=4096,
+                       patch_size=16, tubelet_size=2, rope=ROPE_3D, rope_layout=LAYOUT_TILED,
+                       dtype=DTYPE_BF16, batch=2, frames=16, height=256, width=256, seed=1002)
+    c4 = EncoderConfig(name="vjepa21_vit_g_video", embed_dim=1408, n_layer=40, n_head=22, ffn_dim=6144,
+                       patch_size=16, tubelet_size=2, rope=ROPE_3D, rope_layout=LAYOUT_INTERLEAVED,
+                       rope_interpolate=1, rope_ref_grid=256 // 16, modality_embed=1,
+                       dtype=DTYPE_BF16, batch=1, frames=64, height=384, width=384, seed=1003)
+    c5 = EncoderConfig(name="levjepa_vit_l_blockcausal", embed_dim=1024, n_layer=24, n_head=16,
+                       ffn_dim=4096, patch_size=16, tubelet_size=1, rope=ROPE_3D,
+                       rope_layout=LAYOUT_TILED, cls_token=1, attn_mode=ATTN_BLOCK_CAUSAL,
+                       dtype=DTYPE_BF16, batch=1, frames=16, height=256, width=256, seed=1004)
+    return [c1, c2, c3, c4, c5]
+
+
+CONFIGS: List[EncoderConfig] = _configs()
+BY_NAME: Dict[str, EncoderConfig] = {c.name: c for c in CONFIGS}
+# the headline workload: V-JEPA-2-style ViT-L video encoder, 2 clips x 2048 tokens
+HEADLINE = CONFIGS[2]
+
+
+def sensitised(cfg: EncoderConfig, std_qk: float = 0.2, std_tok: float = 1.0) -> EncoderConfig:
+    """Variant whose attention is far from uniform (large q/k rows) and whose
+    prefix / modality vectors are large, so that position, mask and token-
+    assembly mistakes become visible at the parity gates."""
+    return cfg.replace(name=cfg.name + "_sensitised", std_qk=std_qk, std_tok=std_tok)
+
+
+# ---------------------------------------------------------------------------
+# storage rounding (not a step of the method: it defines the weight values)
+# ---------------------------------------------------------------------------
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = np.isnan(x)
+    r = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantise(x: np.ndarray, dtype: int):
+    """Returns (storage array for the device, exact fp32 values)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == DTYPE_F32:
+        return x, x
+    if dtype == DTYPE_BF16:
+        b = round_bf16(x)
+        return b, bf16_bits_to_f32(b)
+    if dtype == DTYPE_F16:
+        h = x.astype(np.float16)
+        return h, h.astype(np.float32)
+    raise ValueError(dtype)
+
+
+def sincos2d_table(gh: int, gw: int, dim: int, w_first: bool = True) -> np.ndarray:
+    """2-D sine-cosine position table [gh*gw, dim] (the standard MAE-style
+    construction: dim/2 columns per axis, each [sin | cos] over dim/4
+    frequencies 10000^(-k/(dim/4))).  With w_first the w-axis half comes
+    first, as in the I-JEPA checkpoint table described on the schema page."""
+    assert dim % 4 == 0
+    q = dim // 4
+    omega = 1.0 / 10000.0 ** (np.arange(q, dtype=np.float64) / q)
+
+    def axis(pos):
+        a = np.outer(pos, omega)
+        return np.concatenate([np.sin(a), np.cos(a)], axis=1)
+
+    hh, ww = np.meshgrid(np.arange(gh, dtype=np.float64), np.arange(gw, dtype=np.float64),
+                         indexing="ij")
+    eh, ew = axis(hh.reshape(-1)), axis(ww.reshape(-1))
+    t = np.concatenate([ew, eh] if w_first else [eh, ew], axis=1)
+    return t.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# weights
+# ---------------------------------------------------------------------------
+@dataclass
+class Block:
+    qkv_w: np.ndarray
+    qkv_b: np.ndarray
+    out_w: np.ndarray
+    out_b: np.ndarray
+    up_w: np.ndarray
+    up_b: np.ndarray
+    down_w: np.ndarray
+    down_b: np.ndarray
+    ln1_w: np.ndarray
+    ln1_b: np.ndarray
+    ln2_w: np.ndarray
+    ln2_b: np.ndarray
+    ls1: Optional[np.ndarray] = None
+    ls2: Optional[np.ndarray] = None
+    # device storage of the matrices (bf16 bits / f16 / f32)
+    store: Dict[str, np.ndarray] = field(default_factory=dict)
+
+
+@dataclass
+class Weights:
+    patch_w: np.ndarray
+    patch_b: np.ndarray
+    pos: Optional[np.ndarray]
+    cls: Optional[np.ndarray]
+    mod: Optional[np.ndarray]
+    blocks: List[Block]
+    norm_w: np.ndarray
+    norm_b: np.ndarray
+    store: Dict[str, np.ndarray] = field(default_factory=dict)
+
+
+@dataclass
+class Workload:
+    cfg: EncoderConfig
+    pixels: np.ndarray        # fp32 [B, C, T, H, W]
+    weights: Weights
+
+
+def _normal(rng, shape, std):
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+
+
+def make_workload(cfg: EncoderConfig, seed: Optional[int] = None) -> Workload:
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    B, C, T, H, W = cfg.batch, cfg.in_chans, cfg.frames, cfg.height, cfg.width
+    D, F = cfg.embed_dim, cfg.ffn_dim
+    dt = cfg.dtype
+    pixels = rng.standard_normal((B, C, T, H, W), dtype=np.float32)
+
+    wstore = {}
+    pw_s, pw = quantise(_normal(rng, (D, cfg.patch_k), cfg.std_w), dt)
+    wstore["patch_w"] = pw_s
+    pb = _normal(rng, (D,), cfg.std_w)
+
+    pos = cls = mod = None
+    std_tok = cfg.std_w if cfg.std_tok is None else cfg.std_tok
+    if cfg.pos_type == POS_TABLE:
+        if cfg.pos_kind == "sincos2d":
+            gt, gh, gw = cfg.grid
+            assert gt == 1 and not cfg.cls_token
+            pos = sincos2d_table(gh, gw, D, w_first=True)
+        else:
+            pos = _normal(rng, (cfg.n_tokens, D), cfg.std_w)
+    if cfg.cls_token:
+        cls = _normal(rng, (D,), std_tok)
+    if cfg.modality_embed:
+        mod = _normal(rng, (D,), std_tok)
+
+    ones = np.ones(D, np.float32)
+    zeros = np.zeros(D, np.float32)
+    blocks = []
+    for _ in range(cfg.n_layer):
+        st = {}
+        qkv = _normal(rng, (3 * D, D), cfg.std_w)
+        if cfg.std_qk is not None:
+            qkv[: 2 * D] *= np.float32(cfg.std_qk / cfg.std_w)
+        st["qkv_w"], qkv_w = quantise(qkv, dt)
+        qkv_b = _normal(rng, (3 * D,), cfg.std_w)
+        st["out_w"], out_w = quantise(_normal(rng, (D, D), cfg.std_w), dt)
+        out_b = _normal(rng, (D,), cfg.std_w)
+        st["up_w"], up_w = quantise(_normal(rng, (F, D), cfg.std_w), dt)
+        up_b = _normal(rng, (F,), cfg.std_w)
+        st["down_w"], down_w = quantise(_normal(rng, (D, F), cfg.std_w), dt)
+        down_b = _normal(rng, (D,), cfg.std_w)
+        ls1 = ls2 = None
+        if cfg.layer_scale:
+            ls1 = (1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
+            ls2 = (1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32)
+        blocks.append(Block(qkv_w, qkv_b, out_w, out_b, up_w, up_b, down_w, down_b,
+                            ones, zeros, ones, zeros, ls1, ls2, st))
+    w = Weights(pw, pb, pos, cls, mod, blocks, ones, zeros, wstore)
+    return Workload(cfg, pixels, w)
