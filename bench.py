@@ -1,0 +1,217 @@
+"""Throughput of the ViT encoder forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu-baseline]
+
+A step is one vitenc_encode call over one batch: the V-JEPA-2-style ViT-L
+video encoder, 2 clips x 16 frames x 3 x 256 x 256 -> 2 x 2048 tokens, 24
+layers, bf16 with fp32 accumulation, synthetic seeded inputs resident in HBM.
+Prints one JSON line.  The roofline object is measured for the dominant
+kernel by timing its step entry point (the same kernel and launch
+configuration encode uses) with HIP events on the stream it is launched on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def time_region(fn, reps, stream):
+    """Average duration of fn() over reps calls, HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def kernel_breakdown(cfg, wl, enc, reps, stream):
+    """Each step kernel of one layer, timed alone at the encode shapes through
+    its C-ABI entry point.  Returns {name: (ms, flops, bytes)}."""
+    import torch
+    from vision_transformer_amd import vitenc as V
+    B, N, D, F, H = cfg.batch, cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim, cfg.n_head
+    hd = D // H
+    M = B * N
+    dt = cfg.dtype
+    td = V.torch_dtype(dt)
+    dev = "cuda"
+    blk = enc.blocks[0]
+    g = torch.Generator(device=dev).manual_seed(0)
+    Z = torch.randn((M, D), device=dev, generator=g)
+    Y = torch.randn((M, D), device=dev, generator=g).to(td)
+    O = torch.randn((M, D), device=dev, generator=g).to(td)
+    U = torch.randn((M, F), device=dev, generator=g).to(td)
+    Q, K, Vt = V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
+                             rope_layout=cfg.rope_layout, grid=cfg.grid, n_prefix=cfg.n_prefix)
+    tab = torch.empty(V.lib().vitenc_rope_table_floats(hd, *cfg.grid), dtype=torch.float32, device=dev)
+    Yo = torch.empty((M, D), device=dev, dtype=td)
+    Oo = torch.empty((M, D), device=dev, dtype=td)
+    Uo = torch.empty((M, F), device=dev, dtype=td)
+    torch.cuda.synchronize()
+    es = 2
+    pairs = cfg.visible_pairs() * B * H
+    res = {}
+    res["layernorm"] = (time_region(lambda: V.op_layernorm(Z, blk["ln1_w"], blk["ln1_b"], 1e-6, dt, out=Yo), reps, stream),
+                        0.0, M * D * (4 + es) + 8 * D)
+    res["qkv_gemm"] = (time_region(lambda: V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
+                                                         rope_layout=cfg.rope_layout, grid=cfg.grid,
+                                                         n_prefix=cfg.n_prefix, outs=(Q, K, Vt, tab)),
+                                           reps, stream),
+                       2.0 * M * D * 3 * D, (M * D + 3 * D * D + 3 * M * D) * es)
+    res["attention"] = (time_region(lambda: V.op_attention(dt, Q, K, Vt, cfg.attn_mode, cfg.n_prefix,
+                                                           cfg.grid[1] * cfg.grid[2], out=Oo), reps, stream),
+                        4.0 * hd * pairs, 4 * M * D * es)
+    res["out_gemm"] = (time_region(lambda: V.op_linear_residual(dt, O, blk["out_w"], blk["out_b"], Z), reps, stream),
+                       2.0 * M * D * D, (M * D + D * D) * es + 8 * M * D)
+    res["up_gemm"] = (time_region(lambda: V.op_linear_gelu(dt, Y, blk["up_w"], blk["up_b"], out=Uo), reps, stream),
+                      2.0 * M * D * F, (M * D + F * D + M * F) * es)
+    res["down_gemm"] = (time_region(lambda: V.op_linear_residual(dt, U, blk["down_w"], blk["down_b"], Z), reps,
+                                    stream), 2.0 * M * F * D, (M * F + D * F) * es + 8 * M * D)
+    return res
+
+
+def cpu_baseline(cfg, wl, layers=4):
+    """The oracle (unchanged, float64 numpy) on one clip and the first `layers`
+    layers, extrapolated to the full depth."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    one = cfg.replace(batch=1)
+    px = wl.pixels[:1]
+    t0 = time.perf_counter()
+    Z = oracle.embed(one, wl.weights, px)
+    t1 = time.perf_counter()
+    rope_pos, vis = oracle.rope_and_mask(one, px.shape)
+    for blk in wl.weights.blocks[:layers]:
+        Z = oracle.encoder_block(Z, blk, one, rope_pos, vis)
+    t2 = time.perf_counter()
+    out = oracle.layer_norm(Z, wl.weights.norm_w, wl.weights.norm_b, one.ln_eps)
+    t3 = time.perf_counter()
+    per_clip = (t1 - t0) + (t2 - t1) * cfg.n_layer / layers + (t3 - t2)
+    return {"value": round(one.n_tokens / per_clip, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 clip ({one.n_tokens} tokens), patch embed + {layers} of {cfg.n_layer} layers + final norm "
+                      f"timed ({t3 - t0:.1f} s), layer time scaled to {cfg.n_layer} layers"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(items are independent: N GPUs would each encode their own batch).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from vision_transformer_amd import vitenc as V
+    from vision_transformer_amd import workloads as W
+
+    cfg = W.HEADLINE
+    log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
+    wl = W.make_workload(cfg)
+    enc = V.Encoder.from_workload(wl)
+    px = torch.from_numpy(wl.pixels).cuda()
+    ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
+    stream = torch.cuda.current_stream()
+
+    step = lambda: enc.encode_into(px, ws, out, pooled, stream)
+    graph = None
+    if args.graph:
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            enc.encode_into(px, ws, out, pooled)
+        step = graph.replay
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup})")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = start.elapsed_time(end) / args.steps
+    tokens = cfg.batch * cfg.n_tokens
+    tflops = cfg.flops() / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step, {tokens / ms * 1e3:.0f} tokens/s, {tflops:.1f} TFLOP/s "
+        f"(wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
+
+    bd = kernel_breakdown(cfg, wl, enc, args.kernel_reps, stream)
+    per_layer = {k: v[0] for k, v in bd.items()}
+    log("[bench] per-kernel (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per_layer.items()))
+    # the dominant kernel over one forward (layernorm runs twice per layer)
+    weight = {"layernorm": 2}
+    dom = max(bd, key=lambda k: bd[k][0] * weight.get(k, 1))
+    d_ms, d_flops, d_bytes = bd[dom]
+    if d_flops > 0:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(d_flops / (d_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["avg_launch_ms"] = round(d_ms, 5)
+    roof["traffic"] = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline(cfg, wl)
+        log(f"[bench] cpu baseline {cpu}")
+
+    line = {
+        "metric": "encoder tokens/sec + MFMA TFLOP/s fraction of peak (ViT-L video, bf16, 1 GPU)",
+        "value": round(tokens / ms * 1e3, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) pixels, N(0,0.02) weights)",
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "config": {"workload": cfg.name, "global_batch": cfg.batch, "tokens_per_item": cfg.n_tokens,
+                   "embed_dim": cfg.embed_dim, "layers": cfg.n_layer, "heads": cfg.n_head,
+                   "graph": bool(args.graph)},
+        "kernels_ms_per_layer": {k: round(v, 5) for k, v in per_layer.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    enc.close()
+
+
+if __name__ == "__main__":
+    main()

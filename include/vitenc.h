@@ -1,0 +1,219 @@
+/*
+ * vitenc: the shared pre-LN ViT encoder forward on MI355X (gfx950).
+ *
+ * The operation is the encoder graph of jepa.cpp "Architecture", section
+ * "The shared ViT graph":
+ *
+ *   tokens = patch_embed(rearranged pixels) [+ pos] [+ cls] [+ modality vec]
+ *   per block:  x += ls1 * attn(ln1(x));  x += ls2 * ffn(ln2(x))
+ *   out = norm(x)
+ *
+ * with the hyperparameters and tensor layout of jepa.cpp "GGUF schema (v1)",
+ * sections "Encoder (jepa.enc.*)" and "Encoder tensors", the 3-D RoPE and
+ * block-causal mask of jepa.cpp "Architecture", sections "3-D RoPE" and
+ * "Block-causal attention", and the token order of "GGUF schema (v1)",
+ * section "Token order".
+ *
+ * Conventions for every entry point below:
+ *  - Every buffer pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronises device memory; work is enqueued
+ *    on the caller's stream (a hipStream_t passed as void*, NULL = the null
+ *    stream) and the call returns before it completes.
+ *  - Matrices are row-major (PyTorch layout); "[a, b]" means a rows of b
+ *    contiguous elements.  Matrices are in the model dtype; norms, biases,
+ *    layer scales, position tables and token vectors are always fp32 (the
+ *    schema page keeps every add/mul operand f32).
+ *  - Failures are refused, never clamped: a refusal returns a non-zero
+ *    vitenc_status before any device work is enqueued and sets a
+ *    thread-local message readable with vitenc_error_text().
+ *  - A model is immutable after creation; concurrent vitenc_encode calls on
+ *    one model are allowed when each uses its own workspace and outputs.
+ */
+#ifndef VITENC_H
+#define VITENC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VITENC_ABI_VERSION 1
+
+typedef enum {
+    VITENC_OK = 0,
+    VITENC_EINVAL = 1,       /* hyperparameter out of range or inconsistent */
+    VITENC_ESHAPE = 2,       /* an input shape this model cannot encode */
+    VITENC_ENULL = 3,        /* a required pointer is NULL */
+    VITENC_EWORKSPACE = 4,   /* workspace smaller than vitenc_workspace_size() */
+    VITENC_EDEVICE = 5,      /* the HIP runtime reported an error */
+    VITENC_EUNSUPPORTED = 6  /* well-formed but outside what the kernels implement */
+} vitenc_status;
+
+enum { VITENC_F32 = 0, VITENC_BF16 = 1, VITENC_F16 = 2 };             /* dtype */
+enum { VITENC_POS_NONE = 0, VITENC_POS_TABLE = 1 };                   /* pos_type */
+enum { VITENC_ROPE_NONE = 0, VITENC_ROPE_3D = 1 };                    /* rope */
+enum { VITENC_ROPE_TILED = 0, VITENC_ROPE_INTERLEAVED = 1 };          /* rope_layout */
+enum { VITENC_ATTN_FULL = 0, VITENC_ATTN_BLOCK_CAUSAL = 1 };          /* attn_mode */
+
+/* Encoder hyperparameters (jepa.cpp "GGUF schema (v1)", "Encoder (jepa.enc.*)").
+ *  embed_dim D, n_layer L, n_head H (head_dim = D / H), ffn_dim F,
+ *  patch_size P, tubelet_size t, in_chans C, ln_eps (1e-6 for every family),
+ *  rope_theta (10000).
+ *  pos_type TABLE: pos_embed has pos_rows rows [CLS?; patches]; the encoded
+ *    token count must equal pos_rows (no interpolation of the table).
+ *  rope ROPE_3D: 3-D RoPE on q and k of the patch tokens, d = 2*((hd/3)/2)
+ *    rotated dims per axis (t, h, w), rope_layout TILED or INTERLEAVED;
+ *    rope_interpolate rescales h and w by (rope_ref_grid - 1)/(grid - 1).
+ *  cls_token: a prepended CLS (no pos row unless the table has one, no RoPE).
+ *  modality_embed: mod_embed is added to every token.
+ *  layer_scale: ls1/ls2 multiply the attention and FFN branches.
+ *  attn_mode BLOCK_CAUSAL: key j visible to query i iff frame(i) >= frame(j);
+ *    the CLS row sees every key, no patch query sees the CLS key.
+ *  dtype: F32 (true fp32 arithmetic throughout), BF16 or F16 (matrices and
+ *    activations in that type, fp32 accumulation, fp32 residual stream). */
+typedef struct {
+    int32_t embed_dim, n_layer, n_head, ffn_dim;
+    int32_t patch_size, tubelet_size, in_chans;
+    float ln_eps, rope_theta;
+    int32_t pos_type, pos_rows;
+    int32_t rope, rope_layout, rope_interpolate, rope_ref_grid;
+    int32_t cls_token, modality_embed, layer_scale, attn_mode;
+    int32_t dtype;
+} vitenc_hparams;
+
+/* One encoder block ("GGUF schema (v1)", "Encoder tensors", enc.blk.{i}.*).
+ * Matrices in the model dtype: qkv_w [3D, D] with rows [q; k; v] and head h
+ * at rows [h*hd, (h+1)*hd) of each block; out_w [D, D]; up_w [F, D];
+ * down_w [D, F].  fp32 vectors: ln1_w/b, ln2_w/b [D], qkv_b [3D], out_b [D],
+ * up_b [F], down_b [D]; ls1/ls2 [D] required iff layer_scale, else ignored. */
+typedef struct {
+    const float *ln1_w, *ln1_b;
+    const void *qkv_w;   const float *qkv_b;
+    const void *out_w;   const float *out_b;
+    const float *ln2_w, *ln2_b;
+    const void *up_w;    const float *up_b;
+    const void *down_w;  const float *down_b;
+    const float *ls1, *ls2;
+} vitenc_block_weights;
+
+/* Encoder weights.  patch_w [D, C*t*P*P] (the strided convolution flattened in
+ * C-T-H-W order) in the model dtype; patch_b [D] fp32; pos_embed [pos_rows, D]
+ * fp32 iff pos_type TABLE; cls_token [D] fp32 iff cls_token; mod_embed [D]
+ * fp32 iff modality_embed; blocks: HOST array of n_layer entries (copied by
+ * vitenc_model_create; the device pointers inside are borrowed);
+ * norm_w/norm_b [D] fp32 (the final LayerNorm). */
+typedef struct {
+    const void *patch_w;  const float *patch_b;
+    const float *pos_embed, *cls_token, *mod_embed;
+    const vitenc_block_weights *blocks;
+    const float *norm_w, *norm_b;
+} vitenc_weights;
+
+typedef struct vitenc_model vitenc_model;
+
+/* Validates the hyperparameters and that every required pointer is set, then
+ * creates a model that borrows the device weights until vitenc_model_destroy.
+ * Refusals: EINVAL (ranges: embed_dim 1..65536, n_layer 1..1024, n_head
+ * 1..1024, ffn_dim 1..2^20, patch/tubelet/in_chans 1..1024, ln_eps in [0,1],
+ * rope_theta > 0 and finite; embed_dim % n_head; an odd head_dim with RoPE;
+ * rope_interpolate without rope_ref_grid; block_causal without RoPE; unknown
+ * enum values), ENULL (a required weight), EUNSUPPORTED (head_dim other than
+ * 64 or 32 is refused by the attention kernel; embed_dim above 4096). */
+vitenc_status vitenc_model_create(const vitenc_hparams *hp, const vitenc_weights *w,
+                                  vitenc_model **out);
+void vitenc_model_destroy(vitenc_model *m);
+
+/* Bytes of device workspace vitenc_encode needs for a [B, C, T, H, W] input.
+ * Refusals: ESHAPE (non-positive sizes, T % tubelet, H % P, W % P, more than
+ * 2^22 tokens per item, a pos table whose rows differ from the token count,
+ * block_causal with a single-frame grid is accepted). */
+vitenc_status vitenc_workspace_size(const vitenc_model *m, int32_t B, int32_t T, int32_t H,
+                                    int32_t W, size_t *bytes);
+
+/* Encodes B items.  pixels: fp32 [B, C, T, H, W] (NCTHW, already
+ * normalised).  out_tokens: fp32 [B, N, D], N = (CLS ? 1 : 0) + (T/t)(H/P)(W/P),
+ * the final-LayerNorm output.  out_pooled: NULL or fp32 [B, D]: the CLS row
+ * when the model has a CLS, else the mean of the patch rows.  workspace:
+ * ws_bytes >= vitenc_workspace_size() bytes, 256-byte aligned, contents
+ * undefined on entry and exit.  Asynchronous on `stream`; errors of the
+ * launches themselves are reported as EDEVICE. */
+vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t B, int32_t T,
+                            int32_t H, int32_t W, void *workspace, size_t ws_bytes,
+                            float *out_tokens, float *out_pooled, void *stream);
+
+/* Thread-local text of the last refusal on this thread ("" if none). */
+const char *vitenc_error_text(void);
+int32_t vitenc_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Step entry points: each runs one step of the encoder graph with the same
+ * kernels vitenc_encode uses, on caller buffers.  They exist so that every
+ * step can be checked on its own.  dtype is VITENC_F32/BF16/F16 and types
+ * every "T" buffer; the layouts named here are those of the encode path.
+ * ------------------------------------------------------------------------- */
+
+/* a1-a3 (jepa.cpp "Architecture", "The shared ViT graph": rearrange plus one
+ * matmul; "GGUF schema (v1)", "Token order"): pixels fp32 [B,C,T,H,W] ->
+ * Z fp32 [B, N, D] = [cls?; patches(pixels) W^T + b] (+ pos) (+ mod).
+ * scratch: T, at least B*Np*round_up(C*t*P*P, 8) elements.  pos (fp32
+ * [N, D]), cls, mod may be NULL (not applied). */
+vitenc_status vitenc_op_embed(int32_t dtype, const float *pixels, int32_t B, int32_t C,
+                              int32_t T, int32_t H, int32_t W, int32_t tubelet, int32_t patch,
+                              const void *patch_w, const float *patch_b, const float *pos,
+                              const float *cls, const float *mod, int32_t D, void *scratch,
+                              float *Z, void *stream);
+
+/* a4 LayerNorm ("GGUF schema (v1)", jepa.enc.ln_eps; centred two-pass
+ * variance, population, eps inside the root): x fp32 [M, D] -> y [M, D] of
+ * type out_dtype (VITENC_F32 for the final norm). */
+vitenc_status vitenc_op_layernorm(int32_t out_dtype, const float *x, const float *w,
+                                  const float *b, float eps, int32_t M, int32_t D, void *y,
+                                  void *stream);
+
+/* a5+a6 fused QKV projection with bias and 3-D RoPE ("Architecture", "3-D
+ * RoPE"): Y T [B*N, D] times qkv_w [3D, D]^T + qkv_b, split into heads and
+ * written as Q, K: T [B, H, N, hd] (RoPE applied to the patch rows, prefix
+ * rows unrotated) and Vt: T [B, H, hd, ldv] (V transposed per head, ldv =
+ * round_up(N, 64)).  rope = 0 disables the rotation; grid = (gt, gh, gw) and
+ * n_prefix give the token geometry.  rope_table: fp32 scratch of at least
+ * vitenc_rope_table_floats(...) floats, filled by this call. */
+vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w,
+                                 const float *qkv_b, int32_t B, int32_t N, int32_t D,
+                                 int32_t n_head, int32_t rope, int32_t rope_layout,
+                                 int32_t rope_interpolate, int32_t rope_ref_grid,
+                                 float rope_theta, int32_t gt, int32_t gh, int32_t gw,
+                                 int32_t n_prefix, float *rope_table, void *Q, void *K,
+                                 void *Vt, void *stream);
+int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32_t gw);
+
+/* a7 attention ("Architecture", "Block-causal attention"): per item and head,
+ * O = softmax(Q K^T / sqrt(hd) + mask) V with Q, K, Vt in the layouts of
+ * vitenc_op_qkv_rope; O: T [B, N, H*hd] (heads concatenated).  attn_mode
+ * FULL or BLOCK_CAUSAL with frames of `tokens_per_frame` patch tokens after
+ * n_prefix prefix tokens. */
+vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt,
+                                  int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
+                                  int32_t attn_mode, int32_t n_prefix,
+                                  int32_t tokens_per_frame, void *O, void *stream);
+
+/* a8/a10 projection with bias, layer scale and residual: Z[M, Nout] (fp32)
+ * += ls * (A[M, K] W[Nout, K]^T + b); ls may be NULL (= 1). */
+vitenc_status vitenc_op_linear_residual(int32_t dtype, const void *A, const void *W,
+                                        const float *b, const float *ls, int32_t M,
+                                        int32_t Nout, int32_t K, float *Z, void *stream);
+
+/* a9 U[M, Nout] (T) = GELU_erf(A[M, K] W[Nout, K]^T + b). */
+vitenc_status vitenc_op_linear_gelu(int32_t dtype, const void *A, const void *W, const float *b,
+                                    int32_t M, int32_t Nout, int32_t K, void *U, void *stream);
+
+/* a11 pooled feature: pooled[b] = X[b, 0] when cls, else the mean of rows
+ * [n_prefix, N) of X[b]; X fp32 [B, N, D]. */
+vitenc_status vitenc_op_pool(const float *X, int32_t B, int32_t N, int32_t D, int32_t cls,
+                             int32_t n_prefix, float *pooled, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VITENC_H */

@@ -1,0 +1,45 @@
+"""Helpers shared by the GPU parity tests (not a test module)."""
+import sys
+
+import numpy as np
+
+import oracle
+from vision_transformer_amd import workloads as W
+
+# gates: fp32 path max relative error; bf16/f16 path per-token cosine and max abs
+REL_F32 = 1e-4
+COS_BF16 = 0.9999
+ABS_BF16 = 2e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def gates_ok(cfg, stats):
+    if not stats["finite"]:
+        return False
+    if cfg.dtype == W.DTYPE_F32:
+        return stats["rel"] <= REL_F32
+    return stats["min_cos"] >= COS_BF16 and stats["maxabs"] <= ABS_BF16
+
+
+def run_gpu(wl, device="cuda"):
+    """Encode a workload on the GPU through the C ABI; returns numpy fp64."""
+    import torch
+    from vision_transformer_amd.vitenc import Encoder
+    enc = Encoder.from_workload(wl, device)
+    px = torch.from_numpy(wl.pixels).to(device)
+    out, pooled = enc.encode(px)
+    torch.cuda.synchronize()
+    res = to_np(out), to_np(pooled)
+    enc.close()
+    return res

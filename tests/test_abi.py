@@ -1,0 +1,208 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and refuses bad input by name before any device work (refusal,
+never clamping: jepa.cpp "Architecture", section "Robustness").  No kernel
+is launched by any test here."""
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+from vision_transformer_amd import vitenc as V
+from vision_transformer_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vitenc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(V.LIB_PATH), reason="libvitenc.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vitenc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = V.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(V.SIGNATURES), "binding and header disagree"
+    assert L.vitenc_abi_version() == 1
+
+
+FAKE = 0x1000  # a non-NULL pointer that is never dereferenced: creation only validates
+
+
+def _hp(**kw):
+    cfg = W.CONFIGS[2]
+    hp = cfg.hparams()
+    hp["pos_rows"] = 0
+    hp.update(kw)
+    return V.make_hparams(hp)
+
+
+def _weights(n_layer, ls=False, blank=None):
+    bw = (V.BlockWeights * n_layer)()
+    for i in range(n_layer):
+        for f in V.BLOCK_FIELDS:
+            if f in ("ls1", "ls2") and not ls:
+                continue
+            setattr(bw[i], f, FAKE)
+    if blank:
+        setattr(bw[0], blank, None)
+    w = V.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.cast(bw, ctypes.POINTER(V.BlockWeights)), FAKE, FAKE)
+    return w, bw
+
+
+def _create(hp, w):
+    h = ctypes.c_void_p()
+    st = V.lib().vitenc_model_create(ctypes.byref(hp), ctypes.byref(w), ctypes.byref(h))
+    return st, h
+
+
+def _text():
+    return V.lib().vitenc_error_text().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(embed_dim=0), 1, "embed_dim"),
+    (dict(embed_dim=70000), 1, "embed_dim"),
+    (dict(n_layer=0), 1, "n_layer"),
+    (dict(n_head=0), 1, "n_head"),
+    (dict(ffn_dim=0), 1, "ffn_dim"),
+    (dict(patch_size=0), 1, "patch_size"),
+    (dict(tubelet_size=2000), 1, "tubelet_size"),
+    (dict(in_chans=0), 1, "in_chans"),
+    (dict(ln_eps=float("nan")), 1, "ln_eps"),
+    (dict(ln_eps=2.0), 1, "ln_eps"),
+    (dict(dtype=7), 1, "dtype"),
+    (dict(pos_type=5), 1, "pos_type"),
+    (dict(rope=3), 1, "rope"),
+    (dict(rope_layout=4), 1, "rope_layout"),
+    (dict(attn_mode=9), 1, "attn_mode"),
+    (dict(embed_dim=1000, n_head=16), 1, "divisible"),
+    (dict(embed_dim=65, n_head=1), 1, "odd"),
+    (dict(rope_theta=0.0), 1, "rope_theta"),
+    (dict(rope_interpolate=1, rope_ref_grid=0), 1, "rope_ref_grid"),
+    (dict(rope=0, attn_mode=1), 1, "block_causal"),
+    (dict(rope=0, rope_interpolate=1, rope_ref_grid=16), 1, "rope_interpolate"),
+    (dict(pos_type=1, pos_rows=0), 1, "pos_rows"),
+    (dict(embed_dim=1024, n_head=8), 6, "head_dim"),
+    (dict(embed_dim=8192, n_head=128), 6, "embed_dim"),
+])
+def test_hparam_refusals(kw, status, needle):
+    w, _keep = _weights(24)
+    st, h = _create(_hp(**kw), w)
+    assert st == status, _text()
+    assert needle in _text()
+    assert not h.value
+
+
+@pytest.mark.parametrize("blank", ["qkv_w", "ln2_b", "down_b"])
+def test_null_weight_refused(blank):
+    w, _keep = _weights(24, blank=blank)
+    st, h = _create(_hp(), w)
+    assert st == 3 and "block 0" in _text()
+
+
+def test_layer_scale_pointers_required():
+    w, _keep = _weights(24, ls=False)
+    st, _ = _create(_hp(layer_scale=1), w)
+    assert st == 3 and "ls1" in _text()
+    w2, _keep2 = _weights(24, ls=True)
+    st, h = _create(_hp(layer_scale=1), w2)
+    assert st == 0
+    V.lib().vitenc_model_destroy(h)
+
+
+@pytest.fixture()
+def model():
+    w, keep = _weights(24)
+    st, h = _create(_hp(), w)
+    assert st == 0, _text()
+    yield h
+    V.lib().vitenc_model_destroy(h)
+
+
+def test_workspace_size_and_shape_refusals(model):
+    L = V.lib()
+    n = ctypes.c_size_t()
+    assert L.vitenc_workspace_size(model, 2, 16, 256, 256, ctypes.byref(n)) == 0
+    ws_c3 = n.value
+    # Z fp32 + Y, Q, K, Vt, O bf16 [M, D] + U bf16 [M, F] + patch rows, at least
+    M, D, F = 4096, 1024, 4096
+    assert ws_c3 >= M * D * 4 + 5 * M * D * 2 + M * F * 2
+    assert L.vitenc_workspace_size(model, 1, 16, 256, 256, ctypes.byref(n)) == 0 and n.value < ws_c3
+    for shape, needle in [((0, 16, 256, 256), "non-positive"), ((2, 15, 256, 256), "tubelet"),
+                          ((2, 16, 250, 256), "patch_size"), ((1, 2, 16 * 1024, 16), "grid"),
+                          ((1, 2048, 16 * 600, 16 * 600), "grid")]:
+        st = L.vitenc_workspace_size(model, *shape, ctypes.byref(n))
+        assert st == 2 and needle in _text(), (shape, _text())
+
+
+def test_token_limit_refused():
+    w, keep = _weights(1)
+    st, h = _create(_hp(n_layer=1, patch_size=1, tubelet_size=1), w)
+    assert st == 0
+    n = ctypes.c_size_t()
+    st = V.lib().vitenc_workspace_size(h, 1, 5, 1000, 1000, ctypes.byref(n))
+    assert st == 2 and "2^22" in _text()
+    V.lib().vitenc_model_destroy(h)
+
+
+def test_pos_table_rows_must_match_tokens():
+    w, keep = _weights(24)
+    st, h = _create(_hp(pos_type=1, pos_rows=197, rope=0, tubelet_size=1), w)
+    assert st == 0
+    n = ctypes.c_size_t()
+    assert V.lib().vitenc_workspace_size(h, 1, 1, 224, 224, ctypes.byref(n)) == 2
+    assert "position table" in _text()
+    V.lib().vitenc_model_destroy(h)
+
+
+def test_encode_refusals_before_any_launch(model):
+    L = V.lib()
+    n = ctypes.c_size_t()
+    assert L.vitenc_workspace_size(model, 2, 16, 256, 256, ctypes.byref(n)) == 0
+    need = n.value
+    args = lambda ws, nbytes, px=FAKE, out=FAKE: (model, px, 2, 16, 256, 256, ws, nbytes, out, None, None)
+    assert L.vitenc_encode(*args(None, need)) == 3
+    assert L.vitenc_encode(*args(4096, need - 1)) == 4 and "needed" in _text()
+    assert L.vitenc_encode(*args(4096 + 8, need)) == 4 and "aligned" in _text()
+    assert L.vitenc_encode(*args(4096, need, px=None)) == 3
+    assert L.vitenc_encode(*args(4096, need, out=None)) == 3
+    assert L.vitenc_encode(None, FAKE, 2, 16, 256, 256, 4096, need, FAKE, None, None) == 3
+    assert L.vitenc_encode(model, FAKE, 2, 16, 255, 256, 4096, need, FAKE, None, None) == 2
+
+
+def test_step_entry_point_refusals():
+    L = V.lib()
+    assert L.vitenc_op_layernorm(9, FAKE, FAKE, FAKE, 1e-6, 4, 64, FAKE, None) == 1
+    assert L.vitenc_op_layernorm(0, None, FAKE, FAKE, 1e-6, 4, 64, FAKE, None) == 3
+    assert L.vitenc_op_layernorm(0, FAKE, FAKE, FAKE, 1e-6, 4, 5000, FAKE, None) == 6
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 48, 0, 0, 0, FAKE, None) == 6
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 1, 0, 0, FAKE, None) == 2
+    assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 0, 0, 0, 1e4, 2, 2, 2, 0,
+                                FAKE, FAKE, FAKE, FAKE, None) == 2          # 8 patches + 0 prefix != 17
+    assert L.vitenc_op_embed(1, FAKE, 1, 3, 1, 30, 32, 1, 16, FAKE, FAKE, None, None, None, 64, FAKE, FAKE,
+                             None) == 2
+    assert L.vitenc_op_pool(FAKE, 1, 4, 8, 0, 4, FAKE, None) == 2
+
+
+def test_error_text_is_thread_local(model):
+    L = V.lib()
+    n = ctypes.c_size_t()
+    assert L.vitenc_workspace_size(model, 0, 16, 256, 256, ctypes.byref(n)) == 2
+    seen = {}
+
+    def other():
+        seen["text"] = L.vitenc_error_text().decode()
+
+    t = threading.Thread(target=other)
+    t.start(); t.join()
+    assert seen["text"] == ""
+    assert "non-positive" in _text()

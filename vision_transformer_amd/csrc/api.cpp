@@ -1,0 +1,300 @@
+// C ABI of the encoder (include/vitenc.h): validation, workspace planning and
+// the launch sequence of one forward.  Every refusal happens here, before any
+// device work is enqueued; the kernels assume the shapes validated here.
+#include "../../include/vitenc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "launch.h"
+
+using namespace vitenc;
+
+struct vitenc_model {
+    vitenc_hparams hp;
+    vitenc_weights w;
+    std::vector<vitenc_block_weights> blocks;
+};
+
+namespace {
+thread_local std::string g_error;
+} // namespace
+
+namespace vitenc {
+vitenc_status fail(vitenc_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+void clear_error() { g_error.clear(); }
+} // namespace vitenc
+
+namespace {
+
+vitenc_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return VITENC_OK;
+    return fail(VITENC_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxTokens = int64_t(1) << 22;   // per item, as the pages' loader limit
+constexpr int kMaxGrid = 1023;                     // per axis (packed 10-bit positions)
+constexpr int kMaxEmbed = 4096;                    // LayerNorm keeps a row in one wave's registers
+
+bool in_range(int64_t v, int64_t lo, int64_t hi) { return v >= lo && v <= hi; }
+bool valid_dtype(int dt) { return dt == VITENC_F32 || dt == VITENC_BF16 || dt == VITENC_F16; }
+int64_t rup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+vitenc_status validate_hparams(const vitenc_hparams *hp) {
+    if (!hp) return fail(VITENC_ENULL, "hparams is NULL");
+    if (!in_range(hp->embed_dim, 1, 65536)) return fail(VITENC_EINVAL, "embed_dim %d outside 1..65536", hp->embed_dim);
+    if (!in_range(hp->n_layer, 1, 1024)) return fail(VITENC_EINVAL, "n_layer %d outside 1..1024", hp->n_layer);
+    if (!in_range(hp->n_head, 1, 1024)) return fail(VITENC_EINVAL, "n_head %d outside 1..1024", hp->n_head);
+    if (!in_range(hp->ffn_dim, 1, 1 << 20)) return fail(VITENC_EINVAL, "ffn_dim %d outside 1..2^20", hp->ffn_dim);
+    if (!in_range(hp->patch_size, 1, 1024)) return fail(VITENC_EINVAL, "patch_size %d outside 1..1024", hp->patch_size);
+    if (!in_range(hp->tubelet_size, 1, 1024))
+        return fail(VITENC_EINVAL, "tubelet_size %d outside 1..1024", hp->tubelet_size);
+    if (!in_range(hp->in_chans, 1, 1024)) return fail(VITENC_EINVAL, "in_chans %d outside 1..1024", hp->in_chans);
+    if (!std::isfinite(hp->ln_eps) || hp->ln_eps < 0.0f || hp->ln_eps > 1.0f)
+        return fail(VITENC_EINVAL, "ln_eps %g not a finite value in [0, 1]", (double)hp->ln_eps);
+    if (!valid_dtype(hp->dtype)) return fail(VITENC_EINVAL, "unknown dtype %d", hp->dtype);
+    if (hp->pos_type != VITENC_POS_NONE && hp->pos_type != VITENC_POS_TABLE)
+        return fail(VITENC_EINVAL, "unknown pos_type %d", hp->pos_type);
+    if (hp->rope != VITENC_ROPE_NONE && hp->rope != VITENC_ROPE_3D) return fail(VITENC_EINVAL, "unknown rope %d", hp->rope);
+    if (hp->rope_layout != VITENC_ROPE_TILED && hp->rope_layout != VITENC_ROPE_INTERLEAVED)
+        return fail(VITENC_EINVAL, "unknown rope_layout %d", hp->rope_layout);
+    if (hp->attn_mode != VITENC_ATTN_FULL && hp->attn_mode != VITENC_ATTN_BLOCK_CAUSAL)
+        return fail(VITENC_EINVAL, "unknown attn_mode %d", hp->attn_mode);
+    if (hp->embed_dim % hp->n_head != 0)
+        return fail(VITENC_EINVAL, "embed_dim %d not divisible by n_head %d", hp->embed_dim, hp->n_head);
+    const int hd = hp->embed_dim / hp->n_head;
+    if (hp->rope == VITENC_ROPE_3D) {
+        if (!std::isfinite(hp->rope_theta) || hp->rope_theta <= 0.0f)
+            return fail(VITENC_EINVAL, "rope_theta %g must be finite and > 0", (double)hp->rope_theta);
+        if (hd % 2 != 0) return fail(VITENC_EINVAL, "head_dim %d is odd; 3-D RoPE rotates pairs", hd);
+        if (2 * ((hd / 3) / 2) < 2) return fail(VITENC_EINVAL, "head_dim %d leaves no rotated pair per axis", hd);
+        if (hp->rope_interpolate && hp->rope_ref_grid <= 0)
+            return fail(VITENC_EINVAL, "rope_interpolate without a rope_ref_grid to rescale from");
+    } else if (hp->rope_interpolate) {
+        return fail(VITENC_EINVAL, "rope_interpolate set on a model without 3-D RoPE");
+    }
+    if (hp->attn_mode == VITENC_ATTN_BLOCK_CAUSAL && hp->rope != VITENC_ROPE_3D)
+        return fail(VITENC_EINVAL, "block_causal attention on a model without a frame grid (rope3d)");
+    if (hp->pos_type == VITENC_POS_TABLE && hp->pos_rows <= 0)
+        return fail(VITENC_EINVAL, "pos_type TABLE with pos_rows %d", hp->pos_rows);
+    if (hd != 64 && hd != 32)
+        return fail(VITENC_EUNSUPPORTED, "head_dim %d: the attention kernel implements 64 and 32", hd);
+    if (hp->embed_dim > kMaxEmbed)
+        return fail(VITENC_EUNSUPPORTED, "embed_dim %d above %d", hp->embed_dim, kMaxEmbed);
+    return VITENC_OK;
+}
+
+struct Plan {
+    int B, C, T, H, W;
+    int gt, gh, gw, Np, p, N;
+    int64_t M;
+    int D, F, nh, hd, K, lda, ldv;
+    size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_rope, off_tok, total;
+};
+
+vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, int32_t W, Plan &pl) {
+    const vitenc_hparams &hp = m->hp;
+    if (B <= 0 || T <= 0 || H <= 0 || W <= 0)
+        return fail(VITENC_ESHAPE, "non-positive input shape B=%d T=%d H=%d W=%d", B, T, H, W);
+    if (T % hp.tubelet_size) return fail(VITENC_ESHAPE, "T=%d not a multiple of tubelet_size %d", T, hp.tubelet_size);
+    if (H % hp.patch_size || W % hp.patch_size)
+        return fail(VITENC_ESHAPE, "H=%d / W=%d not multiples of patch_size %d", H, W, hp.patch_size);
+    pl.B = B; pl.C = hp.in_chans; pl.T = T; pl.H = H; pl.W = W;
+    pl.gt = T / hp.tubelet_size; pl.gh = H / hp.patch_size; pl.gw = W / hp.patch_size;
+    if (pl.gt > kMaxGrid || pl.gh > kMaxGrid || pl.gw > kMaxGrid)
+        return fail(VITENC_ESHAPE, "token grid %dx%dx%d exceeds %d per axis", pl.gt, pl.gh, pl.gw, kMaxGrid);
+    const int64_t np = (int64_t)pl.gt * pl.gh * pl.gw;
+    pl.p = hp.cls_token ? 1 : 0;
+    if (np + pl.p > kMaxTokens) return fail(VITENC_ESHAPE, "%lld tokens per item exceed 2^22", (long long)(np + pl.p));
+    pl.Np = (int)np;
+    pl.N = pl.Np + pl.p;
+    pl.M = (int64_t)B * pl.N;
+    if (pl.M > (int64_t(1) << 30)) return fail(VITENC_ESHAPE, "B*N = %lld rows exceed 2^30", (long long)pl.M);
+    if (hp.pos_type == VITENC_POS_TABLE && hp.pos_rows != pl.N)
+        return fail(VITENC_ESHAPE, "position table has %d rows but the input makes %d tokens", hp.pos_rows, pl.N);
+    pl.D = hp.embed_dim; pl.F = hp.ffn_dim; pl.nh = hp.n_head; pl.hd = pl.D / pl.nh;
+    pl.K = hp.in_chans * hp.tubelet_size * hp.patch_size * hp.patch_size;
+    pl.lda = (int)rup(pl.K, 8);
+    pl.ldv = (int)rup(pl.N, 64);
+    const size_t es = (size_t)dtype_size(hp.dtype);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = (size_t)rup((int64_t)(off + bytes), 256);
+        return o;
+    };
+    pl.off_Z = take((size_t)pl.M * pl.D * 4);
+    pl.off_Y = take((size_t)pl.M * pl.D * es);
+    pl.off_Q = take((size_t)pl.M * pl.D * es);
+    pl.off_K = take((size_t)pl.M * pl.D * es);
+    pl.off_V = take((size_t)B * pl.nh * pl.hd * pl.ldv * es);
+    pl.off_O = take((size_t)pl.M * pl.D * es);
+    pl.off_U = take((size_t)pl.M * pl.F * es);
+    pl.off_A = take((size_t)B * pl.Np * pl.lda * es);
+    const int d = 2 * ((pl.hd / 3) / 2);
+    pl.off_rope = take((size_t)(pl.gt + pl.gh + pl.gw) * d * 2 * 4);
+    pl.off_tok = take((size_t)pl.Np * 4);
+    pl.total = off;
+    return VITENC_OK;
+}
+
+#define CHECK_DEV(expr, what)                                                                                     \
+    do {                                                                                                          \
+        vitenc_status st_ = device_status((expr), what);                                                          \
+        if (st_ != VITENC_OK) return st_;                                                                         \
+    } while (0)
+
+} // namespace
+
+extern "C" {
+
+int32_t vitenc_abi_version(void) { return VITENC_ABI_VERSION; }
+
+const char *vitenc_error_text(void) { return g_error.c_str(); }
+
+vitenc_status vitenc_model_create(const vitenc_hparams *hp, const vitenc_weights *w, vitenc_model **out) {
+    g_error.clear();
+    if (!out) return fail(VITENC_ENULL, "out is NULL");
+    *out = nullptr;
+    vitenc_status st = validate_hparams(hp);
+    if (st != VITENC_OK) return st;
+    if (!w) return fail(VITENC_ENULL, "weights is NULL");
+    if (!w->patch_w || !w->patch_b) return fail(VITENC_ENULL, "patch_w / patch_b is NULL");
+    if (hp->pos_type == VITENC_POS_TABLE && !w->pos_embed) return fail(VITENC_ENULL, "pos_embed is NULL");
+    if (hp->cls_token && !w->cls_token) return fail(VITENC_ENULL, "cls_token is NULL");
+    if (hp->modality_embed && !w->mod_embed) return fail(VITENC_ENULL, "mod_embed is NULL");
+    if (!w->norm_w || !w->norm_b) return fail(VITENC_ENULL, "norm_w / norm_b is NULL");
+    if (!w->blocks) return fail(VITENC_ENULL, "blocks is NULL");
+    for (int i = 0; i < hp->n_layer; ++i) {
+        const vitenc_block_weights &b = w->blocks[i];
+        const void *req[] = {b.ln1_w, b.ln1_b, b.qkv_w, b.qkv_b, b.out_w, b.out_b,
+                             b.ln2_w, b.ln2_b, b.up_w, b.up_b, b.down_w, b.down_b};
+        for (const void *p : req)
+            if (!p) return fail(VITENC_ENULL, "block %d: a required tensor is NULL", i);
+        if (hp->layer_scale && (!b.ls1 || !b.ls2)) return fail(VITENC_ENULL, "block %d: ls1 / ls2 is NULL", i);
+    }
+    vitenc_model *m = new vitenc_model;
+    m->hp = *hp;
+    m->w = *w;
+    m->blocks.assign(w->blocks, w->blocks + hp->n_layer);
+    m->w.blocks = m->blocks.data();
+    *out = m;
+    return VITENC_OK;
+}
+
+void vitenc_model_destroy(vitenc_model *m) { delete m; }
+
+vitenc_status vitenc_workspace_size(const vitenc_model *m, int32_t B, int32_t T, int32_t H, int32_t W,
+                                    size_t *bytes) {
+    g_error.clear();
+    if (!m || !bytes) return fail(VITENC_ENULL, "model / bytes is NULL");
+    Plan pl;
+    vitenc_status st = make_plan(m, B, T, H, W, pl);
+    if (st != VITENC_OK) return st;
+    *bytes = pl.total;
+    return VITENC_OK;
+}
+
+vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t B, int32_t T, int32_t H, int32_t W,
+                            void *workspace, size_t ws_bytes, float *out_tokens, float *out_pooled, void *stream) {
+    g_error.clear();
+    if (!m) return fail(VITENC_ENULL, "model is NULL");
+    if (!pixels || !out_tokens) return fail(VITENC_ENULL, "pixels / out_tokens is NULL");
+    Plan pl;
+    vitenc_status st = make_plan(m, B, T, H, W, pl);
+    if (st != VITENC_OK) return st;
+    if (!workspace) return fail(VITENC_ENULL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256) return fail(VITENC_EWORKSPACE, "workspace not 256-byte aligned");
+    if (ws_bytes < pl.total)
+        return fail(VITENC_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, pl.total);
+
+    const vitenc_hparams &hp = m->hp;
+    const int dt = hp.dtype;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    float *Z = reinterpret_cast<float *>(ws + pl.off_Z);
+    void *Y = ws + pl.off_Y, *Q = ws + pl.off_Q, *Kb = ws + pl.off_K, *Vt = ws + pl.off_V;
+    void *O = ws + pl.off_O, *U = ws + pl.off_U, *A = ws + pl.off_A;
+    float *rope_tab = reinterpret_cast<float *>(ws + pl.off_rope);
+    int *tok_pos = reinterpret_cast<int *>(ws + pl.off_tok);
+    const int M = (int)pl.M, D = pl.D, F = pl.F;
+
+    // a1-a3: tokens
+    CHECK_DEV(launch_patchify(dt, pixels, B, pl.C, T, H, W, hp.tubelet_size, hp.patch_size, A, pl.lda, s), "patchify");
+    {
+        EpiArgs ep;
+        ep.bias = m->w.patch_b;
+        ep.Z = Z;
+        ep.ldz = D;
+        ep.pos = hp.pos_type == VITENC_POS_TABLE ? m->w.pos_embed : nullptr;
+        ep.mod = hp.modality_embed ? m->w.mod_embed : nullptr;
+        ep.Np = pl.Np;
+        ep.Ntok = pl.N;
+        ep.prefix = pl.p;
+        CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda, m->w.patch_w, pl.K, B * pl.Np, D, pl.K, ep, s), "patch GEMM");
+    }
+    if (pl.p)
+        CHECK_DEV(launch_prefix_rows(m->w.cls_token, hp.pos_type == VITENC_POS_TABLE ? m->w.pos_embed : nullptr,
+                                     hp.modality_embed ? m->w.mod_embed : nullptr,
+                                     B, pl.N, D, Z, s),
+                  "prefix rows");
+    if (hp.rope)
+        CHECK_DEV(launch_rope_table(pl.hd, hp.rope_layout, hp.rope_interpolate, hp.rope_ref_grid, hp.rope_theta, pl.gt,
+                                    pl.gh, pl.gw, rope_tab, tok_pos, s),
+                  "rope tables");
+
+    for (int l = 0; l < hp.n_layer; ++l) {
+        const vitenc_block_weights &bw = m->blocks[l];
+        CHECK_DEV(launch_layernorm(dt, Z, bw.ln1_w, bw.ln1_b, hp.ln_eps, M, D, Y, s), "ln1");
+        {
+            EpiArgs ep;
+            ep.bias = bw.qkv_b;
+            ep.Q = Q; ep.K = Kb; ep.Vt = Vt;
+            ep.D = D; ep.head_dim = pl.hd; ep.ldv = pl.ldv;
+            ep.Ntok = pl.N; ep.prefix = pl.p;
+            ep.rope = hp.rope;
+            ep.d_rot = 2 * ((pl.hd / 3) / 2);
+            ep.rope_tab = rope_tab; ep.tok_pos = tok_pos;
+            ep.gt = pl.gt; ep.gh = pl.gh;
+            CHECK_DEV(launch_gemm(dt, EPI_QKV, Y, D, bw.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
+        }
+        CHECK_DEV(launch_attention(dt, Q, Kb, Vt, B, pl.N, pl.nh, pl.hd, pl.ldv, hp.attn_mode, pl.p, pl.gh * pl.gw, O, s),
+                  "attention");
+        {
+            EpiArgs ep;
+            ep.bias = bw.out_b; ep.Z = Z; ep.ldz = D;
+            ep.ls = hp.layer_scale ? bw.ls1 : nullptr;
+            CHECK_DEV(launch_gemm(dt, EPI_RESID, O, D, bw.out_w, D, M, D, D, ep, s), "out GEMM");
+        }
+        CHECK_DEV(launch_layernorm(dt, Z, bw.ln2_w, bw.ln2_b, hp.ln_eps, M, D, Y, s), "ln2");
+        {
+            EpiArgs ep;
+            ep.bias = bw.up_b; ep.out = U; ep.ldo = F;
+            CHECK_DEV(launch_gemm(dt, EPI_GELU, Y, D, bw.up_w, D, M, F, D, ep, s), "up GEMM");
+        }
+        {
+            EpiArgs ep;
+            ep.bias = bw.down_b; ep.Z = Z; ep.ldz = D;
+            ep.ls = hp.layer_scale ? bw.ls2 : nullptr;
+            CHECK_DEV(launch_gemm(dt, EPI_RESID, U, F, bw.down_w, F, M, D, F, ep, s), "down GEMM");
+        }
+    }
+    CHECK_DEV(launch_layernorm(DT_F32, Z, m->w.norm_w, m->w.norm_b, hp.ln_eps, M, D, out_tokens, s), "final norm");
+    if (out_pooled) CHECK_DEV(launch_pool(out_tokens, B, pl.N, D, hp.cls_token, pl.p, out_pooled, s), "pool");
+    return VITENC_OK;
+}
+
+} // extern "C"

@@ -1,0 +1,111 @@
+// Device-side building blocks shared by the gfx950 kernels: element types,
+// 16-byte vector loads, conversions and the MFMA tiles the kernels use.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vitenc {
+
+typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16 bytes of operand data; reinterpreted as 8 x 16-bit or 4 x fp32.
+struct alignas(16) Chunk {
+    uint32_t w[4];
+};
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kPerChunk = 4;     // elements per 16-byte chunk
+    static constexpr int kMfmaPerChunk = 4; // 32x32x2 f32 MFMAs consuming one chunk per lane
+};
+template <> struct Elem<bf16_t> {
+    static constexpr int kPerChunk = 8;
+    static constexpr int kMfmaPerChunk = 1; // one 32x32x16 bf16 MFMA
+};
+template <> struct Elem<f16_t> {
+    static constexpr int kPerChunk = 8;
+    static constexpr int kMfmaPerChunk = 1; // one 32x32x16 f16 MFMA
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950)
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (f16_t)x; }
+
+// 16-bit payload of an element (for packing two halves into one dword)
+__device__ __forceinline__ uint32_t bits16(bf16_t x) { return __builtin_bit_cast(uint16_t, x); }
+__device__ __forceinline__ uint32_t bits16(f16_t x) { return __builtin_bit_cast(uint16_t, x); }
+
+__device__ __forceinline__ Chunk load_chunk(const void *p) {
+    return *reinterpret_cast<const Chunk *>(p);
+}
+__device__ __forceinline__ void store_chunk(void *p, const Chunk &c) {
+    *reinterpret_cast<Chunk *>(p) = c;
+}
+__device__ __forceinline__ Chunk zero_chunk() {
+    Chunk c;
+    c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0u;
+    return c;
+}
+
+// ----------------------------------------------------------------------------
+// 32x32 MFMA tiles.  Operand layout (one 64-lane wave): lane l supplies row
+// (l % 32) of A / column (l % 32) of B, and the k-slice owned by lane group
+// g = l / 32.  The accumulator holds, in lane l, column (l % 32) and rows
+//   8*(i/4) + 4*g + (i%4),  i = 0..15.
+// mfma_chunk() consumes one 16-byte chunk per lane: for 16-bit types that is
+// one 32x32x16 MFMA (the chunk is the lane group's 8 k values); for fp32 it
+// is four 32x32x2 MFMAs, MFMA j taking element j of every lane's chunk.  In
+// both cases the k values a lane group contributes are the same for A and B,
+// so any assignment of actual k indices to chunks is a valid contraction as
+// long as the A and B lanes of one group read the same k indices.
+// ----------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ void mfma_chunk(f32x16 &acc, const Chunk &a, const Chunk &b);
+
+template <> __device__ __forceinline__ void mfma_chunk<bf16_t>(f32x16 &acc, const Chunk &a, const Chunk &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma_chunk<f16_t>(f32x16 &acc, const Chunk &a, const Chunk &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                 acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma_chunk<float>(f32x16 &acc, const Chunk &a, const Chunk &b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a.w[j]),
+                                                   __builtin_bit_cast(float, b.w[j]), acc, 0, 0, 0);
+}
+
+// accumulator row owned by lane group g for accumulator slot i
+__device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// ----------------------------------------------------------------------------
+// wave-level reductions (64 lanes)
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__host__ __device__ __forceinline__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+__host__ __device__ __forceinline__ int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+} // namespace vitenc

@@ -1,0 +1,242 @@
+// Memory-bound steps of the encoder: patch rearrangement, LayerNorm, prefix
+// (CLS) rows, the 3-D RoPE tables, and the pooled feature.
+#include "common.h"
+#include "launch.h"
+
+namespace vitenc {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// a1 rearrange NCTHW pixels into patch rows (jepa.cpp "Architecture", "The
+// shared ViT graph"; "GGUF schema (v1)", "Encoder tensors": C-T-H-W order;
+// "Token order": T-major, then H, then W).
+//   A[b*Np + n, f] = X[b, c, t'*t + dt, h'*P + dh, w'*P + dw]
+//   n = (t'*gh + h')*gw + w',  f = ((c*t + dt)*P + dh)*P + dw
+// Columns f in [K, lda) are zero padding.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__ X, int C, int T_, int H,
+                                                       int W, int tub, int P, int gh, int gw, int Np,
+                                                       int K, int64_t lda, int64_t total, T *__restrict__ A) {
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = idx / lda;
+        const int f = (int)(idx - m * lda);
+        float v = 0.0f;
+        if (f < K) {
+            const int b = (int)(m / Np), n = (int)(m - (int64_t)b * Np);
+            const int tt = n / (gh * gw), hh = (n / gw) % gh, ww = n % gw;
+            const int dw = f % P, dh = (f / P) % P, dt = (f / (P * P)) % tub, c = f / (P * P * tub);
+            const int64_t src = ((((int64_t)b * C + c) * T_ + (tt * tub + dt)) * H + (hh * P + dh)) * W +
+                                (ww * P + dw);
+            v = X[src];
+        }
+        A[idx] = from_f32<T>(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// a4 LayerNorm: one wave per row, the row held in registers, centred
+// two-pass population variance, eps inside the root ("GGUF schema (v1)",
+// jepa.enc.ln_eps; "Architecture", "Attention and precision").
+// ---------------------------------------------------------------------------
+template <typename TO, int NE>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x, const float *__restrict__ w,
+                                                        const float *__restrict__ b, float eps, int M, int D,
+                                                        TO *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const float *xr = x + (int64_t)row * D;
+    float v[NE];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int c = lane + 64 * i;
+        v[i] = c < D ? xr[c] : 0.0f;
+        s += v[i];
+    }
+    const float mean = wave_sum(s) / (float)D;
+    float q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int c = lane + 64 * i;
+        const float d = v[i] - mean;
+        q += c < D ? d * d : 0.0f;
+    }
+    const float var = wave_sum(q) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    TO *yr = y + (int64_t)row * D;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int c = lane + 64 * i;
+        if (c < D) yr[c] = from_f32<TO>((v[i] - mean) * rstd * w[c] + b[c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// a3 prefix rows: Z[b, 0] = cls (+ pos row 0) (+ mod)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefix_rows_kernel(const float *__restrict__ cls, const float *__restrict__ pos,
+                                                          const float *__restrict__ mod, int B, int Ntok, int D,
+                                                          float *__restrict__ Z) {
+    const int d = blockIdx.x * blockDim.x + threadIdx.x;
+    const int b = blockIdx.y;
+    if (d >= D || b >= B) return;
+    float v = cls[d];
+    if (pos) v += pos[d];
+    if (mod) v += mod[d];
+    Z[(int64_t)b * Ntok * D + d] = v;
+}
+
+// ---------------------------------------------------------------------------
+// a6 tables of the 3-D RoPE ("Architecture", "3-D RoPE"): for axis a in
+// (t, h, w), position p and rotated element j in [0, d):
+//   angle = pos_a(p) * omega_k,  omega_k = theta^(-2k/d),
+//   k = j mod (d/2) (tiled) or j / 2 (interleaved),
+//   pos_a(p) = p, or p * (ref - 1)/(g - 1) on h and w under interpolate_rope
+// stored as (cos, sign_j * sin) with sign -1 on even j and +1 on odd j, so the
+// rotation of element j is x_j * cos + x_{j^1} * signed_sin (rotate90 of the
+// pair (y1, y2) is (-y2, y1)).  Also the packed (t, h, w) of each patch token
+// (i = t*gh*gw + h*gw + w, "GGUF schema (v1)", "Token order").
+// Angles are formed in fp64 and rounded once.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rope_table_kernel(int d, int layout, int interpolate, int ref_grid,
+                                                         double theta, int gt, int gh, int gw,
+                                                         float *__restrict__ tab, int *__restrict__ tok_pos) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const int n_tab = (gt + gh + gw) * d;
+    if (idx < n_tab) {
+        const int p_all = idx / d, j = idx - p_all * d;
+        int axis, p, g;
+        if (p_all < gt) { axis = 0; p = p_all; g = gt; }
+        else if (p_all < gt + gh) { axis = 1; p = p_all - gt; g = gh; }
+        else { axis = 2; p = p_all - gt - gh; g = gw; }
+        double pos = (double)p;
+        if (interpolate && axis > 0 && g > 1) pos = pos * (double)(ref_grid - 1) / (double)(g - 1);
+        const int k = layout == 0 ? (j % (d / 2)) : (j / 2);
+        const double omega = pow(theta, -2.0 * (double)k / (double)d);
+        const double ang = pos * omega;
+        tab[2 * idx] = (float)cos(ang);
+        tab[2 * idx + 1] = (float)((j & 1) ? sin(ang) : -sin(ang));
+    }
+    const int np = gt * gh * gw;
+    if (idx < np) {
+        const int t = idx / (gh * gw), h = (idx / gw) % gh, w = idx % gw;
+        tok_pos[idx] = t | (h << 10) | (w << 20);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// a11 pooled feature: the CLS row, or the mean of the patch rows.
+// 1024 threads: 64 columns x 16 row groups, partial sums combined in LDS in a
+// fixed order (deterministic).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void pool_kernel(const float *__restrict__ X, int N, int D, int cls,
+                                                    int n_prefix, float *__restrict__ pooled) {
+    __shared__ float part[16][64];
+    const int cx = threadIdx.x & 63, rg = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + cx;
+    const int b = blockIdx.y;
+    const float *xb = X + (int64_t)b * N * D;
+    float s = 0.0f;
+    if (d < D) {
+        if (cls) {
+            s = rg == 0 ? xb[d] : 0.0f;
+        } else {
+            for (int n = n_prefix + rg; n < N; n += 16) s += xb[(int64_t)n * D + d];
+        }
+    }
+    part[rg][cx] = s;
+    __syncthreads();
+    if (rg == 0 && d < D) {
+        float t = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t += part[r][cx];
+        pooled[(int64_t)b * D + d] = cls ? t : t / (float)(N - n_prefix);
+    }
+}
+
+template <typename TO>
+hipError_t launch_ln_t(const float *x, const float *w, const float *b, float eps, int M, int D, TO *y,
+                       hipStream_t s) {
+    dim3 grid((unsigned)cdiv(M, 4)), block(256);
+    const int ne = (int)cdiv(D, 64);
+#define VITENC_LN(NE_)                                                                                   \
+    if (ne <= NE_) {                                                                                     \
+        hipLaunchKernelGGL((layernorm_kernel<TO, NE_>), grid, block, 0, s, x, w, b, eps, M, D, y);       \
+        return hipGetLastError();                                                                        \
+    }
+    VITENC_LN(4)
+    VITENC_LN(8)
+    VITENC_LN(16)
+    VITENC_LN(24)
+    VITENC_LN(32)
+    VITENC_LN(48)
+    VITENC_LN(64)
+#undef VITENC_LN
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+hipError_t launch_patchify(int dtype, const float *px, int B, int C, int T, int H, int W, int tub, int P,
+                           void *A, int64_t lda, hipStream_t s) {
+    const int gt = T / tub, gh = H / P, gw = W / P, Np = gt * gh * gw;
+    const int K = C * tub * P * P;
+    const int64_t total = (int64_t)B * Np * lda;
+    if (total == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 65535 * 8);
+    switch (dtype) {
+    case DT_F32:
+        hipLaunchKernelGGL(patchify_kernel<float>, dim3(blocks), dim3(256), 0, s, px, C, T, H, W, tub, P, gh, gw,
+                           Np, K, lda, total, reinterpret_cast<float *>(A));
+        break;
+    case DT_BF16:
+        hipLaunchKernelGGL(patchify_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, px, C, T, H, W, tub, P, gh,
+                           gw, Np, K, lda, total, reinterpret_cast<bf16_t *>(A));
+        break;
+    case DT_F16:
+        hipLaunchKernelGGL(patchify_kernel<f16_t>, dim3(blocks), dim3(256), 0, s, px, C, T, H, W, tub, P, gh, gw,
+                           Np, K, lda, total, reinterpret_cast<f16_t *>(A));
+        break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_layernorm(int out_dtype, const float *x, const float *w, const float *b, float eps, int M, int D,
+                            void *y, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    switch (out_dtype) {
+    case DT_F32: return launch_ln_t<float>(x, w, b, eps, M, D, reinterpret_cast<float *>(y), s);
+    case DT_BF16: return launch_ln_t<bf16_t>(x, w, b, eps, M, D, reinterpret_cast<bf16_t *>(y), s);
+    case DT_F16: return launch_ln_t<f16_t>(x, w, b, eps, M, D, reinterpret_cast<f16_t *>(y), s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix_rows(const float *cls, const float *pos, const float *mod, int B, int Ntok, int D,
+                              float *Z, hipStream_t s) {
+    dim3 grid((unsigned)cdiv(D, 256), (unsigned)B);
+    hipLaunchKernelGGL(prefix_rows_kernel, grid, dim3(256), 0, s, cls, pos, mod, B, Ntok, D, Z);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(int head_dim, int layout, int interpolate, int ref_grid, float theta, int gt, int gh,
+                             int gw, float *rope_tab, int *tok_pos, hipStream_t s) {
+    const int d = 2 * ((head_dim / 3) / 2);
+    const int n = std::max((gt + gh + gw) * d, gt * gh * gw);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, d, layout, interpolate,
+                       ref_grid, (double)theta, gt, gh, gw, rope_tab, tok_pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(const float *X, int B, int N, int D, int cls, int n_prefix, float *pooled, hipStream_t s) {
+    dim3 grid((unsigned)cdiv(D, 64), (unsigned)B);
+    hipLaunchKernelGGL(pool_kernel, grid, dim3(1024), 0, s, X, N, D, cls, n_prefix, pooled);
+    return hipGetLastError();
+}
+
+} // namespace vitenc

@@ -1,0 +1,155 @@
+// Step entry points of include/vitenc.h: one step of the encoder graph each,
+// running the same launchers as vitenc_encode.
+#include "../../include/vitenc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+using namespace vitenc;
+
+namespace {
+
+#define op_fail vitenc::fail
+
+vitenc_status op_dev(hipError_t e, const char *what) {
+    if (e == hipSuccess) return VITENC_OK;
+    return op_fail(VITENC_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int dt) { return dt == VITENC_F32 || dt == VITENC_BF16 || dt == VITENC_F16; }
+
+} // namespace
+
+extern "C" {
+
+vitenc_status vitenc_op_embed(int32_t dtype, const float *pixels, int32_t B, int32_t C, int32_t T, int32_t H,
+                              int32_t W, int32_t tubelet, int32_t patch, const void *patch_w, const float *patch_b,
+                              const float *pos, const float *cls, const float *mod, int32_t D, void *scratch,
+                              float *Z, void *stream) {
+    clear_error();
+    if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
+    if (!pixels || !patch_w || !patch_b || !scratch || !Z) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (B <= 0 || C <= 0 || T <= 0 || H <= 0 || W <= 0 || tubelet <= 0 || patch <= 0 || D <= 0)
+        return op_fail(VITENC_ESHAPE, "non-positive size");
+    if (T % tubelet || H % patch || W % patch) return op_fail(VITENC_ESHAPE, "input not divisible into patches");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int Np = (T / tubelet) * (H / patch) * (W / patch);
+    const int K = C * tubelet * patch * patch;
+    const int lda = (K + 7) / 8 * 8;
+    const int p = cls ? 1 : 0;
+    vitenc_status st = op_dev(launch_patchify(dtype, pixels, B, C, T, H, W, tubelet, patch, scratch, lda, s), "patchify");
+    if (st) return st;
+    EpiArgs ep;
+    ep.bias = patch_b; ep.Z = Z; ep.ldz = D; ep.pos = pos; ep.mod = mod;
+    ep.Np = Np; ep.Ntok = Np + p; ep.prefix = p;
+    st = op_dev(launch_gemm(dtype, EPI_PATCH, scratch, lda, patch_w, K, B * Np, D, K, ep, s), "patch GEMM");
+    if (st) return st;
+    if (p) return op_dev(launch_prefix_rows(cls, pos, mod, B, Np + p, D, Z, s), "prefix rows");
+    return VITENC_OK;
+}
+
+vitenc_status vitenc_op_layernorm(int32_t out_dtype, const float *x, const float *w, const float *b, float eps,
+                                  int32_t M, int32_t D, void *y, void *stream) {
+    clear_error();
+    if (!dtype_ok(out_dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", out_dtype);
+    if (!x || !w || !b || !y) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (M < 0 || D <= 0) return op_fail(VITENC_ESHAPE, "bad size M=%d D=%d", M, D);
+    if (D > 4096) return op_fail(VITENC_EUNSUPPORTED, "D=%d above 4096", D);
+    return op_dev(launch_layernorm(out_dtype, x, w, b, eps, M, D, y, reinterpret_cast<hipStream_t>(stream)),
+                  "layernorm");
+}
+
+int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32_t gw) {
+    const int d = 2 * ((head_dim / 3) / 2);
+    return (int64_t)(gt + gh + gw) * d * 2 + (int64_t)gt * gh * gw; // cos/sin pairs, then packed positions
+}
+
+vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w, const float *qkv_b, int32_t B,
+                                 int32_t N, int32_t D, int32_t n_head, int32_t rope, int32_t rope_layout,
+                                 int32_t rope_interpolate, int32_t rope_ref_grid, float rope_theta, int32_t gt,
+                                 int32_t gh, int32_t gw, int32_t n_prefix, float *rope_table, void *Q, void *K,
+                                 void *Vt, void *stream) {
+    clear_error();
+    if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
+    if (!Y || !qkv_w || !qkv_b || !Q || !K || !Vt) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (B <= 0 || N <= 0 || D <= 0 || n_head <= 0 || D % n_head) return op_fail(VITENC_ESHAPE, "bad sizes");
+    const int hd = D / n_head;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    EpiArgs ep;
+    ep.bias = qkv_b; ep.Q = Q; ep.K = K; ep.Vt = Vt;
+    ep.D = D; ep.head_dim = hd; ep.ldv = (N + 63) / 64 * 64;
+    ep.Ntok = N; ep.prefix = n_prefix;
+    ep.rope = rope;
+    if (rope) {
+        if (!rope_table) return op_fail(VITENC_ENULL, "rope_table is NULL");
+        if (hd % 2) return op_fail(VITENC_EINVAL, "odd head_dim with RoPE");
+        if (gt <= 0 || gh <= 0 || gw <= 0 || gt > 1023 || gh > 1023 || gw > 1023 ||
+            (int64_t)gt * gh * gw + n_prefix != N)
+            return op_fail(VITENC_ESHAPE, "grid %dx%dx%d + %d prefix does not make %d tokens", gt, gh, gw, n_prefix, N);
+        if (rope_interpolate && rope_ref_grid <= 0) return op_fail(VITENC_EINVAL, "interpolate without ref grid");
+        const int d = 2 * ((hd / 3) / 2);
+        float *tab = rope_table;
+        int *tok = reinterpret_cast<int *>(rope_table + (int64_t)(gt + gh + gw) * d * 2);
+        vitenc_status st = op_dev(
+            launch_rope_table(hd, rope_layout, rope_interpolate, rope_ref_grid, rope_theta, gt, gh, gw, tab, tok, s),
+            "rope tables");
+        if (st) return st;
+        ep.d_rot = d; ep.rope_tab = tab; ep.tok_pos = tok; ep.gt = gt; ep.gh = gh;
+    }
+    return op_dev(launch_gemm(dtype, EPI_QKV, Y, D, qkv_w, D, B * N, 3 * D, D, ep, s), "qkv GEMM");
+}
+
+vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt, int32_t B, int32_t N,
+                                  int32_t n_head, int32_t head_dim, int32_t attn_mode, int32_t n_prefix,
+                                  int32_t tokens_per_frame, void *O, void *stream) {
+    clear_error();
+    if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
+    if (!Q || !K || !Vt || !O) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (B <= 0 || N <= 0 || n_head <= 0) return op_fail(VITENC_ESHAPE, "bad sizes");
+    if (head_dim != 64 && head_dim != 32) return op_fail(VITENC_EUNSUPPORTED, "head_dim %d", head_dim);
+    if (attn_mode == 1 && (tokens_per_frame <= 0 || n_prefix < 0 || n_prefix >= N))
+        return op_fail(VITENC_ESHAPE, "block-causal geometry");
+    return op_dev(launch_attention(dtype, Q, K, Vt, B, N, n_head, head_dim, (N + 63) / 64 * 64, attn_mode, n_prefix,
+                                   tokens_per_frame, O, reinterpret_cast<hipStream_t>(stream)),
+                  "attention");
+}
+
+vitenc_status vitenc_op_linear_residual(int32_t dtype, const void *A, const void *W, const float *b, const float *ls,
+                                        int32_t M, int32_t Nout, int32_t K, float *Z, void *stream) {
+    clear_error();
+    if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
+    if (!A || !W || !b || !Z) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (M < 0 || Nout <= 0 || K <= 0) return op_fail(VITENC_ESHAPE, "bad sizes");
+    EpiArgs ep;
+    ep.bias = b; ep.ls = ls; ep.Z = Z; ep.ldz = Nout;
+    return op_dev(launch_gemm(dtype, EPI_RESID, A, K, W, K, M, Nout, K, ep, reinterpret_cast<hipStream_t>(stream)),
+                  "linear residual");
+}
+
+vitenc_status vitenc_op_linear_gelu(int32_t dtype, const void *A, const void *W, const float *b, int32_t M,
+                                    int32_t Nout, int32_t K, void *U, void *stream) {
+    clear_error();
+    if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
+    if (!A || !W || !b || !U) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (M < 0 || Nout <= 0 || K <= 0) return op_fail(VITENC_ESHAPE, "bad sizes");
+    EpiArgs ep;
+    ep.bias = b; ep.out = U; ep.ldo = Nout;
+    return op_dev(launch_gemm(dtype, EPI_GELU, A, K, W, K, M, Nout, K, ep, reinterpret_cast<hipStream_t>(stream)),
+                  "linear gelu");
+}
+
+vitenc_status vitenc_op_pool(const float *X, int32_t B, int32_t N, int32_t D, int32_t cls, int32_t n_prefix,
+                             float *pooled, void *stream) {
+    clear_error();
+    if (!X || !pooled) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (B <= 0 || N <= 0 || D <= 0 || n_prefix < 0 || (!cls && n_prefix >= N))
+        return op_fail(VITENC_ESHAPE, "bad sizes");
+    return op_dev(launch_pool(X, B, N, D, cls, n_prefix, pooled, reinterpret_cast<hipStream_t>(stream)), "pool");
+}
+
+} // extern "C"

@@ -1,0 +1,303 @@
+"""ctypes binding of libvitenc.so (include/vitenc.h).
+
+Argument marshalling only: every step of the encoder runs in the library's
+HIP kernels.  PyTorch provides device memory and the stream.  If the library
+has not been built, lib() raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvitenc.so")
+
+c_i32, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+F32, BF16, F16 = 0, 1, 2
+STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "ENULL", 4: "EWORKSPACE", 5: "EDEVICE", 6: "EUNSUPPORTED"}
+
+
+class VitencError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"vitenc {STATUS.get(status, status)}: {text}")
+        self.status = status
+        self.text = text
+
+
+class Hparams(ctypes.Structure):
+    _fields_ = [(n, c_i32) for n in ("embed_dim", "n_layer", "n_head", "ffn_dim", "patch_size",
+                                      "tubelet_size", "in_chans")] + \
+               [("ln_eps", c_f32), ("rope_theta", c_f32)] + \
+               [(n, c_i32) for n in ("pos_type", "pos_rows", "rope", "rope_layout", "rope_interpolate",
+                                      "rope_ref_grid", "cls_token", "modality_embed", "layer_scale",
+                                      "attn_mode", "dtype")]
+
+
+BLOCK_FIELDS = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "out_w", "out_b", "ln2_w", "ln2_b", "up_w", "up_b",
+                "down_w", "down_b", "ls1", "ls2")
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in BLOCK_FIELDS]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("patch_w", c_vp), ("patch_b", c_vp), ("pos_embed", c_vp), ("cls_token", c_vp),
+                ("mod_embed", c_vp), ("blocks", ctypes.POINTER(BlockWeights)), ("norm_w", c_vp),
+                ("norm_b", c_vp)]
+
+
+_LIB = None
+
+# exported symbol -> (restype, argtypes)
+SIGNATURES = {
+    "vitenc_abi_version": (c_i32, []),
+    "vitenc_error_text": (ctypes.c_char_p, []),
+    "vitenc_model_create": (c_i32, [ctypes.POINTER(Hparams), ctypes.POINTER(Weights), ctypes.POINTER(c_vp)]),
+    "vitenc_model_destroy": (None, [c_vp]),
+    "vitenc_workspace_size": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
+    "vitenc_encode": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp, c_vp, c_vp]),
+    "vitenc_op_embed": (c_i32, [c_i32, c_vp] + [c_i32] * 7 + [c_vp] * 5 + [c_i32, c_vp, c_vp, c_vp]),
+    "vitenc_op_layernorm": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_vp, c_vp]),
+    "vitenc_op_qkv_rope": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 8 + [c_f32] + [c_i32] * 4 +
+                           [c_vp] * 5),
+    "vitenc_rope_table_floats": (ctypes.c_int64, [c_i32] * 4),
+    "vitenc_op_attention": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp]),
+    "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vitenc_op_linear_gelu": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vitenc_op_pool": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+}
+
+
+def lib():
+    """The loaded library.  torch is imported first so that the library binds
+    to the HIP runtime torch already loaded."""
+    global _LIB
+    if _LIB is None:
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m vision_transformer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def check(status: int):
+    if status != 0:
+        raise VitencError(status, lib().vitenc_error_text().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def torch_dtype(dtype: int):
+    import torch
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[dtype]
+
+
+def to_device(arr: np.ndarray, dtype: int, device="cuda"):
+    """Upload a weight matrix held as device-storage numpy (bf16 bits as
+    uint16, f16, or f32)."""
+    import torch
+    if dtype == BF16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == F16:
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def f32_to_device(arr, device="cuda"):
+    import torch
+    if arr is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def make_hparams(hp: Dict) -> Hparams:
+    h = Hparams()
+    for name, _ in Hparams._fields_:
+        setattr(h, name, hp.get(name, 0))
+    return h
+
+
+class Encoder:
+    """A model handle over device-resident weights."""
+
+    def __init__(self, hp: Dict, tensors: Dict, blocks):
+        self.hp = dict(hp)
+        self.tensors = tensors            # keeps device memory alive
+        self.blocks = blocks
+        L = lib()
+        self._hp = make_hparams(self.hp)
+        self._bw = (BlockWeights * len(blocks))()
+        for i, b in enumerate(blocks):
+            for n in BLOCK_FIELDS:
+                setattr(self._bw[i], n, _ptr(b.get(n)))
+        self._w = Weights(_ptr(tensors["patch_w"]), _ptr(tensors["patch_b"]), _ptr(tensors.get("pos")),
+                          _ptr(tensors.get("cls")), _ptr(tensors.get("mod")),
+                          ctypes.cast(self._bw, ctypes.POINTER(BlockWeights)), _ptr(tensors["norm_w"]),
+                          _ptr(tensors["norm_b"]))
+        h = c_vp()
+        check(L.vitenc_model_create(ctypes.byref(self._hp), ctypes.byref(self._w), ctypes.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def from_workload(cls, wl, device="cuda") -> "Encoder":
+        cfg, w = wl.cfg, wl.weights
+        dt = cfg.dtype
+        hp = cfg.hparams()
+        hp["pos_rows"] = 0 if w.pos is None else w.pos.shape[0]
+        t = {"patch_w": to_device(w.store["patch_w"], dt, device), "patch_b": f32_to_device(w.patch_b, device),
+             "pos": f32_to_device(w.pos, device), "cls": f32_to_device(w.cls, device),
+             "mod": f32_to_device(w.mod, device), "norm_w": f32_to_device(w.norm_w, device),
+             "norm_b": f32_to_device(w.norm_b, device)}
+        blocks = []
+        for b in w.blocks:
+            d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
+                 "up_w": to_device(b.store["up_w"], dt, device), "down_w": to_device(b.store["down_w"], dt, device)}
+            for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b", "ls1", "ls2"):
+                d[n] = f32_to_device(getattr(b, n), device)
+            blocks.append(d)
+        return cls(hp, t, blocks)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().vitenc_model_destroy(self.handle)
+            self.handle = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, B, T, H, W) -> int:
+        n = c_size()
+        check(lib().vitenc_workspace_size(self.handle, B, T, H, W, ctypes.byref(n)))
+        return n.value
+
+    def tokens(self, T, H, W) -> int:
+        hp = self.hp
+        return (T // hp["tubelet_size"]) * (H // hp["patch_size"]) * (W // hp["patch_size"]) + \
+            (1 if hp["cls_token"] else 0)
+
+    def alloc(self, B, T, H, W, device="cuda"):
+        """Workspace and outputs for a [B, C, T, H, W] input."""
+        import torch
+        ws = torch.empty(self.workspace_bytes(B, T, H, W), dtype=torch.uint8, device=device)
+        N = self.tokens(T, H, W)
+        D = self.hp["embed_dim"]
+        out = torch.empty((B, N, D), dtype=torch.float32, device=device)
+        pooled = torch.empty((B, D), dtype=torch.float32, device=device)
+        return ws, out, pooled
+
+    def encode_into(self, pixels, ws, out, pooled=None, stream=None):
+        B, C, T, H, W = pixels.shape
+        check(lib().vitenc_encode(self.handle, pixels.data_ptr(), B, T, H, W, ws.data_ptr(), ws.numel(),
+                                  out.data_ptr(), _ptr(pooled), _stream(stream)))
+
+    def encode(self, pixels, stream=None):
+        B, C, T, H, W = pixels.shape
+        ws, out, pooled = self.alloc(B, T, H, W, device=pixels.device)
+        self.encode_into(pixels, ws, out, pooled, stream)
+        return out, pooled
+
+
+# ---------------------------------------------------------------------------
+# step entry points (one kernel or fused pair each)
+# ---------------------------------------------------------------------------
+def op_embed(dtype, pixels, tubelet, patch, patch_w, patch_b, pos=None, cls=None, mod=None, stream=None):
+    import torch
+    B, C, T, H, W = pixels.shape
+    D = patch_w.shape[0]
+    Np = (T // tubelet) * (H // patch) * (W // patch)
+    K = C * tubelet * patch * patch
+    lda = (K + 7) // 8 * 8
+    scratch = torch.empty(B * Np * lda, dtype=torch_dtype(dtype), device=pixels.device)
+    Z = torch.empty((B, Np + (1 if cls is not None else 0), D), dtype=torch.float32, device=pixels.device)
+    check(lib().vitenc_op_embed(dtype, pixels.data_ptr(), B, C, T, H, W, tubelet, patch, patch_w.data_ptr(),
+                                patch_b.data_ptr(), _ptr(pos), _ptr(cls), _ptr(mod), D, scratch.data_ptr(),
+                                Z.data_ptr(), _stream(stream)))
+    return Z
+
+
+def op_layernorm(x, w, b, eps, out_dtype, stream=None, out=None):
+    import torch
+    M, D = x.shape
+    y = torch.empty((M, D), dtype=torch_dtype(out_dtype), device=x.device) if out is None else out
+    check(lib().vitenc_op_layernorm(out_dtype, x.data_ptr(), w.data_ptr(), b.data_ptr(), eps, M, D, y.data_ptr(),
+                                    _stream(stream)))
+    return y
+
+
+def op_qkv_rope(dtype, Y, qkv_w, qkv_b, B, N, n_head, rope=0, rope_layout=0, rope_interpolate=0,
+                rope_ref_grid=0, rope_theta=10000.0, grid=(1, 1, 1), n_prefix=0, stream=None, outs=None):
+    """outs: optional preallocated (Q, K, Vt, rope_table)."""
+    import torch
+    D = Y.shape[1]
+    hd = D // n_head
+    ldv = (N + 63) // 64 * 64
+    td = torch_dtype(dtype)
+    if outs is None:
+        Q = torch.empty((B, n_head, N, hd), dtype=td, device=Y.device)
+        K = torch.empty((B, n_head, N, hd), dtype=td, device=Y.device)
+        Vt = torch.zeros((B, n_head, hd, ldv), dtype=td, device=Y.device)
+        nt = lib().vitenc_rope_table_floats(hd, *grid)
+        tab = torch.empty(max(nt, 1), dtype=torch.float32, device=Y.device)
+    else:
+        Q, K, Vt, tab = outs
+    check(lib().vitenc_op_qkv_rope(dtype, Y.data_ptr(), qkv_w.data_ptr(), qkv_b.data_ptr(), B, N, D, n_head, rope,
+                                   rope_layout, rope_interpolate, rope_ref_grid, rope_theta, grid[0], grid[1],
+                                   grid[2], n_prefix, tab.data_ptr(), Q.data_ptr(), K.data_ptr(), Vt.data_ptr(),
+                                   _stream(stream)))
+    return Q, K, Vt
+
+
+def op_attention(dtype, Q, K, Vt, attn_mode=0, n_prefix=0, tokens_per_frame=0, stream=None, out=None):
+    import torch
+    B, H, N, hd = Q.shape
+    O = torch.empty((B, N, H * hd), dtype=torch_dtype(dtype), device=Q.device) if out is None else out
+    check(lib().vitenc_op_attention(dtype, Q.data_ptr(), K.data_ptr(), Vt.data_ptr(), B, N, H, hd, attn_mode,
+                                    n_prefix, tokens_per_frame, O.data_ptr(), _stream(stream)))
+    return O
+
+
+def op_linear_residual(dtype, A, W, b, Z, ls=None, stream=None):
+    M, K = A.shape
+    Nout = W.shape[0]
+    check(lib().vitenc_op_linear_residual(dtype, A.data_ptr(), W.data_ptr(), b.data_ptr(), _ptr(ls), M, Nout, K,
+                                          Z.data_ptr(), _stream(stream)))
+    return Z
+
+
+def op_linear_gelu(dtype, A, W, b, stream=None, out=None):
+    import torch
+    M, K = A.shape
+    Nout = W.shape[0]
+    U = torch.empty((M, Nout), dtype=torch_dtype(dtype), device=A.device) if out is None else out
+    check(lib().vitenc_op_linear_gelu(dtype, A.data_ptr(), W.data_ptr(), b.data_ptr(), M, Nout, K, U.data_ptr(),
+                                      _stream(stream)))
+    return U
+
+
+def op_pool(X, cls, n_prefix, stream=None):
+    import torch
+    B, N, D = X.shape
+    pooled = torch.empty((B, D), dtype=torch.float32, device=X.device)
+    check(lib().vitenc_op_pool(X.data_ptr(), B, N, D, int(cls), n_prefix, pooled.data_ptr(), _stream(stream)))
+    return pooled
