@@ -1,7 +1,7 @@
 // C ABI of the encoder (include/vitenc.h): validation, workspace planning and
 // the launch sequence of one forward.  Every refusal happens here, before any
 // device work is enqueued; the kernels assume the shapes validated here.
-#include "../../include/vitenc.h"
+#include "vitenc.h"
 
 #include <hip/hip_runtime.h>
 

@@ -13,8 +13,10 @@
 // half of that query's keys sits in lane l ^ 32, so the row max and row sum
 // are in-lane reductions plus one cross-lane exchange.  P^T stays in
 // registers and feeds O^T += V^T P^T directly as the B operand; V arrives
-// already transposed per head (the QKV epilogue writes it that way), so the
-// A operand is read from LDS as 8-byte runs of consecutive keys.
+// already transposed per head (the QKV epilogue writes it that way).  In LDS
+// each 16-key group of a V^T row is stored as [k0-3, k8-11 | k4-7, k12-15],
+// so the 8 keys a lane group contributes to one 32x32x16 MFMA are one
+// 16-byte read.  LDS chunk indices are XOR-swizzled by row (common.h).
 //
 // Mask: query i sees the keys [lo(i), hi(i)):
 //   full attention                 lo = 0, hi = N
@@ -65,8 +67,6 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
     constexpr int KPC = Elem<T>::kPerChunk;
     constexpr int QCH = HD / KPC;     // 16-byte chunks per q/k row
     constexpr int KCH = BKV / KPC;    // 16-byte chunks per V^T row of a tile
-    constexpr int QSW = QCH < 8 ? QCH - 1 : 7;
-    constexpr int VSW = KCH < 8 ? KCH - 1 : 7;
     constexpr int K_PER = BKV * QCH / kThreads;
     constexpr int V_PER = HD * KCH / kThreads;
     constexpr int NDB = HD / 32;      // 32-row blocks of O^T
@@ -145,13 +145,22 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
         for (int i = 0; i < K_PER; ++i) {
             const int e = tid + kThreads * i;
             const int r = e / QCH, c = e % QCH;
-            sK[buf][r][c ^ (r & QSW)] = rk[i];
+            sK[buf][r][c ^ swz<QCH>(r)] = rk[i];
         }
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
             const int e = tid + kThreads * i;
             const int r = e / KCH, c = e % KCH;
-            sV[buf][r][c ^ (r & VSW)] = rv[i];
+            if constexpr (KPC == 8) {
+                // chunk c holds keys 8c..8c+7 = 16u + 8h + (0..7): its halves go to
+                // logical slots 2u (keys +0..3) and 2u+1 (keys +4..7), at byte 8h
+                const int u = c >> 1, h = c & 1;
+                uint2 *row = reinterpret_cast<uint2 *>(&sV[buf][r][0]);
+                row[2 * ((2 * u) ^ swz<KCH>(r)) + h] = make_uint2(rv[i].w[0], rv[i].w[1]);
+                row[2 * ((2 * u + 1) ^ swz<KCH>(r)) + h] = make_uint2(rv[i].w[2], rv[i].w[3]);
+            } else {
+                sV[buf][r][c ^ swz<KCH>(r)] = rv[i];
+            }
         }
     };
 
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                 const int r = 32 * j + l32;
 #pragma unroll
                 for (int s = 0; s < QCH / 2; ++s) {
-                    const Chunk a = sK[cur][r][(2 * s + g) ^ (r & QSW)];
+                    const Chunk a = sK[cur][r][(2 * s + g) ^ swz<QCH>(r)];
                     mfma_chunk<T>(sc[j], a, qf[s]);
                 }
             }
@@ -234,13 +243,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
                             const int r = db * 32 + l32;
-                            const int c0 = 4 * j + 2 * st;
-                            const uint2 lo2 = reinterpret_cast<const uint2 *>(&sV[cur][r][c0 ^ (r & VSW)])[g];
-                            const uint2 hi2 =
-                                reinterpret_cast<const uint2 *>(&sV[cur][r][(c0 + 1) ^ (r & VSW)])[g];
-                            Chunk va;
-                            va.w[0] = lo2.x; va.w[1] = lo2.y; va.w[2] = hi2.x; va.w[3] = hi2.y;
-                            mfma_chunk<T>(o[db], va, pb);
+                            const int slot = 2 * (2 * j + st) + g;
+                            mfma_chunk<T>(o[db], sV[cur][r][slot ^ swz<KCH>(r)], pb);
                         }
                     }
                 } else {
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                         for (int db = 0; db < NDB; ++db) {
                             const int r = db * 32 + l32;
                             const int c = 8 * j + 2 * q4 + g;
-                            mfma_chunk<T>(o[db], sV[cur][r][c ^ (r & VSW)], pb);
+                            mfma_chunk<T>(o[db], sV[cur][r][c ^ swz<KCH>(r)], pb);
                         }
                     }
                 }

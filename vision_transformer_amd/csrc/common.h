@@ -88,6 +88,23 @@ template <> __device__ __forceinline__ void mfma_chunk<float>(f32x16 &acc, const
                                                    __builtin_bit_cast(float, b.w[j]), acc, 0, 0, 0);
 }
 
+// XOR swizzle of the 16-byte chunk index of an LDS row of 8 chunks (128 B).
+// Operand fetches read one chunk per lane from 32 consecutive rows; the LDS
+// serves a 128-bit read per group of lanes covering 128 or 256 bytes of
+// banks, i.e. 8 or 16 consecutive rows.  With this swizzle any 8 consecutive
+// rows use 8 distinct chunk slots, and any 16 consecutive rows use 16
+// distinct (row parity, slot) pairs, so both groupings are conflict-free.
+__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// the same property for rows of 4 chunks (64 B) and of 16 chunks (256 B)
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz16(int row) { return row & 15; }
+template <int NCH> __device__ __forceinline__ int swz(int row) {
+    static_assert(NCH == 4 || NCH == 8 || NCH == 16, "row of 4, 8 or 16 chunks");
+    if constexpr (NCH == 4) return swz4(row);
+    else if constexpr (NCH == 8) return swz8(row);
+    else return swz16(row);
+}
+
 // accumulator row owned by lane group g for accumulator slot i
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 

@@ -5,11 +5,12 @@
 // of one row.  A 256-thread workgroup computes a BM x BN tile as a 2 x 2 grid
 // of waves; each wave owns a (BM/2) x (BN/2) block of 32x32 MFMA tiles with
 // fp32 accumulators.  K advances 128 bytes per step (64 bf16/f16 or 32 fp32
-// elements); the A and W slabs of the next step are fetched into registers
-// while the current step is multiplied out of LDS (two LDS buffers, one
-// barrier per step).  LDS rows are 8 chunks of 16 bytes with the chunk index
-// XOR-swizzled by the row, so the 32 rows a wave reads in one MFMA operand
-// fetch fall on distinct banks.
+// elements); the A and W slabs of step k+2 are fetched into registers while
+// step k is multiplied out of LDS (two LDS buffers, two register staging
+// sets, one barrier per step).  LDS rows are 8 chunks of 16 bytes with the
+// chunk index XOR-swizzled by the row, so the 32 rows a wave reads in one
+// MFMA operand fetch fall on distinct banks (swz8).  The operand fragments of
+// sub-step s+1 are read from LDS while the MFMAs of sub-step s run.
 //
 // Epilogues (jepa.cpp "Architecture", "The shared ViT graph"; "GGUF schema
 // (v1)", "Encoder tensors"):
@@ -64,10 +65,24 @@ __device__ __forceinline__ float gelu_erf(float x) {
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
-template <typename T, int BM, int BN, int EPI, bool ALIGNED>
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8).  Remap so that each XCD receives a contiguous run of tiles; with
+// the N tiles of one M block adjacent, an XCD's L2 serves the A row panel of
+// its tiles instead of every XCD fetching every panel.
+__device__ __forceinline__ int xcd_tile(int b, int nb) {
+    constexpr int kXcd = 8;
+    const int x = b % kXcd, q = nb / kXcd, r = nb % kXcd;
+    return x * q + min(x, r) + b / kXcd;
+}
+
+// FAST: 16-byte aligned rows and K a multiple of the K step, so every load is
+// a full chunk; rows past M / N are clamped to the last row (they only feed
+// accumulator rows / columns that are never stored).  Otherwise loads are
+// element-wise with zero fill past K and past the last row.
+template <typename T, int BM, int BN, int EPI, bool FAST>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__ A, int64_t lda,
                                                            const T *__restrict__ W, int64_t ldw, int M,
-                                                           int N, int K, EpiArgs ep) {
+                                                           int N, int K, int tiles_n, EpiArgs ep) {
     constexpr int KPC = Elem<T>::kPerChunk;
     constexpr int BK = 8 * KPC;
     constexpr int WM = BM / 2, WN = BN / 2;
@@ -81,28 +96,44 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, l32 = lane & 31;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
     const int lc = tid & 7, lr = tid >> 3;
 
-    Chunk ra[A_PER], rb[B_PER];
-    auto gload = [&](int k0) {
+    // per-thread row pointers of the chunks this thread stages
+    const T *pa[A_PER];
+    const T *pb[B_PER];
 #pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            ra[i] = load_tile_chunk<T, ALIGNED>(A, lda, m0 + lr + 32 * i, M, k0 + lc * KPC, K);
+    for (int i = 0; i < A_PER; ++i) pa[i] = A + (int64_t)min(m0 + lr + 32 * i, M - 1) * lda + lc * KPC;
 #pragma unroll
-        for (int i = 0; i < B_PER; ++i)
-            rb[i] = load_tile_chunk<T, ALIGNED>(W, ldw, n0 + lr + 32 * i, N, k0 + lc * KPC, K);
+    for (int i = 0; i < B_PER; ++i) pb[i] = W + (int64_t)min(n0 + lr + 32 * i, N - 1) * ldw + lc * KPC;
+
+    auto gload = [&](Chunk *ra, Chunk *rb, int k0) {
+        if constexpr (FAST) {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i) ra[i] = load_chunk(pa[i] + k0);
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i) rb[i] = load_chunk(pb[i] + k0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_PER; ++i)
+                ra[i] = load_tile_chunk<T, false>(A, lda, m0 + lr + 32 * i, M, k0 + lc * KPC, K);
+#pragma unroll
+            for (int i = 0; i < B_PER; ++i)
+                rb[i] = load_tile_chunk<T, false>(W, ldw, n0 + lr + 32 * i, N, k0 + lc * KPC, K);
+        }
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](const Chunk *ra, const Chunk *rb, int buf) {
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int r = lr + 32 * i;
-            sA[buf][r][lc ^ (r & 7)] = ra[i];
+            sA[buf][r][lc ^ swz8(r)] = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
             const int r = lr + 32 * i;
-            sB[buf][r][lc ^ (r & 7)] = rb[i];
+            sB[buf][r][lc ^ swz8(r)] = rb[i];
         }
     };
 
@@ -114,33 +145,55 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[fm][fn][i] = 0.0f;
 
-    const int nk = (int)cdiv(K, BK);
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload((kt + 1) * BK);
+    auto frags = [&](Chunk *a, Chunk *b, int buf, int s) {
+        const int cc = 2 * s + g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int cc = 2 * s + g;
-            Chunk a[FM], b[FN];
+        for (int fm = 0; fm < FM; ++fm) {
+            const int r = wm * WM + fm * 32 + l32;
+            a[fm] = sA[buf][r][cc ^ swz8(r)];
+        }
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int r = wm * WM + fm * 32 + l32;
-                a[fm] = sA[cur][r][cc ^ (r & 7)];
-            }
+        for (int fn = 0; fn < FN; ++fn) {
+            const int r = wn * WN + fn * 32 + l32;
+            b[fn] = sB[buf][r][cc ^ swz8(r)];
+        }
+    };
+    auto compute = [&](int buf) {
+        Chunk a0[FM], b0[FN], a1[FM], b1[FN];
+        frags(a0, b0, buf, 0);
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int r = wn * WN + fn * 32 + l32;
-                b[fn] = sB[cur][r][cc ^ (r & 7)];
-            }
+        for (int s = 0; s < 4; s += 2) {
+            frags(a1, b1, buf, s + 1);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) mfma_chunk<T>(acc[fm][fn], a[fm], b[fn]);
+                for (int fn = 0; fn < FN; ++fn) mfma_chunk<T>(acc[fm][fn], a0[fm], b0[fn]);
+            if (s + 2 < 4) frags(a0, b0, buf, s + 2);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) mfma_chunk<T>(acc[fm][fn], a1[fm], b1[fn]);
         }
-        if (kt + 1 < nk) sstore(cur ^ 1);
+    };
+
+    // Two LDS buffers and two register staging sets: the slab of step k+2 is
+    // fetched while step k is multiplied, so each load has two compute phases
+    // to land before it is written to LDS.
+    const int nk = (int)cdiv(K, BK);
+    Chunk ra0[A_PER], rb0[B_PER], ra1[A_PER], rb1[B_PER];
+    gload(ra0, rb0, 0);
+    if (nk > 1) gload(ra1, rb1, BK);
+    sstore(ra0, rb0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        if (kt + 2 < nk) gload(ra0, rb0, (kt + 2) * BK);
+        compute(0);
+        if (kt + 1 < nk) sstore(ra1, rb1, 1);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        if (kt + 3 < nk) gload(ra1, rb1, (kt + 3) * BK);
+        compute(1);
+        if (kt + 2 < nk) sstore(ra0, rb0, 0);
         __syncthreads();
     }
 
@@ -241,13 +294,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     }
 }
 
-template <typename T, int EPI, bool ALIGNED>
+template <typename T, int EPI, bool FAST>
 hipError_t launch_t(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K,
                     const EpiArgs &ep, hipStream_t s) {
     constexpr int BM = 128, BN = 128;
-    dim3 grid((unsigned)cdiv(N, BN), (unsigned)cdiv(M, BM));
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, EPI, ALIGNED>), grid, dim3(kThreads), 0, s,
-                       reinterpret_cast<const T *>(A), lda, reinterpret_cast<const T *>(W), ldw, M, N, K, ep);
+    const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, EPI, FAST>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0,
+                       s, reinterpret_cast<const T *>(A), lda, reinterpret_cast<const T *>(W), ldw, M, N, K, tiles_n,
+                       ep);
     return hipGetLastError();
 }
 
@@ -255,9 +309,9 @@ template <typename T, int EPI>
 hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K,
                         const EpiArgs &ep, hipStream_t s) {
     constexpr int KPC = Elem<T>::kPerChunk;
-    const bool aligned = (K % KPC == 0) && (lda % KPC == 0) && (ldw % KPC == 0) &&
-                         ((uintptr_t)A % 16 == 0) && ((uintptr_t)W % 16 == 0);
-    if (aligned) return launch_t<T, EPI, true>(A, lda, W, ldw, M, N, K, ep, s);
+    const bool fast = (K % (8 * KPC) == 0) && (lda % KPC == 0) && (ldw % KPC == 0) &&
+                      ((uintptr_t)A % 16 == 0) && ((uintptr_t)W % 16 == 0);
+    if (fast) return launch_t<T, EPI, true>(A, lda, W, ldw, M, N, K, ep, s);
     return launch_t<T, EPI, false>(A, lda, W, ldw, M, N, K, ep, s);
 }
 

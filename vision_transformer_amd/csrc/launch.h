@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/vitenc.h"
+#include "vitenc.h"
 
 namespace vitenc {
 

@@ -1,6 +1,6 @@
 // Step entry points of include/vitenc.h: one step of the encoder graph each,
 // running the same launchers as vitenc_encode.
-#include "../../include/vitenc.h"
+#include "vitenc.h"
 
 #include <hip/hip_runtime.h>
 
