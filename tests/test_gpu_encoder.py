@@ -70,13 +70,28 @@ SMALL = {
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_clip_full_depth(gpu_lib, name):
-    _parity(SMALL[name])
+def test_small_clip_full_depth_fp32(gpu_lib, name):
+    """Every family at full depth on the fp32 path (the same token assembly,
+    RoPE, mask and pooling code as bf16, with rounding far below the gate)."""
+    _parity(SMALL[name].replace(dtype=W.DTYPE_F32))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_clip_bf16(gpu_lib, name):
+    """Every family on the bf16 path at 8 layers (bf16 activation rounding
+    alone brings a 24-layer small clip to the max-abs gate; the full-depth
+    bf16 configs are checked against the stored oracle samples)."""
+    _parity(SMALL[name].replace(n_layer=8))
 
 
 @pytest.mark.parametrize("name", ["vjepa2", "vjepa21", "levjepa", "hfvit"])
 def test_sensitised_small_clip(gpu_lib, name):
-    cfg = W.sensitised(SMALL[name].replace(n_layer=4), std_qk=0.1, std_tok=1.0)
+    """Large q/k rows and CLS / modality vectors, under which a wrong RoPE
+    layout, a missing interpolation, an open CLS column or a dropped modality
+    vector fails the gates (tests/test_negative_controls.py plants each one
+    in the oracle).  Run on the fp32 path: with such peaked attention, bf16
+    rounding of q and k alone moves the output past the bf16 gate."""
+    cfg = W.sensitised(SMALL[name].replace(n_layer=4, dtype=W.DTYPE_F32), std_qk=0.1, std_tok=1.0)
     _parity(cfg)
 
 

@@ -1,0 +1,41 @@
+"""The five workloads at full size and full depth on the GPU, against the CPU
+oracle's full-depth outputs stored in tests/golden/oracle_<name>.npz (written
+by tests/golden/make_oracle_samples.py, which calls only the oracle).  Every
+token is encoded; the stored sampled token rows (prefix, frame boundaries,
+last row and seeded random rows) and the pooled features are compared at the
+gates: fp32 max relative error <= 1e-4; bf16 per-token cosine >= 0.9999 and
+max abs error <= 2e-2."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from vision_transformer_amd import workloads as W
+
+from gpu_util import gates_ok, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_full_depth_against_oracle_samples(gpu_lib, idx):
+    cfg = W.CONFIGS[idx]
+    path = os.path.join(GOLDEN, f"oracle_{cfg.name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    ref = np.load(path)
+    assert int(ref["n_layer"]) == cfg.n_layer and int(ref["seed"]) == cfg.seed
+    say(f"full depth {cfg.name}: B={cfg.batch} N={cfg.n_tokens} L={cfg.n_layer}")
+    wl = W.make_workload(cfg)
+    out, pooled = run_gpu(wl)
+    rows = ref["rows"]
+    st_tok = oracle.compare(out[:, rows], ref["tokens"])
+    st_pool = oracle.compare(pooled, ref["pooled"])
+    say(f"  tokens {st_tok}\n  pooled {st_pool}")
+    assert np.isfinite(out).all()
+    assert gates_ok(cfg, st_tok), st_tok
+    assert gates_ok(cfg, st_pool), st_pool

@@ -191,3 +191,56 @@ def test_pool(gpu_lib, cls, p):
     got = to_np(V.op_pool(dev(X), cls, p))
     ref = X[:, 0] if cls else X[:, p:].astype(np.float64).mean(1)
     assert np.abs(got - ref).max() < 1e-5
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
+def test_linear_wide_tiles(gpu_lib, dtype):
+    """Shapes with enough tiles for the 256 x 256 direct-to-LDS kernel, with a
+    ragged last row block (M = 4133)."""
+    from vision_transformer_amd import vitenc as V
+    M, N, K = 4133, 4096, 256
+    say(f"linear wide dtype={dtype} M={M} N={N} K={K}")
+    rng = np.random.default_rng(11)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    Wt = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(N) * 0.1).astype(np.float32)
+    ls = (1 + 0.2 * rng.standard_normal(N)).astype(np.float32)
+    Ae, We = exact(A, dtype), exact(Wt, dtype)
+    U = V.op_linear_gelu(dtype, dev(A, dtype), dev(Wt, dtype), dev(b))
+    Z0 = rng.standard_normal((M, N)).astype(np.float32)
+    Zd = dev(Z0)
+    V.op_linear_residual(dtype, dev(A, dtype), dev(Wt, dtype), dev(b), Zd, ls=dev(ls))
+    torch.cuda.synchronize()
+    lin = oracle.linear(Ae, We, b)
+    ref_u = oracle.gelu_erf(lin)
+    acc_tol = 1e-5 * np.abs(lin).max()
+    assert np.abs(to_np(U) - ref_u).max() <= out_tol(dtype) * np.abs(ref_u).max() + acc_tol
+    assert np.abs(to_np(Zd) - (Z0 + ls * lin)).max() <= acc_tol * 4 + 1e-6
+
+
+def test_qkv_rope_wide_tiles(gpu_lib):
+    """QKV at 2 x 2047 tokens (CLS + 2 x 31 x 33 grid), D 1024: the 256 x 192
+    direct-to-LDS kernel with the RoPE epilogue and a ragged last block."""
+    from vision_transformer_amd import vitenc as V
+    dtype = W.DTYPE_BF16
+    B, (gt, gh, gw), p, H, hd = 2, (2, 31, 33), 1, 16, 64
+    D = H * hd
+    N = gt * gh * gw + p
+    say(f"qkv_rope wide B={B} N={N} D={D}")
+    rng = np.random.default_rng(13)
+    Y = rng.standard_normal((B * N, D)).astype(np.float32)
+    Wq = (rng.standard_normal((3 * D, D)) * 0.05).astype(np.float32)
+    bq = (rng.standard_normal(3 * D) * 0.1).astype(np.float32)
+    Q, K, Vt = V.op_qkv_rope(dtype, dev(Y, dtype), dev(Wq, dtype), dev(bq), B, N, H, rope=1,
+                             rope_layout=W.LAYOUT_TILED, grid=(gt, gh, gw), n_prefix=p)
+    torch.cuda.synchronize()
+    qkv = oracle.linear(exact(Y, dtype), exact(Wq, dtype), bq).reshape(B, N, 3, H, hd)
+    q = qkv[:, :, 0].transpose(0, 2, 1, 3).copy()
+    k = qkv[:, :, 1].transpose(0, 2, 1, 3).copy()
+    v = qkv[:, :, 2].transpose(0, 2, 1, 3)
+    pos = oracle.rope_positions(gt * gh * gw, (gt, gh, gw), False, 0)
+    q[:, :, p:] = oracle.rope3d_apply(q[:, :, p:], pos, W.LAYOUT_TILED, 1e4)
+    k[:, :, p:] = oracle.rope3d_apply(k[:, :, p:], pos, W.LAYOUT_TILED, 1e4)
+    tol = out_tol(dtype) * 2
+    for got, ref in ((to_np(Q), q), (to_np(K), k), (to_np(Vt)[..., :N].transpose(0, 1, 3, 2), v)):
+        assert np.abs(got - ref).max() <= tol * np.abs(ref).max() + 1e-5

@@ -268,6 +268,7 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
             ep.rope = hp.rope;
             ep.d_rot = 2 * ((pl.hd / 3) / 2);
             ep.rope_tab = rope_tab; ep.tok_pos = tok_pos;
+            ep.rope_tab_pairs = (pl.gt + pl.gh + pl.gw) * ep.d_rot;
             ep.gt = pl.gt; ep.gh = pl.gh;
             CHECK_DEV(launch_gemm(dt, EPI_QKV, Y, D, bw.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
         }

@@ -105,6 +105,20 @@ template <int NCH> __device__ __forceinline__ int swz(int row) {
     else return swz16(row);
 }
 
+// 16x16x32 MFMA tiles (16-bit types): lane l supplies row (l % 16) of A /
+// column (l % 16) of B and the 8 k values of lane group q = l / 16 (one
+// 16-byte chunk); the accumulator holds, in lane l, column (l % 16) and rows
+// 4*q + i, i = 0..3.
+template <typename T> __device__ __forceinline__ void mfma16_chunk(f32x4 &acc, const Chunk &a, const Chunk &b);
+template <> __device__ __forceinline__ void mfma16_chunk<bf16_t>(f32x4 &acc, const Chunk &a, const Chunk &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mfma16_chunk<f16_t>(f32x4 &acc, const Chunk &a, const Chunk &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), acc,
+                                                 0, 0, 0);
+}
+
 // accumulator row owned by lane group g for accumulator slot i
 __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
 

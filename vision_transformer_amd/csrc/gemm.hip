@@ -21,6 +21,9 @@
 //   QKV    split [q; k; v] into heads, 3-D RoPE on q and k of patch tokens
 //          ("Architecture", "3-D RoPE"), V written transposed per head
 // where v = accumulator + bias.
+#include <climits>
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -33,8 +36,9 @@ constexpr int kThreads = 256;
 struct RowInfo {
     int out_row; // PATCH: token row in Z; QKV: item index b
     int tok;     // QKV: token index inside the item
-    int pos;     // PATCH: pos-table row; QKV: packed (t,h,w) or -1 for prefix tokens
-    int pad;
+    int pos;     // PATCH: pos-table row; QKV: 1 if the row is rotated (a patch token), else 0
+    int base[3]; // QKV: first table entry of this row's position on axis t, h, w
+    int pad[2];
 };
 
 template <typename T, bool ALIGNED>
@@ -61,8 +65,35 @@ __device__ __forceinline__ Chunk load_tile_chunk(const T *__restrict__ base, int
     }
 }
 
+// 8 consecutive outputs from fp32: one 16-byte store for 16-bit types, two for fp32
+template <typename T> __device__ __forceinline__ void store_vec8(T *dst, const float (&v)[8]) {
+    if constexpr (sizeof(T) == 4) {
+        reinterpret_cast<float4 *>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        Chunk c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c.w[e] = bits16(from_f32<T>(v[2 * e])) | (bits16(from_f32<T>(v[2 * e + 1])) << 16);
+        store_chunk(dst, c);
+    }
+}
+
+// GELU(x) = x/2 (1 + erf(x / sqrt 2)), with erf from the rational
+// approximation 7.1.26 of Abramowitz & Stegun (Handbook of Mathematical
+// Functions): erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-z^2},
+// t = 1 / (1 + p z), z >= 0, |error| <= 1.5e-7, and erf(-z) = -erf(z).
 __device__ __forceinline__ float gelu_erf(float x) {
-    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+    const float z = fabsf(x) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    poly *= t;
+    const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+    const float erf_abs = fmaf(-poly, e, 1.0f);
+    const float erf = x < 0.0f ? -erf_abs : erf_abs;
+    return 0.5f * x * (1.0f + erf);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
@@ -73,6 +104,219 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
     constexpr int kXcd = 8;
     const int x = b % kXcd, q = nb / kXcd, r = nb % kXcd;
     return x * q + min(x, r) + b / kXcd;
+}
+
+// Epilogue of one workgroup tile: v = accumulator + bias, then the EPI
+// operation.  Each wave stages one MI-row block of its accumulators at a time
+// through a private LDS area (MI x (WN + 4) fp32) and reads it back so that
+// every lane owns 8 consecutive columns of one row: loads and stores of the
+// outputs are then 16-byte, row-contiguous vectors instead of per-element
+// accesses.  The V part of the QKV projection is read back transposed (8
+// consecutive rows of one column) because V is stored transposed per head.
+// ri: LDS scratch for BM row descriptors, stage: this wave's staging area.
+// Every thread of the workgroup must call this (it contains a barrier).
+template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, typename AccT>
+__device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, float *stage, float2 *lds_tab,
+                                              int lds_tab_cap, int m0, int n0, int woff_m, int woff_n, int M, int N,
+                                              const EpiArgs &ep) {
+    constexpr int NV = MI == 32 ? 16 : 4; // accumulator values per lane per block
+    constexpr int LD = WN + 4;            // staging row stride (floats), 16-byte aligned
+    constexpr int CPR = WN / 8;           // 8-column groups per row
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int lcol = lane & (MI - 1);
+    auto vrow = [&](int i) { return MI == 32 ? acc_row(i, lane >> 5) : 4 * (lane >> 4) + i; };
+
+    if constexpr (EPI == EPI_PATCH || EPI == EPI_QKV) {
+        for (int t = tid; t < BM; t += NT) {
+            const int row = m0 + t;
+            RowInfo info{0, 0, 0, {0, 0, 0}, {0, 0}};
+            if (row < M) {
+                if constexpr (EPI == EPI_PATCH) {
+                    const int b = row / ep.Np, n = row - b * ep.Np;
+                    info.out_row = b * ep.Ntok + ep.prefix + n;
+                    info.pos = ep.prefix + n;
+                } else {
+                    const int b = row / ep.Ntok, tok = row - b * ep.Ntok;
+                    info.out_row = b;
+                    info.tok = tok;
+                    info.pos = 0;
+                    if (ep.rope && tok >= ep.prefix) {
+                        const int pk = ep.tok_pos[tok - ep.prefix];
+                        info.pos = 1;
+                        info.base[0] = (pk & 1023) * ep.d_rot;
+                        info.base[1] = (ep.gt + ((pk >> 10) & 1023)) * ep.d_rot;
+                        info.base[2] = (ep.gt + ep.gh + ((pk >> 20) & 1023)) * ep.d_rot;
+                    }
+                }
+            }
+            ri[t] = info;
+        }
+    }
+    // the RoPE table goes to LDS when it fits (it is read once per element)
+    const float2 *tab = reinterpret_cast<const float2 *>(ep.rope_tab);
+    if constexpr (EPI == EPI_QKV) {
+        if (ep.rope && ep.rope_tab_pairs <= lds_tab_cap) {
+            for (int t = tid; t < ep.rope_tab_pairs; t += NT) lds_tab[t] = tab[t];
+            tab = lds_tab;
+        }
+    }
+    __syncthreads();
+
+    // Row path: lane -> (row, 8-column group).  A lane's 8 columns are the
+    // same for every row it handles, so everything that depends only on the
+    // column (bias, layer scale, QKV head geometry, RoPE axis and table
+    // column) is set up once here.
+    const int c0 = (lane % CPR) * 8;
+    const int col0 = n0 + woff_n + c0;
+    const bool col_any = col0 < N;
+    const bool col_full = col0 + 8 <= N;
+    float bias8[8], ls8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bool ok = col0 + j < N;
+        bias8[j] = (ok && ep.bias) ? ep.bias[col0 + j] : 0.0f;
+        ls8[j] = (ok && ep.ls) ? ep.ls[col0 + j] : 1.0f;
+    }
+    int which = 0, head = 0, dd0 = 0;
+    int axis8[8], jr8[8];
+    if constexpr (EPI == EPI_QKV) {
+        which = col0 / ep.D;
+        const int within = col0 - which * ep.D;
+        head = within / ep.head_dim;
+        dd0 = within - head * ep.head_dim;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int dd = dd0 + j;
+            const int ax = dd >= 3 * ep.d_rot ? 3 : dd >= 2 * ep.d_rot ? 2 : dd >= ep.d_rot ? 1 : 0;
+            axis8[j] = ax; // 3: not rotated
+            jr8[j] = dd - (ax < 3 ? ax : 0) * ep.d_rot;
+        }
+    }
+    const bool qk_cols = EPI == EPI_QKV && which < 2;
+
+    auto row_path = [&](int rt, const float (&x)[8]) {
+        const int row = m0 + rt;
+        if (row >= M || !col_any) return;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = x[j] + bias8[j];
+        if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+            if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = gelu_erf(v[j]);
+            }
+            T *dst = reinterpret_cast<T *>(ep.out) + (int64_t)row * ep.ldo + col0;
+            if (col_full && (ep.ldo % 8) == 0) {
+                store_vec8<T>(dst, v);
+            } else {
+                for (int j = 0; j < 8; ++j)
+                    if (col0 + j < N) dst[j] = from_f32<T>(v[j]);
+            }
+        } else if constexpr (EPI == EPI_RESID) {
+            float *z = ep.Z + (int64_t)row * ep.ldz + col0;
+            if (col_full && (ep.ldz % 4) == 0) {
+                float4 z0 = reinterpret_cast<const float4 *>(z)[0], z1 = reinterpret_cast<const float4 *>(z)[1];
+                z0.x += ls8[0] * v[0]; z0.y += ls8[1] * v[1]; z0.z += ls8[2] * v[2]; z0.w += ls8[3] * v[3];
+                z1.x += ls8[4] * v[4]; z1.y += ls8[5] * v[5]; z1.z += ls8[6] * v[6]; z1.w += ls8[7] * v[7];
+                reinterpret_cast<float4 *>(z)[0] = z0;
+                reinterpret_cast<float4 *>(z)[1] = z1;
+            } else {
+                for (int j = 0; j < 8; ++j)
+                    if (col0 + j < N) z[j] += ls8[j] * v[j];
+            }
+        } else if constexpr (EPI == EPI_PATCH) {
+            const RowInfo info = ri[rt];
+            float *z = ep.Z + (int64_t)info.out_row * ep.ldz + col0;
+            for (int j = 0; j < 8; ++j) {
+                if (col0 + j >= N) break;
+                float y = v[j];
+                if (ep.pos) y += ep.pos[(int64_t)info.pos * ep.ldz + col0 + j];
+                if (ep.mod) y += ep.mod[col0 + j];
+                z[j] = y;
+            }
+        } else if constexpr (EPI == EPI_QKV) {
+            if (!qk_cols) return; // V columns go through the transposed path
+            const RowInfo info = ri[rt];
+            if (ep.rope && info.pos) {
+                float y[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    y[j] = v[j];
+                    if (axis8[j] < 3) {
+                        const int base = axis8[j] == 0 ? info.base[0] : axis8[j] == 1 ? info.base[1] : info.base[2];
+                        const float2 cs = tab[base + jr8[j]];
+                        y[j] = v[j] * cs.x + v[j ^ 1] * cs.y;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = y[j];
+            }
+            const int H = ep.D / ep.head_dim;
+            T *dst = reinterpret_cast<T *>(which == 0 ? ep.Q : ep.K) +
+                     (((int64_t)info.out_row * H + head) * ep.Ntok + info.tok) * ep.head_dim + dd0;
+            store_vec8<T>(dst, v);
+        }
+    };
+
+#pragma clang loop unroll(full)
+    for (int fm = 0; fm < FM; ++fm) {
+        // stage block row fm of this wave's accumulators
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) stage[vrow(i) * LD + fn * MI + lcol] = acc[fm][fn][i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // row path: lane -> (row, 8-column group)
+        constexpr int RPP = 64 / CPR; // rows per pass
+        for (int r0 = 0; r0 < MI; r0 += RPP) {
+            const int r = r0 + lane / CPR;
+            if (r < MI && lane < RPP * CPR) {
+                const float4 x0 = *reinterpret_cast<const float4 *>(&stage[r * LD + c0]);
+                const float4 x1 = *reinterpret_cast<const float4 *>(&stage[r * LD + c0 + 4]);
+                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                row_path(woff_m + fm * MI + r, x);
+            }
+        }
+        if constexpr (EPI == EPI_QKV) {
+            // V columns: lane -> (column, 8 consecutive rows), stored along tokens
+            const int cbase = n0 + woff_n;
+            if (cbase + WN > 2 * ep.D) {
+                const int H = ep.D / ep.head_dim;
+                for (int cc = lane; cc < WN * (MI / 8); cc += 64) {
+                    const int c = cc % WN, rg = cc / WN;
+                    const int col = cbase + c;
+                    if (col < 2 * ep.D || col >= N) continue;
+                    const float bias = ep.bias ? ep.bias[col] : 0.0f;
+                    const int within = col - 2 * ep.D;
+                    const int head = within / ep.head_dim, dd = within - head * ep.head_dim;
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = stage[(rg * 8 + e) * LD + c] + bias;
+                    const int rt0 = woff_m + fm * MI + rg * 8;
+                    const RowInfo i0 = ri[rt0];
+                    const bool vec = (m0 + rt0 + 7 < M) && (i0.tok % 8 == 0) && (i0.tok + 8 <= ep.Ntok);
+                    if (vec) {
+                        T *dst = reinterpret_cast<T *>(ep.Vt) +
+                                 (((int64_t)i0.out_row * H + head) * ep.head_dim + dd) * ep.ldv + i0.tok;
+                        store_vec8<T>(dst, v);
+                    } else {
+                        for (int e = 0; e < 8; ++e) {
+                            if (m0 + rt0 + e >= M) break;
+                            const RowInfo ie = ri[rt0 + e];
+                            T *dst = reinterpret_cast<T *>(ep.Vt) +
+                                     (((int64_t)ie.out_row * H + head) * ep.head_dim + dd) * ep.ldv + ie.tok;
+                            *dst = from_f32<T>(v[e]);
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 }
 
 // FAST: 16-byte aligned rows and K a multiple of the K step, so every load is
@@ -90,10 +334,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     constexpr int A_PER = BM * 8 / kThreads, B_PER = BN * 8 / kThreads;
     static_assert(FM >= 1 && FN >= 1 && A_PER >= 1 && B_PER >= 1, "tile too small");
 
-    __shared__ Chunk sA[2][BM][8];
-    __shared__ Chunk sB[2][BN][8];
+    // A rows [0, BM) and W rows [BM, BM + BN) of each buffer
+    __shared__ Chunk smem[2][BM + BN][8];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, l32 = lane & 31;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -128,12 +373,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 #pragma unroll
         for (int i = 0; i < A_PER; ++i) {
             const int r = lr + 32 * i;
-            sA[buf][r][lc ^ swz8(r)] = ra[i];
+            smem[buf][r][lc ^ swz8(r)] = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_PER; ++i) {
             const int r = lr + 32 * i;
-            sB[buf][r][lc ^ swz8(r)] = rb[i];
+            smem[buf][BM + r][lc ^ swz8(BM + r)] = rb[i];
         }
     };
 
@@ -150,12 +395,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             const int r = wm * WM + fm * 32 + l32;
-            a[fm] = sA[buf][r][cc ^ swz8(r)];
+            a[fm] = smem[buf][r][cc ^ swz8(r)];
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int r = wn * WN + fn * 32 + l32;
-            b[fn] = sB[buf][r][cc ^ swz8(r)];
+            const int r = BM + wn * WN + fn * 32 + l32;
+            b[fn] = smem[buf][r][cc ^ swz8(r)];
         }
     };
     auto compute = [&](int buf) {
@@ -197,101 +442,202 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
         __syncthreads();
     }
 
-    // ---------------------------------------------------------------- epilogue
-    RowInfo *ri = reinterpret_cast<RowInfo *>(&sA[0][0][0]);
-    if constexpr (EPI == EPI_PATCH || EPI == EPI_QKV) {
-        if (tid < BM) {
-            const int row = m0 + tid;
-            RowInfo info{0, 0, -1, 0};
-            if (row < M) {
-                if constexpr (EPI == EPI_PATCH) {
-                    const int b = row / ep.Np, n = row - b * ep.Np;
-                    info.out_row = b * ep.Ntok + ep.prefix + n;
-                    info.pos = ep.prefix + n;
-                } else {
-                    const int b = row / ep.Ntok, tok = row - b * ep.Ntok;
-                    info.out_row = b;
-                    info.tok = tok;
-                    info.pos = (ep.rope && tok >= ep.prefix) ? ep.tok_pos[tok - ep.prefix] : -1;
-                }
-            }
-            ri[tid] = info;
-        }
-        __syncthreads();
-    }
+    char *sbase = reinterpret_cast<char *>(&smem[0][0][0]);
+    constexpr int kRiBytes = (BM * (int)sizeof(RowInfo) + 255) / 256 * 256;
+    constexpr int kStageBytes = 4 * 32 * (WN + 4) * 4;
+    static_assert(kRiBytes + kStageBytes <= (int)sizeof(smem), "epilogue staging exceeds LDS");
+    RowInfo *ri = reinterpret_cast<RowInfo *>(sbase);
+    float *stage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * 32 * (WN + 4);
+    float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
+    constexpr int kTabCap = ((int)sizeof(smem) - kRiBytes - kStageBytes) / 8;
+    gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN>(acc, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M,
+                                                        N, ep);
+}
 
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wide-tile variant for shapes with enough tiles to fill the chip: a BM x BN
+// tile per workgroup of WGM x WGN waves, each wave owning a (BM/WGM) x
+// (BN/WGN) block of 32x32 MFMA tiles, so one 16-byte operand fragment read
+// from LDS feeds several MFMAs.  Slabs of BK = 8*NCH bytes per row go from
+// global memory straight into LDS with buffer loads (lane l of a load
+// instruction writes bytes [16 l, 16 l + 16) of a 1 KB LDS run; rows past M
+// or N lie outside the buffer resource and read as zero), so no staging
+// registers are needed; the LDS swizzle is applied on the global side by
+// choosing which chunk each lane fetches.  A ring of STAGES LDS stages keeps
+// STAGES - 1 slabs in flight while one is multiplied.  Requires the FAST
+// conditions (K a multiple of the slab width, 16-byte aligned rows).
+template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
+                                                                     const T *__restrict__ W, int64_t ldw, int M,
+                                                                     int N, int K, int tiles_n, int a_bytes,
+                                                                     int b_bytes, EpiArgs ep) {
+    constexpr int KPC = Elem<T>::kPerChunk;
+    constexpr int BK = NCH * KPC;
+    constexpr int NW = WGM * WGN, NT = 64 * NW;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int FM = WM / MI, FN = WN / MI;
+    using AccT = typename std::conditional<MI == 32, f32x16, f32x4>::type;
+    constexpr int NV = MI == 32 ? 16 : 4;
+    constexpr int RPI = 64 / NCH;                       // slab rows per load instruction
+    constexpr int AI = BM / (RPI * NW), BI = BN / (RPI * NW); // load instructions per wave and slab
+    constexpr int SROWS = BM + BN;                      // LDS rows per stage
+    static_assert(NCH == 4 || NCH == 8, "slab of 64 or 128 bytes per row");
+    static_assert(WM % MI == 0 && WN % MI == 0 && AI * RPI * NW == BM && BI * RPI * NW == BN, "tile");
+    static_assert(MI == 32 || MI == 16, "MFMA tile");
+
+    __shared__ Chunk lds[STAGES][SROWS][NCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 5, l32 = lane & 31;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // Buffer loads: one resource per operand, a per-lane byte offset and a
+    // scalar offset for the slab and the instruction's row block.  Lane l of
+    // load instruction j fetches row RPI*j + l/NCH of the wave's share of the
+    // slab; the swizzled chunk of rows RPI*j + r depends on j only through
+    // its parity (8-chunk rows), or not at (4-chunk rows), so two lane
+    // offsets cover every instruction.
+    constexpr uint32_t ES = sizeof(T);
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)W, 0, b_bytes, 0x00020000);
+    const int lrow = lane / NCH, lch = lane % NCH;
+    const int sw0 = swz<NCH>(lrow), sw1 = swz<NCH>(lrow + RPI); // row parity 0 / 1 of 8-row blocks
+    const uint32_t va0 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw0) * KPC) * ES);
+    const uint32_t va1 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw1) * KPC) * ES);
+    const uint32_t vb0 = (uint32_t)(((int64_t)(n0 + wave * BI * RPI + lrow) * ldw + (lch ^ sw0) * KPC) * ES);
+    const uint32_t vb1 = (uint32_t)(((int64_t)(n0 + wave * BI * RPI + lrow) * ldw + (lch ^ sw1) * KPC) * ES);
+    auto issue = [&](int stage, int k0) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        const int col = n0 + wn * WN + fn * 32 + l32;
-        const bool col_ok = col < N;
-        const float bias = (col_ok && ep.bias) ? ep.bias[col] : 0.0f;
-        float lsv = 1.0f;
-        if constexpr (EPI == EPI_RESID) {
-            if (col_ok && ep.ls) lsv = ep.ls[col];
+        for (int j = 0; j < AI; ++j) {
+            const int row = (wave * AI + j) * RPI;
+            const uint32_t soff = (uint32_t)((k0 + (int64_t)j * RPI * lda) * ES);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t *)&lds[stage][row][0], 16,
+                                                     ((row / RPI) & 1) ? va1 : va0, soff, 0, 0);
         }
-        // QKV column geometry
-        int which = 0, head = 0, dd = 0, axis = 0, jrot = 0, tab_base = 0;
-        bool rot = false;
-        if constexpr (EPI == EPI_QKV) {
-            which = col / ep.D;
-            const int within = col - which * ep.D;
-            head = within / ep.head_dim;
-            dd = within - head * ep.head_dim;
-            rot = ep.rope && which < 2 && dd < 3 * ep.d_rot;
-            if (rot) {
-                axis = dd / ep.d_rot;
-                jrot = dd - axis * ep.d_rot;
-                tab_base = (axis == 0 ? 0 : axis == 1 ? ep.gt : ep.gt + ep.gh) * ep.d_rot;
-            }
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            const int row = (wave * BI + j) * RPI;
+            const uint32_t soff = (uint32_t)((k0 + (int64_t)j * RPI * ldw) * ES);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t *)&lds[stage][BM + row][0], 16,
+                                                     (((BM + row) / RPI) & 1) ? vb1 : vb0, soff, 0, 0);
         }
+    };
+
+    AccT acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) acc[fm][fn][i] = 0.0f;
+
+    // one MFMA k-step: 32x32x16 consumes chunk 2s + (l/32); 16x16x32 consumes
+    // chunk 4s + (l/16) of each operand row
+    constexpr int KSUB = MI == 32 ? NCH / 2 : NCH / 4;
+    const int lr = lane & (MI - 1);
+    const int lq = MI == 32 ? (lane >> 5) : (lane >> 4);
+    auto frags = [&](Chunk *a, Chunk *b, int stage, int s) {
+        const int cc = (MI == 32 ? 2 : 4) * s + lq;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
+            const int r = wm * WM + fm * MI + lr;
+            a[fm] = lds[stage][r][cc ^ swz<NCH>(r)];
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = wm * WM + fm * 32 + acc_row(i, g);
-                const int row = m0 + r;
-                float v = acc[fm][fn][i] + bias;
-                if constexpr (EPI == EPI_QKV) {
-                    const float partner = __shfl_xor(v, 1, 64);
-                    if (row < M && col_ok) {
-                        const RowInfo info = ri[r];
-                        if (rot && info.pos >= 0) {
-                            const int p = (info.pos >> (10 * axis)) & 1023;
-                            const float2 cs =
-                                reinterpret_cast<const float2 *>(ep.rope_tab)[tab_base + p * ep.d_rot + jrot];
-                            v = v * cs.x + partner * cs.y;
-                        }
-                        const int H = ep.D / ep.head_dim;
-                        const int64_t bh = (int64_t)info.out_row * H + head;
-                        if (which < 2) {
-                            T *dst = reinterpret_cast<T *>(which == 0 ? ep.Q : ep.K);
-                            dst[(bh * ep.Ntok + info.tok) * ep.head_dim + dd] = from_f32<T>(v);
-                        } else {
-                            T *dst = reinterpret_cast<T *>(ep.Vt);
-                            dst[(bh * ep.head_dim + dd) * ep.ldv + info.tok] = from_f32<T>(v);
-                        }
-                    }
-                } else {
-                    if (row < M && col_ok) {
-                        if constexpr (EPI == EPI_STORE) {
-                            reinterpret_cast<T *>(ep.out)[(int64_t)row * ep.ldo + col] = from_f32<T>(v);
-                        } else if constexpr (EPI == EPI_GELU) {
-                            reinterpret_cast<T *>(ep.out)[(int64_t)row * ep.ldo + col] = from_f32<T>(gelu_erf(v));
-                        } else if constexpr (EPI == EPI_RESID) {
-                            float *z = ep.Z + (int64_t)row * ep.ldz + col;
-                            *z = *z + lsv * v;
-                        } else if constexpr (EPI == EPI_PATCH) {
-                            const RowInfo info = ri[r];
-                            float x = v;
-                            if (ep.pos) x += ep.pos[(int64_t)info.pos * ep.ldz + col];
-                            if (ep.mod) x += ep.mod[col];
-                            ep.Z[(int64_t)info.out_row * ep.ldz + col] = x;
-                        }
-                    }
+        for (int fn = 0; fn < FN; ++fn) {
+            const int r = BM + wn * WN + fn * MI + lr;
+            b[fn] = lds[stage][r][cc ^ swz<NCH>(r)];
+        }
+    };
+    auto mfmas = [&](const Chunk *a, const Chunk *b) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                if constexpr (MI == 32) mfma_chunk<T>(acc[fm][fn], a[fm], b[fn]);
+                else mfma16_chunk<T>(acc[fm][fn], a[fm], b[fn]);
+            }
+    };
+    // keep the next sub-step's fragment reads ahead of this sub-step's MFMAs
+    auto order_reads_first = [&]() {
+        __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0); // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0); // MFMAs
+    };
+    // Wait until this wave's loads of one slab have landed while `later`
+    // slabs issued after it may still be in flight, then barrier: every
+    // wave's part of the slab is visible and every wave has finished reading
+    // what it read before.
+    auto wait_slab = [&](int later) {
+        if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (AI + BI)) : "memory");
+        else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AI + BI) : "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    static_assert(STAGES >= 2 && STAGES <= 3, "wait_slab covers up to 2 later slabs");
+
+    // Software pipeline over the whole K loop: the fragments of sub-step s+1
+    // are read while the MFMAs of sub-step s run.  At the last sub-step of
+    // slab kt the hand-off comes before that sub-step's MFMAs: wait for slab
+    // kt+1, barrier (after which slab kt's stage is free), issue slab
+    // kt+STAGES into it, and read the first fragments of slab kt+1; those
+    // reads then overlap the last MFMAs of slab kt.
+    const int nk = K / BK;
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+        if (s < nk) issue(s, s * BK);
+    wait_slab(min(STAGES, nk) - 1);
+    Chunk a0[FM], b0[FN], a1[FM], b1[FN];
+    frags(a0, b0, 0, 0);
+    int stage = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        int nstage = stage + 1;
+        if (nstage == STAGES) nstage = 0;
+#pragma unroll
+        for (int s = 0; s < KSUB; ++s) {
+            Chunk *ca = (s & 1) ? a1 : a0, *cb = (s & 1) ? b1 : b0;
+            Chunk *na = (s & 1) ? a0 : a1, *nb = (s & 1) ? b0 : b1;
+            if (s + 1 < KSUB) {
+                frags(na, nb, stage, s + 1);
+                mfmas(ca, cb);
+                order_reads_first();
+            } else {
+                if (kt + 1 < nk) {
+                    // slabs issued so far: 0 .. min(kt + STAGES - 1, nk - 1)
+                    wait_slab(min(kt + STAGES - 1, nk - 1) - (kt + 1));
+                    if (kt + STAGES < nk) issue(stage, (kt + STAGES) * BK);
+                    frags(na, nb, nstage, 0);
                 }
+                mfmas(ca, cb);
+                if (kt + 1 < nk) order_reads_first();
             }
         }
+        stage = nstage;
+        if (KSUB & 1) {
+            // odd sub-step count: the next slab's first fragments sit in the
+            // other register set; swap the roles of the two sets
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) { Chunk t = a0[fm]; a0[fm] = a1[fm]; a1[fm] = t; }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) { Chunk t = b0[fn]; b0[fn] = b1[fn]; b1[fn] = t; }
+        }
     }
+    __syncthreads();
+    char *sbase = reinterpret_cast<char *>(&lds[0][0][0]);
+    constexpr int kRiBytes = (BM * (int)sizeof(RowInfo) + 255) / 256 * 256;
+    constexpr int kStageBytes = NW * MI * (WN + 4) * 4;
+    static_assert(kRiBytes + kStageBytes <= (int)sizeof(lds), "epilogue staging exceeds LDS");
+    RowInfo *ri = reinterpret_cast<RowInfo *>(sbase);
+    float *estage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * MI * (WN + 4);
+    float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
+    constexpr int kTabCap = ((int)sizeof(lds) - kRiBytes - kStageBytes) / 8;
+    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
+                                                  ep);
 }
 
 template <typename T, int EPI, bool FAST>
@@ -305,12 +651,48 @@ hipError_t launch_t(const void *A, int64_t lda, const void *W, int64_t ldw, int 
     return hipGetLastError();
 }
 
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI>
+hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K, const EpiArgs &ep,
+                      hipStream_t s) {
+    const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
+    hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(64 * WGM * WGN), 0, s, reinterpret_cast<const T *>(A), lda,
+                       reinterpret_cast<const T *>(W), ldw, M, N, K, tiles_n,
+                       (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * sizeof(T)), ep);
+    return hipGetLastError();
+}
+
+// Tile configuration (measured on the ViT-L shapes: M = 4096, N = 1024 ..
+// 4096): 256 x 256 tiles (8 waves) when they give at least one full wave of
+// workgroups over the 256 CUs, else 128 x 128 tiles (4 waves, two workgroups
+// per CU), both with direct-to-LDS slabs.  fp32 and shapes that break the
+// FAST conditions use the register-staged kernel.
+enum TileCfg { TILE_REG = 0, TILE_256x256 = 1, TILE_128x128 = 2 };
+
+inline int pick_tile(int M, int N, bool fast, bool fp32) {
+    constexpr int kCUs = 256;
+    if (!fast || fp32) return TILE_REG;
+    if (cdiv(M, 256) * cdiv(N, 256) >= kCUs) return TILE_256x256;
+    return TILE_128x128;
+}
+
 template <typename T, int EPI>
 hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K,
                         const EpiArgs &ep, hipStream_t s) {
     constexpr int KPC = Elem<T>::kPerChunk;
     const bool fast = (K % (8 * KPC) == 0) && (lda % KPC == 0) && (ldw % KPC == 0) &&
                       ((uintptr_t)A % 16 == 0) && ((uintptr_t)W % 16 == 0);
+    // buffer offsets are 32-bit: the wide kernel needs both operands (plus a
+    // tile of overhang) below 2 GiB
+    const bool small = ((int64_t)M + 256) * lda * (int64_t)sizeof(T) < INT32_MAX &&
+                       ((int64_t)N + 256) * ldw * (int64_t)sizeof(T) < INT32_MAX;
+    if constexpr (!std::is_same<T, float>::value) {
+        switch (pick_tile(M, N, fast && small, false)) {
+        case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
+        case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 2, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
+        default: break;
+        }
+    }
     if (fast) return launch_t<T, EPI, true>(A, lda, W, ldw, M, N, K, ep, s);
     return launch_t<T, EPI, false>(A, lda, W, ldw, M, N, K, ep, s);
 }

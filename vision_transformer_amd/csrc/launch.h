@@ -36,6 +36,7 @@ struct EpiArgs {
     int D = 0, head_dim = 0, ldv = 0;
     int rope = 0, d_rot = 0;
     const float *rope_tab = nullptr; // cos / signed sin pairs per (axis, position, j)
+    int rope_tab_pairs = 0;          // number of (cos, signed sin) pairs in rope_tab
     const int *tok_pos = nullptr;    // packed (t, h, w) per patch token
     int gt = 0, gh = 0;              // axis offsets into rope_tab
 };

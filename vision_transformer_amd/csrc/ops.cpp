@@ -100,6 +100,7 @@ vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w
             "rope tables");
         if (st) return st;
         ep.d_rot = d; ep.rope_tab = tab; ep.tok_pos = tok; ep.gt = gt; ep.gh = gh;
+        ep.rope_tab_pairs = (gt + gh + gw) * d;
     }
     return op_dev(launch_gemm(dtype, EPI_QKV, Y, D, qkv_w, D, B * N, 3 * D, D, ep, s), "qkv GEMM");
 }
