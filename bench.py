@@ -1,6 +1,8 @@
 """Throughput of the ViT encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu-baseline]
+    python bench.py --write-counters FETCH.csv WRITE.csv OUT.txt
+
 
 A step is one vitenc_encode call over one batch: the V-JEPA-2-style ViT-L
 video encoder, 2 clips x 16 frames x 3 x 256 x 256 -> 2 x 2048 tokens, 24
@@ -8,10 +10,18 @@ layers, bf16 with fp32 accumulation, synthetic seeded inputs resident in HBM.
 Prints one JSON line.  The roofline object is measured for the dominant
 kernel by timing its step entry point (the same kernel and launch
 configuration encode uses) with HIP events on the stream it is launched on.
+
+Its `traffic` figure comes from a committed counter summary (written by the
+--write-counters mode from two rocprofv3 --pmc runs of this script: one
+collecting FETCH_SIZE, one WRITE_SIZE).  Each counter is scaled by what it
+reads for a plain 256 MiB device copy timed in the same run, and the figure is
+reported only while the kernel's sources still hash to what was profiled.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +34,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 256 << 20        # plain device copy used to calibrate the HBM byte counters
+CSRC = os.path.join(ROOT, "vision_transformer_amd", "csrc")
+# kernel-breakdown name -> (device kernel name prefix, sources it is compiled from)
+KERNEL_SOURCES = {
+    "attention": ("attention_kernel", ["attention.hip", "common.h", "launch.h"]),
+    "qkv_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
+    "up_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
+    "down_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
+    "out_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
+    "layernorm": ("layernorm", ["elementwise.hip", "common.h", "launch.h"]),
+}
 
 
 def log(*a):
@@ -38,7 +59,75 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
+                    help="summarise two rocprofv3 --pmc counter_collection.csv files of this script")
     return ap.parse_args()
+
+
+def sources_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_means(path, counter):
+    """{kernel name: (mean counter value, dispatches)} from a rocprofv3 counter csv."""
+    acc = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            k = r["Kernel_Name"]
+            v, n = acc.get(k, (0.0, 0))
+            acc[k] = (v + float(r["Counter_Value"]), n + 1)
+    return {k: (v / n, n) for k, (v, n) in acc.items()}
+
+
+def write_counters(fetch_csv, write_csv, out_txt, dominant):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel and of
+    the calibration copy, plus the hash of the kernel's sources."""
+    prefix, files = KERNEL_SOURCES[dominant]
+    lines = [f"kernel: {dominant}", f"device_kernel_prefix: {prefix}", f"sources: {' '.join(files)}",
+             f"source_sha256_16: {sources_hash(files)}", f"copy_bytes: {COPY_BYTES}"]
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        means = counter_means(path, counter)
+        kern = [(k, v) for k, v in means.items() if prefix in k.split("(")[0]]
+        copy = [(k, v) for k, v in means.items() if "copy" in k.split("(")[0].lower()]
+        if not kern or not copy:
+            raise SystemExit(f"{path}: no {prefix} or copy dispatches with {counter}")
+        # the copy with the largest reading is the 256 MiB calibration copy
+        ck, (cv, cn) = max(copy, key=lambda kv: kv[1][0])
+        kk, (kv, kn) = max(kern, key=lambda kv: kv[1][0])
+        lines += [f"{counter}_KiB_per_dispatch: {kv:.1f}", f"{counter}_dispatches: {kn}",
+                  f"{counter}_kernel: {kk.split('(')[0][:160]}",
+                  f"copy_{counter}_KiB_per_dispatch: {cv:.1f}", f"copy_{counter}_dispatches: {cn}"]
+    with open(out_txt, "a") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_traffic(dominant, workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"{dominant}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    prefix, files = KERNEL_SOURCES[dominant]
+    if kv.get("kernel") != dominant or kv.get("source_sha256_16") != sources_hash(files):
+        return None
+    total = 0.0
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        scale = float(kv["copy_bytes"]) / (float(kv[f"copy_{c}_KiB_per_dispatch"]) * 1024.0)
+        total += float(kv[f"{c}_KiB_per_dispatch"]) * 1024.0 * scale
+    return total
 
 
 def time_region(fn, reps, stream):
@@ -97,18 +186,25 @@ def kernel_breakdown(cfg, wl, enc, reps, stream):
                       2.0 * M * D * F, (M * D + F * D + M * F) * es)
     res["down_gemm"] = (time_region(lambda: V.op_linear_residual(dt, U, blk["down_w"], blk["down_b"], Z), reps,
                                     stream), 2.0 * M * F * D, (M * F + D * F) * es + 8 * M * D)
+    # calibration for the HBM byte counters: a plain copy of known size
+    src = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    copy_ms = time_region(lambda: dst.copy_(src), 3, stream)
+    log(f"[bench] calibration copy {COPY_BYTES >> 20} MiB: {2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9:.0f} GB/s")
+    del src, dst
     return res
 
 
-def cpu_baseline(cfg, wl, layers=4):
-    """The oracle (unchanged, float64 numpy) on one clip and the first `layers`
-    layers, extrapolated to the full depth."""
+def cpu_baseline(cfg, wl, layers=None):
+    """The oracle (unchanged, float64 numpy) on one clip through `layers`
+    layers (default: all of them), scaled to the full depth if fewer."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    layers = layers or cfg.n_layer
     one = cfg.replace(batch=1)
     px = wl.pixels[:1]
     t0 = time.perf_counter()
@@ -122,12 +218,15 @@ def cpu_baseline(cfg, wl, layers=4):
     t3 = time.perf_counter()
     per_clip = (t1 - t0) + (t2 - t1) * cfg.n_layer / layers + (t3 - t2)
     return {"value": round(one.n_tokens / per_clip, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 clip ({one.n_tokens} tokens), patch embed + {layers} of {cfg.n_layer} layers + final norm "
-                      f"timed ({t3 - t0:.1f} s), layer time scaled to {cfg.n_layer} layers"}
+            "sample": f"1 of {cfg.batch} clips ({one.n_tokens} tokens), patch embed + {layers} of {cfg.n_layer} "
+                      f"layers + final norm, {t3 - t0:.1f} s"}
 
 
 def main():
     args = parse()
+    if args.write_counters:
+        write_counters(*args.write_counters, dominant="attention")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(items are independent: N GPUs would each encode their own batch).", file=sys.stderr)
@@ -188,7 +287,10 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["avg_launch_ms"] = round(d_ms, 5)
-    roof["traffic"] = None
+    traffic = read_traffic(dom, cfg.name)
+    roof["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
+    roof["traffic_unit"] = "MB per launch"
+    roof["algorithmic_bytes"] = round(d_bytes / 1e6, 2)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -35,7 +35,7 @@ def out_tol(dtype):
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_F32, W.DTYPE_BF16])
-@pytest.mark.parametrize("M,D", [(37, 192), (130, 1024), (9, 1408), (5, 100)])
+@pytest.mark.parametrize("M,D", [(37, 192), (130, 1024), (9, 1408), (5, 100), (7, 98), (3, 4096)])
 def test_layernorm(gpu_lib, dtype, M, D):
     from vision_transformer_amd import vitenc as V
     say(f"layernorm dtype={dtype} M={M} D={D}")

@@ -40,7 +40,61 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__
 // a4 LayerNorm: one wave per row, the row held in registers, centred
 // two-pass population variance, eps inside the root ("GGUF schema (v1)",
 // jepa.enc.ln_eps; "Architecture", "Attention and precision").
+// When D is a multiple of 4 (and the rows 16-byte aligned) each lane moves 4
+// consecutive elements per access (16-byte loads, 8-byte bf16 stores);
+// otherwise element-wise.
 // ---------------------------------------------------------------------------
+template <typename TO>
+__device__ __forceinline__ void store4(TO *dst, float a, float b, float c, float d) {
+    if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
+    } else {
+        uint2 u;
+        u.x = bits16(from_f32<TO>(a)) | (bits16(from_f32<TO>(b)) << 16);
+        u.y = bits16(from_f32<TO>(c)) | (bits16(from_f32<TO>(d)) << 16);
+        *reinterpret_cast<uint2 *>(dst) = u;
+    }
+}
+
+template <typename TO, int NE>
+__global__ __launch_bounds__(256) void layernorm_vec4_kernel(const float *__restrict__ x, const float *__restrict__ w,
+                                                             const float *__restrict__ b, float eps, int M, int D,
+                                                             TO *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const int D4 = D >> 2;
+    const float4 *xr = reinterpret_cast<const float4 *>(x + (int64_t)row * D);
+    float4 v[NE];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int c4 = lane + 64 * i;
+        v[i] = c4 < D4 ? xr[c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = wave_sum(s) / (float)D;
+    float q = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const float a = v[i].x - mean, bb = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
+        const float t = (a * a + bb * bb) + (c * c + d * d);
+        q += lane + 64 * i < D4 ? t : 0.0f;
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + eps);
+    const float4 *w4 = reinterpret_cast<const float4 *>(w);
+    const float4 *b4 = reinterpret_cast<const float4 *>(b);
+    TO *yr = y + (int64_t)row * D;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+        const int c4 = lane + 64 * i;
+        if (c4 >= D4) break;
+        const float4 ww = w4[c4], bb = b4[c4];
+        store4<TO>(yr + 4 * c4, (v[i].x - mean) * rstd * ww.x + bb.x, (v[i].y - mean) * rstd * ww.y + bb.y,
+                   (v[i].z - mean) * rstd * ww.z + bb.z, (v[i].w - mean) * rstd * ww.w + bb.w);
+    }
+}
+
 template <typename TO, int NE>
 __global__ __launch_bounds__(256) void layernorm_kernel(const float *__restrict__ x, const float *__restrict__ w,
                                                         const float *__restrict__ b, float eps, int M, int D,
@@ -162,6 +216,25 @@ template <typename TO>
 hipError_t launch_ln_t(const float *x, const float *w, const float *b, float eps, int M, int D, TO *y,
                        hipStream_t s) {
     dim3 grid((unsigned)cdiv(M, 4)), block(256);
+    const bool vec = D % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)w % 16 == 0 && (uintptr_t)b % 16 == 0 &&
+                     (uintptr_t)y % 16 == 0;
+    if (vec) {
+        const int ne = (int)cdiv(D / 4, 64);
+#define VITENC_LN4(NE_)                                                                                  \
+    if (ne <= NE_) {                                                                                     \
+        hipLaunchKernelGGL((layernorm_vec4_kernel<TO, NE_>), grid, block, 0, s, x, w, b, eps, M, D, y);  \
+        return hipGetLastError();                                                                        \
+    }
+        VITENC_LN4(1)
+        VITENC_LN4(2)
+        VITENC_LN4(3)
+        VITENC_LN4(4)
+        VITENC_LN4(6)
+        VITENC_LN4(8)
+        VITENC_LN4(12)
+        VITENC_LN4(16)
+#undef VITENC_LN4
+    }
     const int ne = (int)cdiv(D, 64);
 #define VITENC_LN(NE_)                                                                                   \
     if (ne <= NE_) {                                                                                     \
