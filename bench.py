@@ -130,22 +130,13 @@ def read_traffic(dominant, workload):
     return total
 
 
-def time_region(fn, reps, stream):
-    """Average duration of fn() over reps calls, HIP events on `stream`."""
-    import torch
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(reps):
-        fn()
-    end.record(stream)
-    end.synchronize()
-    return start.elapsed_time(end) / reps
-
-
-def kernel_breakdown(cfg, wl, enc, reps, stream):
-    """Each step kernel of one layer, timed alone at the encode shapes through
-    its C-ABI entry point.  Returns {name: (ms, flops, bytes)}."""
+def kernel_breakdown(cfg, enc, reps, stream, busy):
+    """The kernels of one encoder layer, launched in encode's order through
+    their C-ABI entry points at the encode shapes, each bracketed by a pair of
+    HIP events on `stream`.  `busy()` queues a few full encode steps first so
+    that the GPU is still working while the host queues the layer sequences:
+    each event pair then brackets the kernel alone, with the caches and clocks
+    it meets inside encode.  Returns {name: (ms per launch, flops, bytes)}."""
     import torch
     from vision_transformer_amd import vitenc as V
     B, N, D, F, H = cfg.batch, cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim, cfg.n_head
@@ -157,40 +148,64 @@ def kernel_breakdown(cfg, wl, enc, reps, stream):
     blk = enc.blocks[0]
     g = torch.Generator(device=dev).manual_seed(0)
     Z = torch.randn((M, D), device=dev, generator=g)
-    Y = torch.randn((M, D), device=dev, generator=g).to(td)
-    O = torch.randn((M, D), device=dev, generator=g).to(td)
-    U = torch.randn((M, F), device=dev, generator=g).to(td)
-    Q, K, Vt = V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
+    Y = torch.empty((M, D), device=dev, dtype=td)
+    O = torch.empty((M, D), device=dev, dtype=td)
+    U = torch.empty((M, F), device=dev, dtype=td)
+    Q, K, Vt = V.op_qkv_rope(dt, Y.normal_(generator=g), blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
                              rope_layout=cfg.rope_layout, grid=cfg.grid, n_prefix=cfg.n_prefix)
     tab = torch.empty(V.lib().vitenc_rope_table_floats(hd, *cfg.grid), dtype=torch.float32, device=dev)
-    Yo = torch.empty((M, D), device=dev, dtype=td)
-    Oo = torch.empty((M, D), device=dev, dtype=td)
-    Uo = torch.empty((M, F), device=dev, dtype=td)
     torch.cuda.synchronize()
     es = 2
     pairs = cfg.visible_pairs() * B * H
+    seq = [
+        ("layernorm", lambda: V.op_layernorm(Z, blk["ln1_w"], blk["ln1_b"], cfg.ln_eps, dt, out=Y),
+         0.0, M * D * (4 + es) + 8 * D),
+        ("qkv_gemm", lambda: V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
+                                           rope_layout=cfg.rope_layout, grid=cfg.grid, n_prefix=cfg.n_prefix,
+                                           outs=(Q, K, Vt, tab)),
+         2.0 * M * D * 3 * D, (M * D + 3 * D * D + 3 * M * D) * es),
+        ("attention", lambda: V.op_attention(dt, Q, K, Vt, cfg.attn_mode, cfg.n_prefix,
+                                             cfg.grid[1] * cfg.grid[2], out=O),
+         4.0 * hd * pairs, 4 * M * D * es),
+        ("out_gemm", lambda: V.op_linear_residual(dt, O, blk["out_w"], blk["out_b"], Z),
+         2.0 * M * D * D, (M * D + D * D) * es + 8 * M * D),
+        ("layernorm", lambda: V.op_layernorm(Z, blk["ln2_w"], blk["ln2_b"], cfg.ln_eps, dt, out=Y),
+         0.0, M * D * (4 + es) + 8 * D),
+        ("up_gemm", lambda: V.op_linear_gelu(dt, Y, blk["up_w"], blk["up_b"], out=U),
+         2.0 * M * D * F, (M * D + F * D + M * F) * es),
+        ("down_gemm", lambda: V.op_linear_residual(dt, U, blk["down_w"], blk["down_b"], Z),
+         2.0 * M * F * D, (M * F + D * F) * es + 8 * M * D),
+    ]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in seq]
+          for _ in range(reps)]
+    first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy()
+    first.record(stream)
+    for r in range(reps):
+        for (name, fn, _, _), (e0, e1) in zip(seq, ev[r]):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    last.record(stream)
+    torch.cuda.synchronize()
+    acc, cnt = {}, {}
+    for r in range(reps):
+        for (name, _, _, _), (e0, e1) in zip(seq, ev[r]):
+            acc[name] = acc.get(name, 0.0) + e0.elapsed_time(e1)
+            cnt[name] = cnt.get(name, 0) + 1
+    busy_ms = sum(acc.values())
+    span_ms = first.elapsed_time(last)
+    log(f"[bench] layer sequence: kernels {busy_ms:.3f} ms of {span_ms:.3f} ms span over {reps} layers")
     res = {}
-    res["layernorm"] = (time_region(lambda: V.op_layernorm(Z, blk["ln1_w"], blk["ln1_b"], 1e-6, dt, out=Yo), reps, stream),
-                        0.0, M * D * (4 + es) + 8 * D)
-    res["qkv_gemm"] = (time_region(lambda: V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
-                                                         rope_layout=cfg.rope_layout, grid=cfg.grid,
-                                                         n_prefix=cfg.n_prefix, outs=(Q, K, Vt, tab)),
-                                           reps, stream),
-                       2.0 * M * D * 3 * D, (M * D + 3 * D * D + 3 * M * D) * es)
-    res["attention"] = (time_region(lambda: V.op_attention(dt, Q, K, Vt, cfg.attn_mode, cfg.n_prefix,
-                                                           cfg.grid[1] * cfg.grid[2], out=Oo), reps, stream),
-                        4.0 * hd * pairs, 4 * M * D * es)
-    res["out_gemm"] = (time_region(lambda: V.op_linear_residual(dt, O, blk["out_w"], blk["out_b"], Z), reps, stream),
-                       2.0 * M * D * D, (M * D + D * D) * es + 8 * M * D)
-    res["up_gemm"] = (time_region(lambda: V.op_linear_gelu(dt, Y, blk["up_w"], blk["up_b"], out=Uo), reps, stream),
-                      2.0 * M * D * F, (M * D + F * D + M * F) * es)
-    res["down_gemm"] = (time_region(lambda: V.op_linear_residual(dt, U, blk["down_w"], blk["down_b"], Z), reps,
-                                    stream), 2.0 * M * F * D, (M * F + D * F) * es + 8 * M * D)
-    # calibration for the HBM byte counters: a plain copy of known size
+    for name, _, flops, nbytes in seq:
+        res[name] = (acc[name] / cnt[name], flops, nbytes)
+    # calibration for the HBM byte counters: a plain device copy of known size
+    # (fp32 -> int32 keeps the element size, so torch launches its own copy kernel)
     src = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
-    dst = torch.empty_like(src)
-    copy_ms = time_region(lambda: dst.copy_(src), 3, stream)
-    log(f"[bench] calibration copy {COPY_BYTES >> 20} MiB: {2 * COPY_BYTES / (copy_ms * 1e-3) / 1e9:.0f} GB/s")
+    dst = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.int32)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
     del src, dst
     return res
 
@@ -272,7 +287,11 @@ def main():
     log(f"[bench] {ms:.3f} ms/step, {tokens / ms * 1e3:.0f} tokens/s, {tflops:.1f} TFLOP/s "
         f"(wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
 
-    bd = kernel_breakdown(cfg, wl, enc, args.kernel_reps, stream)
+    def busy():
+        for _ in range(4):
+            enc.encode_into(px, ws, out, pooled, stream)
+
+    bd = kernel_breakdown(cfg, enc, args.kernel_reps, stream, busy)
     per_layer = {k: v[0] for k, v in bd.items()}
     log("[bench] per-kernel (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per_layer.items()))
     # the dominant kernel over one forward (layernorm runs twice per layer)
