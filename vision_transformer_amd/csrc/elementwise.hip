@@ -36,6 +36,56 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__
     }
 }
 
+// Row form of the same rearrangement: one thread moves one patch row, the P
+// consecutive pixels of one (channel, frame, pixel row) of one token, which are
+// P consecutive elements of A.  With P a multiple of 4 and W a multiple of 4 the
+// row is read with 16-byte loads; bf16/f16 rows of 16 are written as two 16-byte
+// chunks.  The thread that owns a token's last row also zeroes the pad columns.
+template <typename T, int P, bool VEC>
+__global__ __launch_bounds__(256) void patchify_rows_kernel(const float *__restrict__ X, int C, int T_, int H,
+                                                            int W, int tub, int gh, int gw, int Np, int R, int K,
+                                                            int lda, uint32_t total, T *__restrict__ A) {
+    const uint32_t r = blockIdx.x * 256u + threadIdx.x;
+    if (r >= total) return;
+    const uint32_t m = r / (uint32_t)R, q = r - m * (uint32_t)R;
+    const int dh = (int)(q % P), dt = (int)((q / P) % (uint32_t)tub), c = (int)(q / (P * (uint32_t)tub));
+    const int b = (int)(m / (uint32_t)Np), n = (int)(m - (uint32_t)b * (uint32_t)Np);
+    const int S = gh * gw;
+    const int tt = n / S, hw = n - tt * S, hh = hw / gw, ww = hw - hh * gw;
+    const float *src = X + ((((int64_t)b * C + c) * T_ + (tt * tub + dt)) * H + (hh * P + dh)) * (int64_t)W + ww * P;
+    T *dst = A + (int64_t)m * lda + (int64_t)q * P;
+    float v[P];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < P / 4; ++i) {
+            const float4 f = reinterpret_cast<const float4 *>(src)[i];
+            v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) v[i] = src[i];
+    }
+    if constexpr (VEC && sizeof(T) == 2 && P % 8 == 0) {
+#pragma unroll
+        for (int i = 0; i < P / 8; ++i) {
+            Chunk ch;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                ch.w[j] = bits16(from_f32<T>(v[8 * i + 2 * j])) | (bits16(from_f32<T>(v[8 * i + 2 * j + 1])) << 16);
+            store_chunk(dst + 8 * i, ch);
+        }
+    } else if constexpr (VEC && sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < P / 4; ++i)
+            reinterpret_cast<float4 *>(dst)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < P; ++i) dst[i] = from_f32<T>(v[i]);
+    }
+    if (q == (uint32_t)R - 1)
+        for (int f = K; f < lda; ++f) A[(int64_t)m * lda + f] = from_f32<T>(0.0f);
+}
+
 // ---------------------------------------------------------------------------
 // a4 LayerNorm: one wave per row, the row held in registers, centred
 // two-pass population variance, eps inside the root ("GGUF schema (v1)",
@@ -189,9 +239,11 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int d, int layout, int 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void pool_kernel(const float *__restrict__ X, int N, int D, int cls,
                                                     int n_prefix, float *__restrict__ pooled) {
-    __shared__ float part[16][64];
-    const int cx = threadIdx.x & 63, rg = threadIdx.x >> 6;
-    const int d = blockIdx.x * 64 + cx;
+    // 16 columns x 64 row groups per block: enough blocks to spread one clip's
+    // rows over the chip, each row group reading 64 contiguous bytes per row
+    __shared__ float part[64][16];
+    const int cx = threadIdx.x & 15, rg = threadIdx.x >> 4;
+    const int d = blockIdx.x * 16 + cx;
     const int b = blockIdx.y;
     const float *xb = X + (int64_t)b * N * D;
     float s = 0.0f;
@@ -199,15 +251,14 @@ __global__ __launch_bounds__(1024) void pool_kernel(const float *__restrict__ X,
         if (cls) {
             s = rg == 0 ? xb[d] : 0.0f;
         } else {
-            for (int n = n_prefix + rg; n < N; n += 16) s += xb[(int64_t)n * D + d];
+            for (int n = n_prefix + rg; n < N; n += 64) s += xb[(int64_t)n * D + d];
         }
     }
     part[rg][cx] = s;
     __syncthreads();
     if (rg == 0 && d < D) {
         float t = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t += part[r][cx];
+        for (int r = 0; r < 64; ++r) t += part[r][cx];
         pooled[(int64_t)b * D + d] = cls ? t : t / (float)(N - n_prefix);
     }
 }
@@ -254,29 +305,46 @@ hipError_t launch_ln_t(const float *x, const float *w, const float *b, float eps
 
 } // namespace
 
+namespace {
+template <typename T>
+hipError_t launch_patchify_t(const float *px, int B, int C, int T_, int H, int W, int tub, int P, T *A,
+                             int64_t lda, hipStream_t s) {
+    const int gt = T_ / tub, gh = H / P, gw = W / P, Np = gt * gh * gw;
+    const int K = C * tub * P * P;
+    const int R = C * tub * P;
+    const int64_t rows = (int64_t)B * Np * R;
+    const bool aligned = W % 4 == 0 && (uintptr_t)px % 16 == 0 && (uintptr_t)A % 16 == 0 &&
+                         (lda * (int64_t)sizeof(T)) % 16 == 0;
+    if (rows < (int64_t(1) << 31) && lda < (int64_t(1) << 31) && (P == 16 || P == 14)) {
+        const unsigned blocks = (unsigned)cdiv(rows, 256);
+        if (P == 16 && aligned)
+            hipLaunchKernelGGL((patchify_rows_kernel<T, 16, true>), dim3(blocks), dim3(256), 0, s, px, C, T_, H, W,
+                               tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+        else if (P == 16)
+            hipLaunchKernelGGL((patchify_rows_kernel<T, 16, false>), dim3(blocks), dim3(256), 0, s, px, C, T_, H,
+                               W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+        else
+            hipLaunchKernelGGL((patchify_rows_kernel<T, 14, false>), dim3(blocks), dim3(256), 0, s, px, C, T_, H,
+                               W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+        return hipGetLastError();
+    }
+    const int64_t total = (int64_t)B * Np * lda;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 65535 * 8);
+    hipLaunchKernelGGL(patchify_kernel<T>, dim3(blocks), dim3(256), 0, s, px, C, T_, H, W, tub, P, gh, gw, Np, K,
+                       lda, total, A);
+    return hipGetLastError();
+}
+} // namespace
+
 hipError_t launch_patchify(int dtype, const float *px, int B, int C, int T, int H, int W, int tub, int P,
                            void *A, int64_t lda, hipStream_t s) {
-    const int gt = T / tub, gh = H / P, gw = W / P, Np = gt * gh * gw;
-    const int K = C * tub * P * P;
-    const int64_t total = (int64_t)B * Np * lda;
-    if (total == 0) return hipSuccess;
-    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(total, 256), 65535 * 8);
+    if ((int64_t)B * (T / tub) * (H / P) * (W / P) == 0) return hipSuccess;
     switch (dtype) {
-    case DT_F32:
-        hipLaunchKernelGGL(patchify_kernel<float>, dim3(blocks), dim3(256), 0, s, px, C, T, H, W, tub, P, gh, gw,
-                           Np, K, lda, total, reinterpret_cast<float *>(A));
-        break;
-    case DT_BF16:
-        hipLaunchKernelGGL(patchify_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, px, C, T, H, W, tub, P, gh,
-                           gw, Np, K, lda, total, reinterpret_cast<bf16_t *>(A));
-        break;
-    case DT_F16:
-        hipLaunchKernelGGL(patchify_kernel<f16_t>, dim3(blocks), dim3(256), 0, s, px, C, T, H, W, tub, P, gh, gw,
-                           Np, K, lda, total, reinterpret_cast<f16_t *>(A));
-        break;
-    default: return hipErrorInvalidValue;
+    case DT_F32: return launch_patchify_t(px, B, C, T, H, W, tub, P, reinterpret_cast<float *>(A), lda, s);
+    case DT_BF16: return launch_patchify_t(px, B, C, T, H, W, tub, P, reinterpret_cast<bf16_t *>(A), lda, s);
+    case DT_F16: return launch_patchify_t(px, B, C, T, H, W, tub, P, reinterpret_cast<f16_t *>(A), lda, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_layernorm(int out_dtype, const float *x, const float *w, const float *b, float eps, int M, int D,
@@ -307,7 +375,7 @@ hipError_t launch_rope_table(int head_dim, int layout, int interpolate, int ref_
 }
 
 hipError_t launch_pool(const float *X, int B, int N, int D, int cls, int n_prefix, float *pooled, hipStream_t s) {
-    dim3 grid((unsigned)cdiv(D, 64), (unsigned)B);
+    dim3 grid((unsigned)cdiv(D, 16), (unsigned)B);
     hipLaunchKernelGGL(pool_kernel, grid, dim3(1024), 0, s, X, N, D, cls, n_prefix, pooled);
     return hipGetLastError();
 }

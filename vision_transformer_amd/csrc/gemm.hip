@@ -468,6 +468,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // choosing which chunk each lane fetches.  A ring of STAGES LDS stages keeps
 // STAGES - 1 slabs in flight while one is multiplied.  Requires the FAST
 // conditions (K a multiple of the slab width, 16-byte aligned rows).
+// Wait until at most N of this wave's vector memory operations are still in
+// flight (the direct-to-LDS loads retire in issue order).
+template <int N> __device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
                                                                      const T *__restrict__ W, int64_t ldw, int M,
@@ -572,14 +578,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     // Wait until this wave's loads of one slab have landed while `later`
     // slabs issued after it may still be in flight, then barrier: every
     // wave's part of the slab is visible and every wave has finished reading
-    // what it read before.
+    // what it read before.  (STAGES - 1 is at most 7, so `later` is at most 6
+    // wherever a later slab exists.)
+    constexpr int PER = AI + BI; // load instructions per wave and slab
+    static_assert(STAGES >= 2 && STAGES <= 8 && (STAGES - 1) * PER <= 63, "vmcnt range");
     auto wait_slab = [&](int later) {
-        if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (AI + BI)) : "memory");
-        else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AI + BI) : "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        switch (later) {
+        case 0: vm_wait<0>(); break;
+        case 1: vm_wait<PER>(); break;
+        case 2: vm_wait<(STAGES > 2 ? 2 * PER : 0)>(); break;
+        case 3: vm_wait<(STAGES > 3 ? 3 * PER : 0)>(); break;
+        case 4: vm_wait<(STAGES > 4 ? 4 * PER : 0)>(); break;
+        case 5: vm_wait<(STAGES > 5 ? 5 * PER : 0)>(); break;
+        default: vm_wait<(STAGES > 6 ? 6 * PER : 0)>(); break;
+        }
         __syncthreads();
     };
-    static_assert(STAGES >= 2 && STAGES <= 3, "wait_slab covers up to 2 later slabs");
 
     // Software pipeline over the whole K loop: the fragments of sub-step s+1
     // are read while the MFMAs of sub-step s run.  At the last sub-step of
