@@ -37,6 +37,30 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BQ = 128;   // queries per workgroup
 constexpr int BKV = 64;   // keys per tile
+constexpr float kRescale = 8.0f; // log2 headroom before the running max moves
+#ifndef VITENC_ATTN_PIPE
+#define VITENC_ATTN_PIPE 0
+#endif
+constexpr bool kPipe = VITENC_ATTN_PIPE; // scores of the next tile overlap this tile's softmax
+#ifndef VITENC_ATTN_STAGES
+#define VITENC_ATTN_STAGES 4
+#endif
+constexpr int kStages = VITENC_ATTN_STAGES; // LDS ring depth of the direct-to-LDS kernel
+#ifndef VITENC_ATTN_DOT
+#define VITENC_ATTN_DOT 1
+#endif
+
+// acc + lo + hi of a dword holding two 16-bit values (one packed dot product
+// with (1, 1), fp32 accumulation)
+template <typename T> __device__ __forceinline__ float sum2(uint32_t pk, float acc);
+template <> __device__ __forceinline__ float sum2<bf16_t>(uint32_t pk, float acc) {
+    const bf16x2_t one = {(bf16_t)1.0f, (bf16_t)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+}
+template <> __device__ __forceinline__ float sum2<f16_t>(uint32_t pk, float acc) {
+    const f16x2_t one = {(f16_t)1.0f, (f16_t)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), one, acc, false);
+}
 
 __device__ __forceinline__ int wave_min_i(int v) {
 #pragma unroll
@@ -108,14 +132,28 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
         qf[s] = qrow < N ? load_chunk(Qb + (int64_t)qrow * HD + (2 * s + g) * KPC) : zero_chunk();
 
     Chunk rk[K_PER], rv[V_PER];
-    auto gload = [&](int kt) {
+    // A tile wholly inside [0, N) is fetched without per-chunk bounds checks
+    // (the branch is uniform); the last, ragged tile zero-fills past N.
+    auto gload_k = [&](int kt) {
         const int kb = kt * BKV;
 #pragma unroll
         for (int i = 0; i < K_PER; ++i) {
             const int e = tid + kThreads * i;
             const int r = e / QCH, c = e % QCH;
             const int key = kb + r;
-            rk[i] = key < N ? load_chunk(Kb + (int64_t)key * HD + c * KPC) : zero_chunk();
+            rk[i] = (kb + BKV <= N || key < N) ? load_chunk(Kb + (int64_t)key * HD + c * KPC) : zero_chunk();
+        }
+    };
+    auto gload_v = [&](int kt) {
+        const int kb = kt * BKV;
+        if (kb + BKV <= N) {
+#pragma unroll
+            for (int i = 0; i < V_PER; ++i) {
+                const int e = tid + kThreads * i;
+                const int r = e / KCH, c = e % KCH;
+                rv[i] = load_chunk(Vb + (int64_t)r * ldv + kb + c * KPC);
+            }
+            return;
         }
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
@@ -140,13 +178,15 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
             }
         }
     };
-    auto sstore = [&](int buf) {
+    auto sstore_k = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < K_PER; ++i) {
             const int e = tid + kThreads * i;
             const int r = e / QCH, c = e % QCH;
             sK[buf][r][c ^ swz<QCH>(r)] = rk[i];
         }
+    };
+    auto sstore_v = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < V_PER; ++i) {
             const int e = tid + kThreads * i;
@@ -163,6 +203,21 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
             }
         }
     };
+    // S^T of one tile: two 32-key blocks of this wave's 32 queries
+    auto scores = [&](f32x16 (&sc)[2], int buf) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[j][i] = 0.0f;
+            const int r = 32 * j + l32;
+#pragma unroll
+            for (int s2 = 0; s2 < QCH / 2; ++s2) {
+                const Chunk a = sK[buf][r][(2 * s2 + g) ^ swz<QCH>(r)];
+                mfma_chunk<T>(sc[j], a, qf[s2]);
+            }
+        }
+    };
+    auto tile_active = [&](int kt) { return kt * BKV < w_hi && kt * BKV + BKV > w_lo; };
 
     f32x16 o[NDB];
 #pragma unroll
@@ -171,65 +226,92 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
         for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    if (kt_begin < kt_end) {
-        gload(kt_begin);
-        sstore(0);
+    // Software pipeline over key tiles.  At the start of iteration t the
+    // scores S(t) are in registers, LDS holds V(t) and K(t+1); the iteration
+    // fetches K(t+2) and V(t+1) into registers, issues the MFMAs of S(t+1)
+    // (they run while the softmax of tile t occupies the vector ALUs), does
+    // P(t) and O += V(t)^T P(t)^T, then stores K(t+2) over K(t) and V(t+1)
+    // over V(t-1), both last read before the previous barrier.
+    f32x16 sc[2], sn[2];
+    if constexpr (kPipe) {
+        if (kt_begin < kt_end) {
+            gload_k(kt_begin);
+            gload_v(kt_begin);
+            sstore_k(0);
+            sstore_v(0);
+            if (kt_begin + 1 < kt_end) {
+                gload_k(kt_begin + 1);
+                sstore_k(1);
+            }
+        }
+        __syncthreads();
+        if (kt_begin < kt_end && tile_active(kt_begin)) scores(sc, 0);
+    } else {
+        if (kt_begin < kt_end) {
+            gload_k(kt_begin);
+            gload_v(kt_begin);
+            sstore_k(0);
+            sstore_v(0);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     for (int kt = kt_begin; kt < kt_end; ++kt) {
         const int cur = (kt - kt_begin) & 1;
         const int kb = kt * BKV;
-        if (kt + 1 < kt_end) gload(kt + 1);
-
-        const bool active = kb < w_hi && kb + BKV > w_lo;
-        if (active) {
-            const bool need_mask = !(kb >= w_full_lo && kb + BKV <= w_full_hi);
-            // ---- S^T for two 32-key blocks
-            f32x16 sc[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sc[j][i] = 0.0f;
-                const int r = 32 * j + l32;
-#pragma unroll
-                for (int s = 0; s < QCH / 2; ++s) {
-                    const Chunk a = sK[cur][r][(2 * s + g) ^ swz<QCH>(r)];
-                    mfma_chunk<T>(sc[j], a, qf[s]);
-                }
+        bool next_active = false;
+        if constexpr (kPipe) {
+            if (kt + 2 < kt_end) gload_k(kt + 2);
+            if (kt + 1 < kt_end) gload_v(kt + 1);
+            next_active = kt + 1 < kt_end && tile_active(kt + 1);
+            if (next_active) scores(sn, cur ^ 1);
+        } else {
+            if (kt + 1 < kt_end) {
+                gload_k(kt + 1);
+                gload_v(kt + 1);
             }
-            // ---- scale, mask, running max
+            if (tile_active(kt)) scores(sc, cur);
+        }
+
+        if (tile_active(kt)) {
+            const bool need_mask = !(kb >= w_full_lo && kb + BKV <= w_full_hi);
+            // ---- mask, tile max of the raw scores (the scale is positive)
             float mx = -INFINITY;
+            if (need_mask) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb + 32 * j + acc_row(i, g);
+                        if (key < lo || key >= hi) sc[j][i] = -INFINITY;
+                    }
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = sc[j][i] * scale_log2;
-                    if (need_mask) {
-                        const int key = kb + 32 * j + acc_row(i, g);
-                        if (key < lo || key >= hi) x = -INFINITY;
-                    }
-                    sc[j][i] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-            l_run *= alpha;
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[j][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+            // Lazy rescaling: the running max m_run (log2 units) moves only
+            // when a score exceeds it by more than kRescale, so most tiles skip
+            // the O rescale; exponents stay <= kRescale, and O / l is the same
+            // for any m_run.
+            const bool grow = mx > m_run + kRescale;
+            if (__ballot(grow)) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new); // 0 on the first tile
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+            }
+            const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
             // ---- P = exp2(S - m), row sums, O^T += V^T P^T
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float pv[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    pv[i] = __builtin_amdgcn_exp2f(sc[j][i] - m_use);
-                    l_run += pv[i];
-                }
+                for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(fmaf(sc[j][i], scale_log2, neg_m));
                 if constexpr (KPC == 8) {
                     // one 32x32x16 MFMA per 8 P values: slot e of lane group g is
                     // key 32j + 16st + 8*(e/4) + 4g + e%4 (accumulator slot 8st + e)
@@ -237,9 +319,12 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                     for (int st = 0; st < 2; ++st) {
                         Chunk pb;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            pb.w[e] = bits16(from_f32<T>(pv[8 * st + 2 * e])) |
-                                      (bits16(from_f32<T>(pv[8 * st + 2 * e + 1])) << 16);
+                        for (int e = 0; e < 4; ++e) {
+                            pb.w[e] = pack2<T>(pv[8 * st + 2 * e], pv[8 * st + 2 * e + 1]);
+                            // the row sum adds the rounded weights the MFMA uses
+                            if constexpr (VITENC_ATTN_DOT) l_run = sum2<T>(pb.w[e], l_run);
+                            else l_run += pv[8 * st + 2 * e] + pv[8 * st + 2 * e + 1];
+                        }
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
                             const int r = db * 32 + l32;
@@ -254,7 +339,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                     for (int q4 = 0; q4 < 4; ++q4) {
                         Chunk pb;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) pb.w[e] = __builtin_bit_cast(uint32_t, pv[4 * q4 + e]);
+                        for (int e = 0; e < 4; ++e) {
+                            pb.w[e] = __builtin_bit_cast(uint32_t, pv[4 * q4 + e]);
+                            l_run += pv[4 * q4 + e];
+                        }
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
                             const int r = db * 32 + l32;
@@ -265,8 +353,24 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                 }
             }
         }
-        if (kt + 1 < kt_end) sstore(cur ^ 1);
-        __syncthreads();
+        if constexpr (kPipe) {
+            // every wave has read K(t0) (the scores before the loop) before the
+            // first store overwrites it; later K(t) were read before the last barrier
+            if (kt == kt_begin) __syncthreads();
+            if (kt + 2 < kt_end) sstore_k(cur);
+            if (kt + 1 < kt_end) sstore_v(cur ^ 1);
+            __syncthreads();
+            if (next_active) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) sc[j] = sn[j];
+            }
+        } else {
+            if (kt + 1 < kt_end) {
+                sstore_k(cur ^ 1);
+                sstore_v(cur ^ 1);
+            }
+            __syncthreads();
+        }
     }
 
     // ---- normalise and store O[b, q, head*HD + d]
@@ -274,21 +378,259 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (qrow < N) {
         T *orow = O + ((int64_t)b * N + qrow) * D + head * HD;
+        // accumulator slots 4u..4u+3 are 4 consecutive dims: one 8-byte store
+        // (16 bytes for fp32) per group
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) orow[db * 32 + acc_row(i, g)] = from_f32<T>(o[db][i] * inv);
+            for (int u = 0; u < 4; ++u) {
+                T *dst = orow + db * 32 + acc_row(4 * u, g);
+                const float a0 = o[db][4 * u] * inv, a1 = o[db][4 * u + 1] * inv;
+                const float a2 = o[db][4 * u + 2] * inv, a3 = o[db][4 * u + 3] * inv;
+                if constexpr (sizeof(T) == 4) {
+                    *reinterpret_cast<float4 *>(dst) = make_float4(a0, a1, a2, a3);
+                } else {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(a0, a1), pack2<T>(a2, a3));
+                }
+            }
     }
 }
 
+// Direct-to-LDS form for 16-bit types: the K and V^T tiles are fetched from
+// HBM straight into a ring of STAGES LDS stages with buffer loads, so up to
+// STAGES - 1 tiles are in flight while one is computed.  The K rows of each
+// 16-key group are stored with bits 2 and 3 of the row index swapped: the
+// score accumulator row R then holds key pi(R), and the 8 probabilities a lane
+// group feeds one P.V MFMA are 8 consecutive keys, matching a plain 16-byte
+// read of a V^T row.  Loads past the end of K read zeros (buffer range
+// check); the V^T columns of the ragged last tile are zeroed in LDS.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, Chunk *dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+template <typename T, int HD, int STAGES>
+__global__ __launch_bounds__(kThreads, 2) void attention_lds_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+                                                                    const T *__restrict__ Vt, int N, int H, int ldv,
+                                                                    int causal, int p, int S, float scale_log2,
+                                                                    T *__restrict__ O) {
+    static_assert(sizeof(T) == 2, "16-bit types");
+    constexpr int KPC = 8;
+    constexpr int QCH = HD / KPC;              // chunks per K row (8 or 4)
+    constexpr int VCH = BKV / KPC;             // chunks per V^T row of a tile (8)
+    constexpr int KRI = 64 / QCH;              // K rows per load instruction
+    constexpr int VRI = 64 / VCH;              // V^T rows per load instruction
+    constexpr int NW = kThreads / 64;
+    constexpr int K_INST = BKV / (KRI * NW);   // per wave and tile
+    constexpr int V_INST = HD / (VRI * NW);
+    constexpr int PER = K_INST + V_INST;
+    constexpr int NDB = HD / 32;
+    static_assert(K_INST >= 1 && V_INST >= 1 && K_INST * KRI * NW == BKV && V_INST * VRI * NW == HD, "tile");
+    static_assert(STAGES >= 2 && STAGES <= 4 && (STAGES - 2) * PER <= 63, "vmcnt range");
+
+    __shared__ Chunk sK[STAGES][BKV][QCH];
+    __shared__ Chunk sV[STAGES][HD][VCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5, l32 = lane & 31;
+    const int bh = blockIdx.x;
+    const int b = bh / H, head = bh - b * H;
+    const int qt = gridDim.y - 1 - blockIdx.y; // heavy (late-frame) tiles first
+    const int q0 = qt * BQ;
+    const int D = H * HD;
+
+    const T *Qb = Q + (int64_t)bh * N * HD;
+    const T *Kb = K + (int64_t)bh * N * HD;
+    const T *Vb = Vt + (int64_t)bh * HD * ldv;
+    const __amdgpu_buffer_rsrc_t rsk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Kb, 0, (int)((int64_t)N * HD * sizeof(T)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Vb, 0, (int)((int64_t)HD * ldv * sizeof(T)), 0x00020000);
+
+    const int qrow = q0 + wave * 32 + l32;
+    int lo, hi;
+    key_interval(min(qrow, N - 1), N, causal, p, S, lo, hi);
+    const int w_lo = wave_min_i(lo), w_hi = wave_max_i(hi);
+    const int w_full_lo = wave_max_i(lo), w_full_hi = wave_min_i(hi);
+    int wg_lo, wg_hi, tmp;
+    key_interval(q0, N, causal, p, S, wg_lo, tmp);
+    key_interval(min(q0 + BQ - 1, N - 1), N, causal, p, S, tmp, wg_hi);
+    if (q0 < p) wg_hi = N;
+    const int kt_begin = wg_lo / BKV, kt_end = (int)cdiv(wg_hi, BKV);
+    const int ntiles = kt_end - kt_begin;
+
+    Chunk qf[QCH / 2];
+#pragma unroll
+    for (int s2 = 0; s2 < QCH / 2; ++s2)
+        qf[s2] = qrow < N ? load_chunk(Qb + (int64_t)qrow * HD + (2 * s2 + g) * KPC) : zero_chunk();
+
+    // per-lane byte offsets of the tile loads (the tile's key offset goes in
+    // the scalar offset)
+    uint32_t vk[K_INST], vv[V_INST];
+#pragma unroll
+    for (int j = 0; j < K_INST; ++j) {
+        const int r = (wave * K_INST + j) * KRI + lane / QCH, c = lane % QCH;
+        vk[j] = (uint32_t)((key_perm(r) * HD + (c ^ swz<QCH>(r)) * KPC) * sizeof(T));
+    }
+#pragma unroll
+    for (int j = 0; j < V_INST; ++j) {
+        const int r = (wave * V_INST + j) * VRI + lane / VCH, c = lane % VCH;
+        vv[j] = (uint32_t)(((int64_t)r * ldv + (c ^ swz<VCH>(r)) * KPC) * sizeof(T));
+    }
+    auto issue = [&](int stage, int kt) {
+        const uint32_t koff = (uint32_t)(kt * BKV) * HD * (uint32_t)sizeof(T);
+        const uint32_t voff = (uint32_t)(kt * BKV) * (uint32_t)sizeof(T);
+#pragma unroll
+        for (int j = 0; j < K_INST; ++j)
+            load_lds16(rsk, &sK[stage][(wave * K_INST + j) * KRI][0], vk[j], koff);
+#pragma unroll
+        for (int j = 0; j < V_INST; ++j)
+            load_lds16(rsv, &sV[stage][(wave * V_INST + j) * VRI][0], vv[j], voff);
+    };
+    auto wait_tile = [&](int later) {
+        if (later >= 2) vm_wait<(STAGES > 3 ? 2 * PER : 0)>();
+        else if (later == 1) vm_wait<(STAGES > 2 ? PER : 0)>();
+        else vm_wait<0>();
+        __syncthreads();
+    };
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+#pragma unroll
+    for (int s2 = 0; s2 < STAGES - 1; ++s2)
+        if (s2 < ntiles) issue(s2, kt_begin + s2);
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int kt = kt_begin + t, kb = kt * BKV;
+        const int stg = t % STAGES;
+        // tiles issued so far: 0 .. min(t + STAGES - 2, ntiles - 1)
+        wait_tile(min(t + STAGES - 2, ntiles - 1) - t);
+        // every wave is past tile t-1, so its stage can be refilled
+        if (t + STAGES - 1 < ntiles) issue((t + STAGES - 1) % STAGES, kt + STAGES - 1);
+        if (kb + BKV > N) {
+            // ragged last tile: V^T columns of keys >= N hold whatever follows
+            // the last token in memory; make them zero
+            for (int e = tid; e < HD * BKV; e += kThreads) {
+                const int d = e / BKV, key = e % BKV;
+                if (kb + key >= N) {
+                    T *row = reinterpret_cast<T *>(&sV[stg][d][0]);
+                    row[((key / KPC) ^ swz<VCH>(d)) * KPC + key % KPC] = from_f32<T>(0.0f);
+                }
+            }
+            __syncthreads();
+        }
+        if (!(kb < w_hi && kb + BKV > w_lo)) continue;
+        const bool need_mask = !(kb >= w_full_lo && kb + BKV <= w_full_hi);
+
+        f32x16 sc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[j][i] = 0.0f;
+            const int r = 32 * j + l32;
+#pragma unroll
+            for (int s2 = 0; s2 < QCH / 2; ++s2) mfma_chunk<T>(sc[j], sK[stg][r][(2 * s2 + g) ^ swz<QCH>(r)], qf[s2]);
+        }
+        float mx = -INFINITY;
+        if (need_mask) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kb + 32 * j + key_perm(acc_row(i, g));
+                    if (key < lo || key >= hi) sc[j][i] = -INFINITY;
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[j][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+        const bool grow = mx > m_run + kRescale;
+        if (__ballot(grow)) {
+            const float m_new = grow ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        }
+        const float neg_m = m_run == -INFINITY ? 0.0f : -m_run;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                // accumulator slots 8st .. 8st+7 of lane group g are keys
+                // 32j + 16st + 8g + (0..7)
+                Chunk pb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[j][8 * st + 2 * e], scale_log2, neg_m));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[j][8 * st + 2 * e + 1], scale_log2, neg_m));
+                    pb.w[e] = pack2<T>(p0, p1);
+                    l_run = sum2<T>(pb.w[e], l_run); // the rounded weights the MFMA uses
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int r = db * 32 + l32;
+                    mfma_chunk<T>(o[db], sV[stg][r][(2 * (2 * j + st) + g) ^ swz<VCH>(r)], pb);
+                }
+            }
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (qrow < N) {
+        T *orow = O + ((int64_t)b * N + qrow) * D + head * HD;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                T *dst = orow + db * 32 + acc_row(4 * u, g);
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(o[db][4 * u] * inv, o[db][4 * u + 1] * inv),
+                                                             pack2<T>(o[db][4 * u + 2] * inv, o[db][4 * u + 3] * inv));
+            }
+    }
+}
+
+// 16-bit types: the direct-to-LDS kernel; fp32: the register-staged one
 template <typename T, int HD>
 hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal, int p,
                     int S, void *O, hipStream_t s) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
     dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, BQ));
-    hipLaunchKernelGGL((attention_kernel<T, HD>), grid, dim3(kThreads), 0, s, reinterpret_cast<const T *>(Q),
-                       reinterpret_cast<const T *>(K), reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S,
-                       scale_log2, reinterpret_cast<T *>(O));
+    hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages>), grid, dim3(kThreads), 0, s,
+                       reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
+                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, scale_log2, reinterpret_cast<T *>(O));
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_t<float, 64>(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal,
+                               int p, int S, void *O, hipStream_t s) {
+    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, BQ));
+    hipLaunchKernelGGL((attention_kernel<float, 64>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
+                       reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
+                       S, 1.4426950408889634f / 8.0f, reinterpret_cast<float *>(O));
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_t<float, 32>(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal,
+                               int p, int S, void *O, hipStream_t s) {
+    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, BQ));
+    hipLaunchKernelGGL((attention_kernel<float, 32>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
+                       reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
+                       S, 1.4426950408889634f / sqrtf(32.0f), reinterpret_cast<float *>(O));
     return hipGetLastError();
 }
 

@@ -47,6 +47,19 @@ template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (
 __device__ __forceinline__ uint32_t bits16(bf16_t x) { return __builtin_bit_cast(uint16_t, x); }
 __device__ __forceinline__ uint32_t bits16(f16_t x) { return __builtin_bit_cast(uint16_t, x); }
 
+// two fp32 values -> one dword of two 16-bit values (a in the low half), with
+// one packed hardware conversion (round to nearest even)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+template <> __device__ __forceinline__ uint32_t pack2<f16_t>(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), f16x2_t));
+}
+
 __device__ __forceinline__ Chunk load_chunk(const void *p) {
     return *reinterpret_cast<const Chunk *>(p);
 }
@@ -103,6 +116,15 @@ template <int NCH> __device__ __forceinline__ int swz(int row) {
     if constexpr (NCH == 4) return swz4(row);
     else if constexpr (NCH == 8) return swz8(row);
     else return swz16(row);
+}
+
+// LDS destination of the direct global -> LDS buffer loads
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until at most N of this wave's vector memory operations are still in
+// flight (the direct-to-LDS loads retire in issue order).
+template <int N> __device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // 16x16x32 MFMA tiles (16-bit types): lane l supplies row (l % 16) of A /

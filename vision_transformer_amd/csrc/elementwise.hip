@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void patchify_rows_kernel(const float *__restr
             Chunk ch;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                ch.w[j] = bits16(from_f32<T>(v[8 * i + 2 * j])) | (bits16(from_f32<T>(v[8 * i + 2 * j + 1])) << 16);
+                ch.w[j] = pack2<T>(v[8 * i + 2 * j], v[8 * i + 2 * j + 1]);
             store_chunk(dst + 8 * i, ch);
         }
     } else if constexpr (VEC && sizeof(T) == 4) {
@@ -100,8 +100,8 @@ __device__ __forceinline__ void store4(TO *dst, float a, float b, float c, float
         *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
     } else {
         uint2 u;
-        u.x = bits16(from_f32<TO>(a)) | (bits16(from_f32<TO>(b)) << 16);
-        u.y = bits16(from_f32<TO>(c)) | (bits16(from_f32<TO>(d)) << 16);
+        u.x = pack2<TO>(a, b);
+        u.y = pack2<TO>(c, d);
         *reinterpret_cast<uint2 *>(dst) = u;
     }
 }

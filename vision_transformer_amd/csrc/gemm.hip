@@ -73,7 +73,7 @@ template <typename T> __device__ __forceinline__ void store_vec8(T *dst, const f
     } else {
         Chunk c;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c.w[e] = bits16(from_f32<T>(v[2 * e])) | (bits16(from_f32<T>(v[2 * e + 1])) << 16);
+        for (int e = 0; e < 4; ++e) c.w[e] = pack2<T>(v[2 * e], v[2 * e + 1]);
         store_chunk(dst, c);
     }
 }
@@ -455,7 +455,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 }
 
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Wide-tile variant for shapes with enough tiles to fill the chip: a BM x BN
 // tile per workgroup of WGM x WGN waves, each wave owning a (BM/WGM) x
@@ -468,12 +467,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // choosing which chunk each lane fetches.  A ring of STAGES LDS stages keeps
 // STAGES - 1 slabs in flight while one is multiplied.  Requires the FAST
 // conditions (K a multiple of the slab width, 16-byte aligned rows).
-// Wait until at most N of this wave's vector memory operations are still in
-// flight (the direct-to-LDS loads retire in issue order).
-template <int N> __device__ __forceinline__ void vm_wait() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
                                                                      const T *__restrict__ W, int64_t ldw, int M,
