@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import re
 import hashlib
 import json
 import os
@@ -36,14 +37,16 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 256 << 20        # plain device copy used to calibrate the HBM byte counters
 CSRC = os.path.join(ROOT, "vision_transformer_amd", "csrc")
-# kernel-breakdown name -> (device kernel name prefix, sources it is compiled from)
+# kernel-breakdown name -> (pattern of its device kernel's mangled name, sources it is compiled from).
+# The GEMM epilogue is the last template argument of gemm_lds_kernel (STORE 0, GELU 1, RESID 2,
+# PATCH 3, QKV 4); the out and down projections share the RESID instantiation.
 KERNEL_SOURCES = {
-    "attention": ("attention_kernel", ["attention.hip", "common.h", "launch.h"]),
-    "qkv_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
-    "up_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
-    "down_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
-    "out_gemm": ("gemm_lds_kernel", ["gemm.hip", "common.h", "launch.h"]),
-    "layernorm": ("layernorm", ["elementwise.hip", "common.h", "launch.h"]),
+    "attention": (r"attention_lds_kernel", ["attention.hip", "common.h", "launch.h"]),
+    "qkv_gemm": (r"gemm_lds_kernel.*Li4EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "up_gemm": (r"gemm_lds_kernel.*Li1EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "down_gemm": (r"gemm_lds_kernel.*Li2EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "out_gemm": (r"gemm_lds_kernel.*Li2EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "layernorm": (r"layernorm", ["elementwise.hip", "common.h", "launch.h"]),
 }
 
 
@@ -59,8 +62,9 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--write-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
-                    help="summarise two rocprofv3 --pmc counter_collection.csv files of this script")
+    ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
+                    help="summarise two rocprofv3 --pmc counter_collection.csv files of this script "
+                         "for KERNEL (a kernel-breakdown name)")
     return ap.parse_args()
 
 
@@ -85,21 +89,23 @@ def counter_means(path, counter):
     return {k: (v / n, n) for k, (v, n) in acc.items()}
 
 
-def write_counters(fetch_csv, write_csv, out_txt, dominant):
+def write_counters(dominant, fetch_csv, write_csv, out_txt):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the dominant kernel and of
     the calibration copy, plus the hash of the kernel's sources."""
-    prefix, files = KERNEL_SOURCES[dominant]
-    lines = [f"kernel: {dominant}", f"device_kernel_prefix: {prefix}", f"sources: {' '.join(files)}",
+    pattern, files = KERNEL_SOURCES[dominant]
+    lines = [f"kernel: {dominant}", f"device_kernel_pattern: {pattern}", f"sources: {' '.join(files)}",
              f"source_sha256_16: {sources_hash(files)}", f"copy_bytes: {COPY_BYTES}"]
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         means = counter_means(path, counter)
-        kern = [(k, v) for k, v in means.items() if prefix in k.split("(")[0]]
+        kern = [(k, v) for k, v in means.items() if re.search(pattern, k.split("(")[0])]
         copy = [(k, v) for k, v in means.items() if "copy" in k.split("(")[0].lower()]
         if not kern or not copy:
-            raise SystemExit(f"{path}: no {prefix} or copy dispatches with {counter}")
+            raise SystemExit(f"{path}: no {pattern} or copy dispatches with {counter}")
         # the copy with the largest reading is the 256 MiB calibration copy
         ck, (cv, cn) = max(copy, key=lambda kv: kv[1][0])
-        kk, (kv, kn) = max(kern, key=lambda kv: kv[1][0])
+        if len(kern) > 1:
+            raise SystemExit(f"{path}: {pattern} matches {len(kern)} kernels")
+        kk, (kv, kn) = kern[0]
         lines += [f"{counter}_KiB_per_dispatch: {kv:.1f}", f"{counter}_dispatches: {kn}",
                   f"{counter}_kernel: {kk.split('(')[0][:160]}",
                   f"copy_{counter}_KiB_per_dispatch: {cv:.1f}", f"copy_{counter}_dispatches: {cn}"]
@@ -120,7 +126,7 @@ def read_traffic(dominant, workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    prefix, files = KERNEL_SOURCES[dominant]
+    _, files = KERNEL_SOURCES[dominant]
     if kv.get("kernel") != dominant or kv.get("source_sha256_16") != sources_hash(files):
         return None
     total = 0.0
@@ -240,7 +246,7 @@ def cpu_baseline(cfg, wl, layers=None):
 def main():
     args = parse()
     if args.write_counters:
-        write_counters(*args.write_counters, dominant="attention")
+        write_counters(*args.write_counters)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

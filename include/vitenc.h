@@ -157,8 +157,10 @@ int32_t vitenc_abi_version(void);
 /* a1-a3 (jepa.cpp "Architecture", "The shared ViT graph": rearrange plus one
  * matmul; "GGUF schema (v1)", "Token order"): pixels fp32 [B,C,T,H,W] ->
  * Z fp32 [B, N, D] = [cls?; patches(pixels) W^T + b] (+ pos) (+ mod).
- * scratch: T, at least B*Np*round_up(C*t*P*P, 8) elements.  pos (fp32
- * [N, D]), cls, mod may be NULL (not applied). */
+ * scratch: T, at least B*Np*2*round_up(C*t*P*P, 8) elements (for 16-bit
+ * types with C*t*P*P a multiple of 64 each pixel is held as a hi and a lo
+ * part, which takes the factor 2).  pos (fp32 [N, D]), cls, mod may be NULL
+ * (not applied). */
 vitenc_status vitenc_op_embed(int32_t dtype, const float *pixels, int32_t B, int32_t C,
                               int32_t T, int32_t H, int32_t W, int32_t tubelet, int32_t patch,
                               const void *patch_w, const float *patch_b, const float *pos,

@@ -127,7 +127,7 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
         return fail(VITENC_ESHAPE, "position table has %d rows but the input makes %d tokens", hp.pos_rows, pl.N);
     pl.D = hp.embed_dim; pl.F = hp.ffn_dim; pl.nh = hp.n_head; pl.hd = pl.D / pl.nh;
     pl.K = hp.in_chans * hp.tubelet_size * hp.patch_size * hp.patch_size;
-    pl.lda = (int)rup(pl.K, 8);
+    pl.lda = embed_lda(hp.dtype, pl.K);
     pl.ldv = (int)rup(pl.N, 64);
     const size_t es = (size_t)dtype_size(hp.dtype);
     size_t off = 0;
@@ -244,7 +244,10 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
         ep.Np = pl.Np;
         ep.Ntok = pl.N;
         ep.prefix = pl.p;
-        CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda, m->w.patch_w, pl.K, B * pl.Np, D, pl.K, ep, s), "patch GEMM");
+        const bool split = pl.lda == 2 * pl.K;
+        ep.kwrap = split ? pl.K : 0;
+        CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda, m->w.patch_w, pl.K, B * pl.Np, D, split ? 2 * pl.K : pl.K, ep, s),
+                  "patch GEMM");
     }
     if (pl.p)
         CHECK_DEV(launch_prefix_rows(m->w.cls_token, hp.pos_type == VITENC_POS_TABLE ? m->w.pos_embed : nullptr,

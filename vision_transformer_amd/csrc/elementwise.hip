@@ -22,7 +22,10 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = idx / lda;
-        const int f = (int)(idx - m * lda);
+        const int f0 = (int)(idx - m * lda);
+        // split rows (lda == 2K): columns [K, 2K) hold x - round(x) of column f - K
+        const bool lo = lda == 2 * (int64_t)K && f0 >= K;
+        const int f = lo ? f0 - K : f0;
         float v = 0.0f;
         if (f < K) {
             const int b = (int)(m / Np), n = (int)(m - (int64_t)b * Np);
@@ -32,7 +35,8 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__
                                 (ww * P + dw);
             v = X[src];
         }
-        A[idx] = from_f32<T>(v);
+        const T h = from_f32<T>(v);
+        A[idx] = lo ? from_f32<T>(v - to_f32(h)) : h;
     }
 }
 
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__
 // P consecutive elements of A.  With P a multiple of 4 and W a multiple of 4 the
 // row is read with 16-byte loads; bf16/f16 rows of 16 are written as two 16-byte
 // chunks.  The thread that owns a token's last row also zeroes the pad columns.
-template <typename T, int P, bool VEC>
+template <typename T, int P, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(256) void patchify_rows_kernel(const float *__restrict__ X, int C, int T_, int H,
                                                             int W, int tub, int gh, int gw, int Np, int R, int K,
                                                             int lda, uint32_t total, T *__restrict__ A) {
@@ -65,7 +69,32 @@ __global__ __launch_bounds__(256) void patchify_rows_kernel(const float *__restr
 #pragma unroll
         for (int i = 0; i < P; ++i) v[i] = src[i];
     }
-    if constexpr (VEC && sizeof(T) == 2 && P % 8 == 0) {
+    if constexpr (SPLIT && !(VEC && P % 8 == 0)) {
+        // hi = round(x) in the first K columns, lo = round(x - hi) in the next K
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const T h = from_f32<T>(v[i]);
+            dst[i] = h;
+            dst[K + i] = from_f32<T>(v[i] - to_f32(h));
+        }
+        return;
+    } else if constexpr (SPLIT) {
+        static_assert(sizeof(T) == 2, "split rows are 16-bit");
+#pragma unroll
+        for (int i = 0; i < P / 8; ++i) {
+            Chunk hi, lo;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a = v[8 * i + 2 * j], b = v[8 * i + 2 * j + 1];
+                const T ha = from_f32<T>(a), hb = from_f32<T>(b);
+                hi.w[j] = bits16(ha) | (bits16(hb) << 16);
+                lo.w[j] = pack2<T>(a - to_f32(ha), b - to_f32(hb));
+            }
+            store_chunk(dst + 8 * i, hi);
+            store_chunk(dst + K + 8 * i, lo);
+        }
+        return;
+    } else if constexpr (VEC && sizeof(T) == 2 && P % 8 == 0) {
 #pragma unroll
         for (int i = 0; i < P / 8; ++i) {
             Chunk ch;
@@ -315,17 +344,30 @@ hipError_t launch_patchify_t(const float *px, int B, int C, int T_, int H, int W
     const int64_t rows = (int64_t)B * Np * R;
     const bool aligned = W % 4 == 0 && (uintptr_t)px % 16 == 0 && (uintptr_t)A % 16 == 0 &&
                          (lda * (int64_t)sizeof(T)) % 16 == 0;
+    const bool split = lda == 2 * (int64_t)K;
     if (rows < (int64_t(1) << 31) && lda < (int64_t(1) << 31) && (P == 16 || P == 14)) {
         const unsigned blocks = (unsigned)cdiv(rows, 256);
-        if (P == 16 && aligned)
-            hipLaunchKernelGGL((patchify_rows_kernel<T, 16, true>), dim3(blocks), dim3(256), 0, s, px, C, T_, H, W,
-                               tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+        if (split) {
+            if constexpr (sizeof(T) == 2) {
+                if (P == 16 && aligned)
+                    hipLaunchKernelGGL((patchify_rows_kernel<T, 16, true, true>), dim3(blocks), dim3(256), 0, s, px,
+                                       C, T_, H, W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+                else if (P == 16)
+                    hipLaunchKernelGGL((patchify_rows_kernel<T, 16, false, true>), dim3(blocks), dim3(256), 0, s, px,
+                                       C, T_, H, W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+                else
+                    hipLaunchKernelGGL((patchify_rows_kernel<T, 14, false, true>), dim3(blocks), dim3(256), 0, s, px,
+                                       C, T_, H, W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+            }
+        } else if (P == 16 && aligned)
+            hipLaunchKernelGGL((patchify_rows_kernel<T, 16, true, false>), dim3(blocks), dim3(256), 0, s, px, C, T_,
+                               H, W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
         else if (P == 16)
-            hipLaunchKernelGGL((patchify_rows_kernel<T, 16, false>), dim3(blocks), dim3(256), 0, s, px, C, T_, H,
-                               W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+            hipLaunchKernelGGL((patchify_rows_kernel<T, 16, false, false>), dim3(blocks), dim3(256), 0, s, px, C,
+                               T_, H, W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
         else
-            hipLaunchKernelGGL((patchify_rows_kernel<T, 14, false>), dim3(blocks), dim3(256), 0, s, px, C, T_, H,
-                               W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
+            hipLaunchKernelGGL((patchify_rows_kernel<T, 14, false, false>), dim3(blocks), dim3(256), 0, s, px, C,
+                               T_, H, W, tub, gh, gw, Np, R, K, (int)lda, (uint32_t)rows, A);
         return hipGetLastError();
     }
     const int64_t total = (int64_t)B * Np * lda;

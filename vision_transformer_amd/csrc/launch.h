@@ -39,7 +39,20 @@ struct EpiArgs {
     int rope_tab_pairs = 0;          // number of (cos, signed sin) pairs in rope_tab
     const int *tok_pos = nullptr;    // packed (t, h, w) per patch token
     int gt = 0, gh = 0;              // axis offsets into rope_tab
+    // A has 2*kwrap columns whose second half pairs with W's columns again
+    // (the split-pixel patch embedding); 0: A and W share K
+    int kwrap = 0;
 };
+
+// Patch embedding in a 16-bit type with K a multiple of 64 stores each pixel
+// as two values, hi = round(x) and lo = round(x - hi), in the two halves of a
+// row of 2K columns, and runs the patch GEMM over both halves against the
+// same weights: the pixels then enter the embedding with about 16 significant
+// bits instead of 8.  Returns the A row length (elements) of a patch row.
+inline int embed_lda(int dtype, int K) {
+    if (dtype != DT_F32 && K % 64 == 0) return 2 * K;
+    return (K + 7) / 8 * 8;
+}
 
 hipError_t launch_gemm(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw,
                        int M, int N, int K, const EpiArgs &ep, hipStream_t s);
@@ -47,6 +60,7 @@ hipError_t launch_gemm(int dtype, int epi, const void *A, int64_t lda, const voi
 hipError_t launch_layernorm(int out_dtype, const float *x, const float *w, const float *b, float eps,
                             int M, int D, void *y, hipStream_t s);
 
+// lda == 2K selects the split (hi, lo) representation (embed_lda)
 hipError_t launch_patchify(int dtype, const float *px, int B, int C, int T, int H, int W, int tub,
                            int P, void *A, int64_t lda, hipStream_t s);
 

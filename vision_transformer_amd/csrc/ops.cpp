@@ -40,14 +40,17 @@ vitenc_status vitenc_op_embed(int32_t dtype, const float *pixels, int32_t B, int
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int Np = (T / tubelet) * (H / patch) * (W / patch);
     const int K = C * tubelet * patch * patch;
-    const int lda = (K + 7) / 8 * 8;
+    const int lda = embed_lda(dtype, K);
+    const bool split = lda == 2 * K;
     const int p = cls ? 1 : 0;
     vitenc_status st = op_dev(launch_patchify(dtype, pixels, B, C, T, H, W, tubelet, patch, scratch, lda, s), "patchify");
     if (st) return st;
     EpiArgs ep;
     ep.bias = patch_b; ep.Z = Z; ep.ldz = D; ep.pos = pos; ep.mod = mod;
     ep.Np = Np; ep.Ntok = Np + p; ep.prefix = p;
-    st = op_dev(launch_gemm(dtype, EPI_PATCH, scratch, lda, patch_w, K, B * Np, D, K, ep, s), "patch GEMM");
+    ep.kwrap = split ? K : 0;
+    st = op_dev(launch_gemm(dtype, EPI_PATCH, scratch, lda, patch_w, K, B * Np, D, split ? 2 * K : K, ep, s),
+                "patch GEMM");
     if (st) return st;
     if (p) return op_dev(launch_prefix_rows(cls, pos, mod, B, Np + p, D, Z, s), "prefix rows");
     return VITENC_OK;

@@ -228,7 +228,7 @@ def op_embed(dtype, pixels, tubelet, patch, patch_w, patch_b, pos=None, cls=None
     Np = (T // tubelet) * (H // patch) * (W // patch)
     K = C * tubelet * patch * patch
     lda = (K + 7) // 8 * 8
-    scratch = torch.empty(B * Np * lda, dtype=torch_dtype(dtype), device=pixels.device)
+    scratch = torch.empty(B * Np * 2 * lda, dtype=torch_dtype(dtype), device=pixels.device)
     Z = torch.empty((B, Np + (1 if cls is not None else 0), D), dtype=torch.float32, device=pixels.device)
     check(lib().vitenc_op_embed(dtype, pixels.data_ptr(), B, C, T, H, W, tubelet, patch, patch_w.data_ptr(),
                                 patch_b.data_ptr(), _ptr(pos), _ptr(cls), _ptr(mod), D, scratch.data_ptr(),
