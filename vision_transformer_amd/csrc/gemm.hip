@@ -354,19 +354,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) pb[i] = W + (int64_t)min(n0 + lr + 32 * i, N - 1) * ldw + lc * KPC;
 
+    const int kw = ep.kwrap ? ep.kwrap : K; // W columns
     auto gload = [&](Chunk *ra, Chunk *rb, int k0) {
+        const int kb = k0 >= kw ? k0 - kw : k0; // W column of A column k0
         if constexpr (FAST) {
 #pragma unroll
             for (int i = 0; i < A_PER; ++i) ra[i] = load_chunk(pa[i] + k0);
 #pragma unroll
-            for (int i = 0; i < B_PER; ++i) rb[i] = load_chunk(pb[i] + k0);
+            for (int i = 0; i < B_PER; ++i) rb[i] = load_chunk(pb[i] + kb);
         } else {
 #pragma unroll
             for (int i = 0; i < A_PER; ++i)
                 ra[i] = load_tile_chunk<T, false>(A, lda, m0 + lr + 32 * i, M, k0 + lc * KPC, K);
 #pragma unroll
             for (int i = 0; i < B_PER; ++i)
-                rb[i] = load_tile_chunk<T, false>(W, ldw, n0 + lr + 32 * i, N, k0 + lc * KPC, K);
+                rb[i] = load_tile_chunk<T, false>(W, ldw, n0 + lr + 32 * i, N, kb + lc * KPC, kw);
         }
     };
     auto sstore = [&](const Chunk *ra, const Chunk *rb, int buf) {
@@ -511,6 +513,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     const uint32_t va1 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw1) * KPC) * ES);
     const uint32_t vb0 = (uint32_t)(((int64_t)(n0 + wave * BI * RPI + lrow) * ldw + (lch ^ sw0) * KPC) * ES);
     const uint32_t vb1 = (uint32_t)(((int64_t)(n0 + wave * BI * RPI + lrow) * ldw + (lch ^ sw1) * KPC) * ES);
+    const int kw = ep.kwrap ? ep.kwrap : K; // W columns
     auto issue = [&](int stage, int k0) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
@@ -519,10 +522,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t *)&lds[stage][row][0], 16,
                                                      ((row / RPI) & 1) ? va1 : va0, soff, 0, 0);
         }
+        const int kb = k0 >= kw ? k0 - kw : k0; // W column of A column k0
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
             const int row = (wave * BI + j) * RPI;
-            const uint32_t soff = (uint32_t)((k0 + (int64_t)j * RPI * ldw) * ES);
+            const uint32_t soff = (uint32_t)((kb + (int64_t)j * RPI * ldw) * ES);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t *)&lds[stage][BM + row][0], 16,
                                                      (((BM + row) / RPI) & 1) ? vb1 : vb0, soff, 0, 0);
         }
