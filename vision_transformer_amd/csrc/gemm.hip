@@ -34,11 +34,11 @@ namespace {
 constexpr int kThreads = 256;
 
 struct RowInfo {
-    int out_row; // PATCH: token row in Z; QKV: item index b
-    int tok;     // QKV: token index inside the item
-    int pos;     // PATCH: pos-table row; QKV: 1 if the row is rotated (a patch token), else 0
-    int base[3]; // QKV: first table entry of this row's position on axis t, h, w
-    int pad[2];
+    int out_row;    // PATCH: token row in Z; QKV: item index b
+    int tok;        // QKV: token index inside the item
+    int pos;        // PATCH: pos-table row; QKV: 1 if the row is rotated (a patch token), else 0
+    int base[3];    // QKV: first table entry of this row's position on axis t, h, w
+    int64_t qk_off; // QKV: element offset of (b, head 0, tok, dim 0) in Q / K [B, H, N, hd]
 };
 
 template <typename T, bool ALIGNED>
@@ -126,10 +126,47 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
     const int lcol = lane & (MI - 1);
     auto vrow = [&](int i) { return MI == 32 ? acc_row(i, lane >> 5) : 4 * (lane >> 4) + i; };
 
+    if constexpr (EPI == EPI_QKV && MI == 32) {
+        // A tile of V columns only: the accumulators already hold, per lane,
+        // one feature and runs of 4 consecutive tokens (slots 4q..4q+3 are rows
+        // 8q + 4(l/32) + 0..3), which is V^T's layout: store them directly as
+        // 8-byte runs, with no staging.  Needs token runs that never cross an
+        // item (N % 4 == 0); the condition is uniform over the workgroup.
+        if (n0 >= 2 * ep.D && (ep.Ntok & 3) == 0) {
+            const int H = ep.D / ep.head_dim, g = lane >> 5;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int col = n0 + woff_n + fn * MI + lcol;
+                if (col >= N) continue;
+                const float bias = ep.bias ? ep.bias[col] : 0.0f;
+                const int within = col - 2 * ep.D;
+                const int head = within / ep.head_dim, dd = within - head * ep.head_dim;
+                T *vcol = reinterpret_cast<T *>(ep.Vt) + (int64_t)head * ep.head_dim * ep.ldv + (int64_t)dd * ep.ldv;
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int row0 = m0 + woff_m + fm * MI + 8 * q + 4 * g;
+                        if (row0 >= M) continue;
+                        const int b = row0 / ep.Ntok, tok = row0 - b * ep.Ntok;
+                        T *dst = vcol + (int64_t)b * H * ep.head_dim * ep.ldv + tok;
+                        const float v0 = acc[fm][fn][4 * q] + bias, v1 = acc[fm][fn][4 * q + 1] + bias;
+                        const float v2 = acc[fm][fn][4 * q + 2] + bias, v3 = acc[fm][fn][4 * q + 3] + bias;
+                        if constexpr (sizeof(T) == 4) {
+                            *reinterpret_cast<float4 *>(dst) = make_float4(v0, v1, v2, v3);
+                        } else {
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
+                        }
+                    }
+            }
+            return;
+        }
+    }
+
     if constexpr (EPI == EPI_PATCH || EPI == EPI_QKV) {
         for (int t = tid; t < BM; t += NT) {
             const int row = m0 + t;
-            RowInfo info{0, 0, 0, {0, 0, 0}, {0, 0}};
+            RowInfo info{0, 0, 0, {0, 0, 0}, 0};
             if (row < M) {
                 if constexpr (EPI == EPI_PATCH) {
                     const int b = row / ep.Np, n = row - b * ep.Np;
@@ -140,6 +177,7 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
                     info.out_row = b;
                     info.tok = tok;
                     info.pos = 0;
+                    info.qk_off = ((int64_t)b * (ep.D / ep.head_dim) * ep.Ntok + tok) * ep.head_dim;
                     if (ep.rope && tok >= ep.prefix) {
                         const int pk = ep.tok_pos[tok - ep.prefix];
                         info.pos = 1;
@@ -152,12 +190,16 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
             ri[t] = info;
         }
     }
-    // the RoPE table goes to LDS when it fits (it is read once per element)
+    // The RoPE table goes to LDS when it fits, followed by one identity pair
+    // (cos 1, sin 0) that the unrotated dims read, so that the rotation needs
+    // no per-element branch.  Otherwise it is read from global memory.
     const float2 *tab = reinterpret_cast<const float2 *>(ep.rope_tab);
+    const int id_pair = ep.rope_tab_pairs;
+    const bool tab_lds = EPI == EPI_QKV && ep.rope && ep.rope_tab_pairs + 1 <= lds_tab_cap;
     if constexpr (EPI == EPI_QKV) {
-        if (ep.rope && ep.rope_tab_pairs <= lds_tab_cap) {
+        if (tab_lds) {
             for (int t = tid; t < ep.rope_tab_pairs; t += NT) lds_tab[t] = tab[t];
-            tab = lds_tab;
+            if (tid == 0) lds_tab[id_pair] = make_float2(1.0f, 0.0f);
         }
     }
     __syncthreads();
@@ -179,18 +221,32 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
     }
     int which = 0, head = 0, dd0 = 0;
     int axis8[8], jr8[8];
+    // LDS-table RoPE: a lane's 8 dims meet at most two axis segments (every
+    // segment is at least 10 dims wide): selectors s_lo / s_hi of the row's
+    // table base (0..2 = t, h, w; 3 = the identity pair), dims j < jsplit use
+    // s_lo, and off8[j] is the entry within the segment (0 for the identity)
+    int s_lo = 3, s_hi = 3, jsplit = 8, off8[8];
+    int64_t qk_col = 0;
     if constexpr (EPI == EPI_QKV) {
         which = col0 / ep.D;
         const int within = col0 - which * ep.D;
         head = within / ep.head_dim;
         dd0 = within - head * ep.head_dim;
+        qk_col = (int64_t)head * ep.Ntok * ep.head_dim + dd0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int dd = dd0 + j;
             const int ax = dd >= 3 * ep.d_rot ? 3 : dd >= 2 * ep.d_rot ? 2 : dd >= ep.d_rot ? 1 : 0;
             axis8[j] = ax; // 3: not rotated
             jr8[j] = dd - (ax < 3 ? ax : 0) * ep.d_rot;
+            off8[j] = ax < 3 ? jr8[j] : 0;
         }
+        s_lo = axis8[0];
+        s_hi = axis8[7];
+        jsplit = 8;
+#pragma unroll
+        for (int j = 7; j >= 1; --j)
+            if (axis8[j] != axis8[0]) jsplit = j;
     }
     const bool qk_cols = EPI == EPI_QKV && which < 2;
 
@@ -239,21 +295,31 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
             const RowInfo info = ri[rt];
             if (ep.rope && info.pos) {
                 float y[8];
+                if (tab_lds) {
+                    auto sel = [&](int sx) {
+                        return sx == 0 ? info.base[0] : sx == 1 ? info.base[1] : sx == 2 ? info.base[2] : id_pair;
+                    };
+                    const int b_lo = sel(s_lo), b_hi = sel(s_hi);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    y[j] = v[j];
-                    if (axis8[j] < 3) {
-                        const int base = axis8[j] == 0 ? info.base[0] : axis8[j] == 1 ? info.base[1] : info.base[2];
-                        const float2 cs = tab[base + jr8[j]];
+                    for (int j = 0; j < 8; ++j) {
+                        const float2 cs = lds_tab[(j < jsplit ? b_lo : b_hi) + off8[j]];
                         y[j] = v[j] * cs.x + v[j ^ 1] * cs.y;
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        y[j] = v[j];
+                        if (axis8[j] < 3) {
+                            const int base = axis8[j] == 0 ? info.base[0] : axis8[j] == 1 ? info.base[1] : info.base[2];
+                            const float2 cs = tab[base + jr8[j]];
+                            y[j] = v[j] * cs.x + v[j ^ 1] * cs.y;
+                        }
                     }
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) v[j] = y[j];
             }
-            const int H = ep.D / ep.head_dim;
-            T *dst = reinterpret_cast<T *>(which == 0 ? ep.Q : ep.K) +
-                     (((int64_t)info.out_row * H + head) * ep.Ntok + info.tok) * ep.head_dim + dd0;
+            T *dst = reinterpret_cast<T *>(which == 0 ? ep.Q : ep.K) + info.qk_off + qk_col;
             store_vec8<T>(dst, v);
         }
     };
