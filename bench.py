@@ -76,17 +76,27 @@ def sources_hash(files):
     return h.hexdigest()[:16]
 
 
-def counter_means(path, counter):
-    """{kernel name: (mean counter value, dispatches)} from a rocprofv3 counter csv."""
-    acc = {}
+# kernels that share one device instantiation: (index, count) of each one's dispatches in the
+# repeating launch order (every layer launches the out projection, then the down projection)
+SHARED_DISPATCH = {"out_gemm": (0, 2), "down_gemm": (1, 2)}
+
+
+def counter_means(path, counter, share=None):
+    """{kernel name: (mean counter value, dispatches)} from a rocprofv3 counter csv; with
+    share = (index, count) only every count-th dispatch of a kernel, starting at index."""
+    rows = {}
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            if r["Counter_Name"] != counter:
-                continue
-            k = r["Kernel_Name"]
-            v, n = acc.get(k, (0.0, 0))
-            acc[k] = (v + float(r["Counter_Value"]), n + 1)
-    return {k: (v / n, n) for k, (v, n) in acc.items()}
+            if r["Counter_Name"] == counter:
+                rows.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    out = {}
+    for k, vals in rows.items():
+        vals.sort()
+        if share is not None:
+            vals = vals[share[0]::share[1]]
+        if vals:
+            out[k] = (sum(v for _, v in vals) / len(vals), len(vals))
+    return out
 
 
 def write_counters(dominant, fetch_csv, write_csv, out_txt):
@@ -97,7 +107,8 @@ def write_counters(dominant, fetch_csv, write_csv, out_txt):
              f"source_sha256_16: {sources_hash(files)}", f"copy_bytes: {COPY_BYTES}"]
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         means = counter_means(path, counter)
-        kern = [(k, v) for k, v in means.items() if re.search(pattern, k.split("(")[0])]
+        shared = counter_means(path, counter, SHARED_DISPATCH.get(dominant))
+        kern = [(k, shared[k]) for k in shared if re.search(pattern, k.split("(")[0])]
         copy = [(k, v) for k, v in means.items() if "copy" in k.split("(")[0].lower()]
         if not kern or not copy:
             raise SystemExit(f"{path}: no {pattern} or copy dispatches with {counter}")
@@ -139,10 +150,12 @@ def read_traffic(dominant, workload):
 def kernel_breakdown(cfg, enc, reps, stream, busy):
     """The kernels of one encoder layer, launched in encode's order through
     their C-ABI entry points at the encode shapes, each bracketed by a pair of
-    HIP events on `stream`.  `busy()` queues a few full encode steps first so
-    that the GPU is still working while the host queues the layer sequences:
-    each event pair then brackets the kernel alone, with the caches and clocks
-    it meets inside encode.  Returns {name: (ms per launch, flops, bytes)}."""
+    HIP events on `stream`.  Repetition r uses the weights of layer r mod L,
+    so that, as inside encode, each launch streams weights the previous ones
+    did not; the RoPE table is filled once, as encode does.  `busy()` queues a
+    few full encode steps first so that the GPU is still working while the
+    host queues the layer sequences: each event pair then brackets the kernel
+    alone.  Returns {name: (ms per launch, flops, bytes)}."""
     import torch
     from vision_transformer_amd import vitenc as V
     B, N, D, F, H = cfg.batch, cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim, cfg.n_head
@@ -151,60 +164,65 @@ def kernel_breakdown(cfg, enc, reps, stream, busy):
     dt = cfg.dtype
     td = V.torch_dtype(dt)
     dev = "cuda"
-    blk = enc.blocks[0]
     g = torch.Generator(device=dev).manual_seed(0)
     Z = torch.randn((M, D), device=dev, generator=g)
     Y = torch.empty((M, D), device=dev, dtype=td)
     O = torch.empty((M, D), device=dev, dtype=td)
     U = torch.empty((M, F), device=dev, dtype=td)
-    Q, K, Vt = V.op_qkv_rope(dt, Y.normal_(generator=g), blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
-                             rope_layout=cfg.rope_layout, grid=cfg.grid, n_prefix=cfg.n_prefix)
-    tab = torch.empty(V.lib().vitenc_rope_table_floats(hd, *cfg.grid), dtype=torch.float32, device=dev)
+    blk0 = enc.blocks[0]
+    tab = V.op_rope_table(hd, cfg.grid, cfg.rope_layout, cfg.rope_interpolate, cfg.rope_ref_grid, cfg.rope_theta)
+    Q, K, Vt = V.op_qkv_rope(dt, Y.normal_(generator=g), blk0["qkv_w"], blk0["qkv_b"], B, N, H, rope=cfg.rope,
+                             grid=cfg.grid, n_prefix=cfg.n_prefix,
+                             outs=(torch.empty((B, H, N, hd), dtype=td, device=dev),
+                                   torch.empty((B, H, N, hd), dtype=td, device=dev),
+                                   torch.zeros((B, H, hd, (N + 63) // 64 * 64), dtype=td, device=dev), tab),
+                             table_ready=True)
     torch.cuda.synchronize()
     es = 2
     pairs = cfg.visible_pairs() * B * H
-    seq = [
-        ("layernorm", lambda: V.op_layernorm(Z, blk["ln1_w"], blk["ln1_b"], cfg.ln_eps, dt, out=Y),
-         0.0, M * D * (4 + es) + 8 * D),
-        ("qkv_gemm", lambda: V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
-                                           rope_layout=cfg.rope_layout, grid=cfg.grid, n_prefix=cfg.n_prefix,
-                                           outs=(Q, K, Vt, tab)),
-         2.0 * M * D * 3 * D, (M * D + 3 * D * D + 3 * M * D) * es),
-        ("attention", lambda: V.op_attention(dt, Q, K, Vt, cfg.attn_mode, cfg.n_prefix,
-                                             cfg.grid[1] * cfg.grid[2], out=O),
-         4.0 * hd * pairs, 4 * M * D * es),
-        ("out_gemm", lambda: V.op_linear_residual(dt, O, blk["out_w"], blk["out_b"], Z),
-         2.0 * M * D * D, (M * D + D * D) * es + 8 * M * D),
-        ("layernorm", lambda: V.op_layernorm(Z, blk["ln2_w"], blk["ln2_b"], cfg.ln_eps, dt, out=Y),
-         0.0, M * D * (4 + es) + 8 * D),
-        ("up_gemm", lambda: V.op_linear_gelu(dt, Y, blk["up_w"], blk["up_b"], out=U),
-         2.0 * M * D * F, (M * D + F * D + M * F) * es),
-        ("down_gemm", lambda: V.op_linear_residual(dt, U, blk["down_w"], blk["down_b"], Z),
-         2.0 * M * F * D, (M * F + D * F) * es + 8 * M * D),
-    ]
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in seq]
-          for _ in range(reps)]
+    work = {
+        "layernorm": (0.0, M * D * (4 + es) + 8 * D),
+        "qkv_gemm": (2.0 * M * D * 3 * D, (M * D + 3 * D * D + 3 * M * D) * es),
+        "attention": (4.0 * hd * pairs, 4 * M * D * es),
+        "out_gemm": (2.0 * M * D * D, (M * D + D * D) * es + 8 * M * D),
+        "up_gemm": (2.0 * M * D * F, (M * D + F * D + M * F) * es),
+        "down_gemm": (2.0 * M * F * D, (M * F + D * F) * es + 8 * M * D),
+    }
+
+    def layer(blk):
+        return [
+            ("layernorm", lambda: V.op_layernorm(Z, blk["ln1_w"], blk["ln1_b"], cfg.ln_eps, dt, out=Y)),
+            ("qkv_gemm", lambda: V.op_qkv_rope(dt, Y, blk["qkv_w"], blk["qkv_b"], B, N, H, rope=cfg.rope,
+                                               grid=cfg.grid, n_prefix=cfg.n_prefix, outs=(Q, K, Vt, tab),
+                                               table_ready=True)),
+            ("attention", lambda: V.op_attention(dt, Q, K, Vt, cfg.attn_mode, cfg.n_prefix,
+                                                 cfg.grid[1] * cfg.grid[2], out=O)),
+            ("out_gemm", lambda: V.op_linear_residual(dt, O, blk["out_w"], blk["out_b"], Z, ls=blk.get("ls1"))),
+            ("layernorm", lambda: V.op_layernorm(Z, blk["ln2_w"], blk["ln2_b"], cfg.ln_eps, dt, out=Y)),
+            ("up_gemm", lambda: V.op_linear_gelu(dt, Y, blk["up_w"], blk["up_b"], out=U)),
+            ("down_gemm", lambda: V.op_linear_residual(dt, U, blk["down_w"], blk["down_b"], Z, ls=blk.get("ls2"))),
+        ]
+
+    seqs = [layer(enc.blocks[r % len(enc.blocks)]) for r in range(reps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in seq] for seq in seqs]
     first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     busy()
     first.record(stream)
-    for r in range(reps):
-        for (name, fn, _, _), (e0, e1) in zip(seq, ev[r]):
+    for seq, evs in zip(seqs, ev):
+        for (name, fn), (e0, e1) in zip(seq, evs):
             e0.record(stream)
             fn()
             e1.record(stream)
     last.record(stream)
     torch.cuda.synchronize()
     acc, cnt = {}, {}
-    for r in range(reps):
-        for (name, _, _, _), (e0, e1) in zip(seq, ev[r]):
+    for seq, evs in zip(seqs, ev):
+        for (name, _), (e0, e1) in zip(seq, evs):
             acc[name] = acc.get(name, 0.0) + e0.elapsed_time(e1)
             cnt[name] = cnt.get(name, 0) + 1
-    busy_ms = sum(acc.values())
-    span_ms = first.elapsed_time(last)
-    log(f"[bench] layer sequence: kernels {busy_ms:.3f} ms of {span_ms:.3f} ms span over {reps} layers")
-    res = {}
-    for name, _, flops, nbytes in seq:
-        res[name] = (acc[name] / cnt[name], flops, nbytes)
+    log(f"[bench] layer sequence: kernels {sum(acc.values()):.3f} ms of {first.elapsed_time(last):.3f} ms span "
+        f"over {reps} layers")
+    res = {name: (acc[name] / cnt[name],) + work[name] for name in acc}
     # calibration for the HBM byte counters: a plain device copy of known size
     # (fp32 -> int32 keeps the element size, so torch launches its own copy kernel)
     src = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)

@@ -174,19 +174,30 @@ vitenc_status vitenc_op_layernorm(int32_t out_dtype, const float *x, const float
                                   const float *b, float eps, int32_t M, int32_t D, void *y,
                                   void *stream);
 
+/* a6 tables ("Architecture", "3-D RoPE"; SkyVision.cpp README, V-JEPA 2
+ * backend notes): fills rope_table (fp32, vitenc_rope_table_floats(...)
+ * floats, device) with the (cos, signed sin) pairs of every position of every
+ * axis -- d = 2*((head_dim/3)/2) pairs per position, in the tiled or
+ * interleaved frequency order, h and w positions rescaled by
+ * (rope_ref_grid - 1)/(g - 1) when rope_interpolate is set -- followed by
+ * the packed (t, h, w) grid position of each patch token.  head_dim even;
+ * grid axes 1..1023. */
+vitenc_status vitenc_op_rope_table(int32_t head_dim, int32_t rope_layout, int32_t rope_interpolate,
+                                   int32_t rope_ref_grid, float rope_theta, int32_t gt, int32_t gh,
+                                   int32_t gw, float *rope_table, void *stream);
+
 /* a5+a6 fused QKV projection with bias and 3-D RoPE ("Architecture", "3-D
  * RoPE"): Y T [B*N, D] times qkv_w [3D, D]^T + qkv_b, split into heads and
  * written as Q, K: T [B, H, N, hd] (RoPE applied to the patch rows, prefix
  * rows unrotated) and Vt: T [B, H, hd, ldv] (V transposed per head, ldv =
  * round_up(N, 64)).  rope = 0 disables the rotation; grid = (gt, gh, gw) and
- * n_prefix give the token geometry.  rope_table: fp32 scratch of at least
- * vitenc_rope_table_floats(...) floats, filled by this call. */
+ * n_prefix give the token geometry.  rope_table: as filled by
+ * vitenc_op_rope_table for this head width and grid (read only; NULL when
+ * rope = 0). */
 vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w,
                                  const float *qkv_b, int32_t B, int32_t N, int32_t D,
-                                 int32_t n_head, int32_t rope, int32_t rope_layout,
-                                 int32_t rope_interpolate, int32_t rope_ref_grid,
-                                 float rope_theta, int32_t gt, int32_t gh, int32_t gw,
-                                 int32_t n_prefix, float *rope_table, void *Q, void *K,
+                                 int32_t n_head, int32_t rope, int32_t gt, int32_t gh, int32_t gw,
+                                 int32_t n_prefix, const float *rope_table, void *Q, void *K,
                                  void *Vt, void *stream);
 int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32_t gw);
 

@@ -186,8 +186,14 @@ def test_step_entry_point_refusals():
     assert L.vitenc_op_layernorm(0, FAKE, FAKE, FAKE, 1e-6, 4, 5000, FAKE, None) == 6
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 48, 0, 0, 0, FAKE, None) == 6
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 1, 0, 0, FAKE, None) == 2
-    assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 0, 0, 0, 1e4, 2, 2, 2, 0,
+    assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 2, 2, 2, 0,
                                 FAKE, FAKE, FAKE, FAKE, None) == 2          # 8 patches + 0 prefix != 17
+    assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 8, 64, 1, 1, 2, 2, 2, 0,
+                                None, FAKE, FAKE, FAKE, None) == 3          # RoPE without a table
+    assert L.vitenc_op_rope_table(63, 0, 0, 0, 1e4, 2, 2, 2, FAKE, None) == 1   # odd head width
+    assert L.vitenc_op_rope_table(64, 0, 1, 0, 1e4, 2, 2, 2, FAKE, None) == 1   # interpolate, no ref grid
+    assert L.vitenc_op_rope_table(64, 0, 0, 0, 1e4, 2, 0, 2, FAKE, None) == 2   # empty grid
+    assert L.vitenc_op_rope_table(64, 0, 0, 0, 1e4, 2, 2, 2, None, None) == 3
     assert L.vitenc_op_embed(1, FAKE, 1, 3, 1, 30, 32, 1, 16, FAKE, FAKE, None, None, None, 64, FAKE, FAKE,
                              None) == 2
     assert L.vitenc_op_pool(FAKE, 1, 4, 8, 0, 4, FAKE, None) == 2

@@ -741,8 +741,8 @@ hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, in
 
 // Tile configuration (measured on the ViT-L shapes: M = 4096, N = 1024 ..
 // 4096): 256 x 256 tiles (8 waves) when they give at least one full wave of
-// workgroups over the 256 CUs, else 128 x 128 tiles (4 waves, two workgroups
-// per CU), both with direct-to-LDS slabs.  fp32 and shapes that break the
+// workgroups over the 256 CUs, else 128 x 128 tiles (8 waves of 64 x 32, up
+// to two workgroups per CU), both with direct-to-LDS slabs.  fp32 and shapes that break the
 // FAST conditions use the register-staged kernel.
 enum TileCfg { TILE_REG = 0, TILE_256x256 = 1, TILE_128x128 = 2 };
 
@@ -766,7 +766,7 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
     if constexpr (!std::is_same<T, float>::value) {
         switch (pick_tile(M, N, fast && small, false)) {
         case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
-        case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 2, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
+        case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
         default: break;
         }
     }

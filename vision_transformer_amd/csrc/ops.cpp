@@ -72,11 +72,26 @@ int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32
     return (int64_t)(gt + gh + gw) * d * 2 + (int64_t)gt * gh * gw; // cos/sin pairs, then packed positions
 }
 
+vitenc_status vitenc_op_rope_table(int32_t head_dim, int32_t rope_layout, int32_t rope_interpolate,
+                                  int32_t rope_ref_grid, float rope_theta, int32_t gt, int32_t gh, int32_t gw,
+                                  float *rope_table, void *stream) {
+    clear_error();
+    if (!rope_table) return op_fail(VITENC_ENULL, "rope_table is NULL");
+    if (head_dim <= 0 || head_dim % 2) return op_fail(VITENC_EINVAL, "head_dim %d (RoPE needs an even one)", head_dim);
+    if (gt <= 0 || gh <= 0 || gw <= 0 || gt > 1023 || gh > 1023 || gw > 1023)
+        return op_fail(VITENC_ESHAPE, "grid %dx%dx%d", gt, gh, gw);
+    if (rope_interpolate && rope_ref_grid <= 0) return op_fail(VITENC_EINVAL, "interpolate without ref grid");
+    const int d = 2 * ((head_dim / 3) / 2);
+    int *tok = reinterpret_cast<int *>(rope_table + (int64_t)(gt + gh + gw) * d * 2);
+    return op_dev(launch_rope_table(head_dim, rope_layout, rope_interpolate, rope_ref_grid, rope_theta, gt, gh, gw,
+                                    rope_table, tok, reinterpret_cast<hipStream_t>(stream)),
+                  "rope tables");
+}
+
 vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w, const float *qkv_b, int32_t B,
-                                 int32_t N, int32_t D, int32_t n_head, int32_t rope, int32_t rope_layout,
-                                 int32_t rope_interpolate, int32_t rope_ref_grid, float rope_theta, int32_t gt,
-                                 int32_t gh, int32_t gw, int32_t n_prefix, float *rope_table, void *Q, void *K,
-                                 void *Vt, void *stream) {
+                                 int32_t N, int32_t D, int32_t n_head, int32_t rope, int32_t gt, int32_t gh,
+                                 int32_t gw, int32_t n_prefix, const float *rope_table, void *Q, void *K, void *Vt,
+                                 void *stream) {
     clear_error();
     if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
     if (!Y || !qkv_w || !qkv_b || !Q || !K || !Vt) return op_fail(VITENC_ENULL, "a required pointer is NULL");
@@ -94,15 +109,10 @@ vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w
         if (gt <= 0 || gh <= 0 || gw <= 0 || gt > 1023 || gh > 1023 || gw > 1023 ||
             (int64_t)gt * gh * gw + n_prefix != N)
             return op_fail(VITENC_ESHAPE, "grid %dx%dx%d + %d prefix does not make %d tokens", gt, gh, gw, n_prefix, N);
-        if (rope_interpolate && rope_ref_grid <= 0) return op_fail(VITENC_EINVAL, "interpolate without ref grid");
         const int d = 2 * ((hd / 3) / 2);
-        float *tab = rope_table;
-        int *tok = reinterpret_cast<int *>(rope_table + (int64_t)(gt + gh + gw) * d * 2);
-        vitenc_status st = op_dev(
-            launch_rope_table(hd, rope_layout, rope_interpolate, rope_ref_grid, rope_theta, gt, gh, gw, tab, tok, s),
-            "rope tables");
-        if (st) return st;
-        ep.d_rot = d; ep.rope_tab = tab; ep.tok_pos = tok; ep.gt = gt; ep.gh = gh;
+        ep.d_rot = d; ep.rope_tab = rope_table;
+        ep.tok_pos = reinterpret_cast<const int *>(rope_table + (int64_t)(gt + gh + gw) * d * 2);
+        ep.gt = gt; ep.gh = gh;
         ep.rope_tab_pairs = (gt + gh + gw) * d;
     }
     return op_dev(launch_gemm(dtype, EPI_QKV, Y, D, qkv_w, D, B * N, 3 * D, D, ep, s), "qkv GEMM");

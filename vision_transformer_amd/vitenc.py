@@ -63,8 +63,8 @@ SIGNATURES = {
     "vitenc_encode": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp, c_vp, c_vp]),
     "vitenc_op_embed": (c_i32, [c_i32, c_vp] + [c_i32] * 7 + [c_vp] * 5 + [c_i32, c_vp, c_vp, c_vp]),
     "vitenc_op_layernorm": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_vp, c_vp]),
-    "vitenc_op_qkv_rope": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 8 + [c_f32] + [c_i32] * 4 +
-                           [c_vp] * 5),
+    "vitenc_op_rope_table": (c_i32, [c_i32] * 4 + [c_f32] + [c_i32] * 3 + [c_vp, c_vp]),
+    "vitenc_op_qkv_rope": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 9 + [c_vp] * 5),
     "vitenc_rope_table_floats": (ctypes.c_int64, [c_i32] * 4),
     "vitenc_op_attention": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp]),
     "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
@@ -245,9 +245,22 @@ def op_layernorm(x, w, b, eps, out_dtype, stream=None, out=None):
     return y
 
 
+def op_rope_table(head_dim, grid, rope_layout=0, rope_interpolate=0, rope_ref_grid=0, rope_theta=10000.0,
+                  stream=None, out=None, device="cuda"):
+    import torch
+    tab = out if out is not None else torch.empty(max(lib().vitenc_rope_table_floats(head_dim, *grid), 1),
+                                                  dtype=torch.float32, device=device)
+    check(lib().vitenc_op_rope_table(head_dim, rope_layout, rope_interpolate, rope_ref_grid, rope_theta, grid[0],
+                                     grid[1], grid[2], tab.data_ptr(), _stream(stream)))
+    return tab
+
+
 def op_qkv_rope(dtype, Y, qkv_w, qkv_b, B, N, n_head, rope=0, rope_layout=0, rope_interpolate=0,
-                rope_ref_grid=0, rope_theta=10000.0, grid=(1, 1, 1), n_prefix=0, stream=None, outs=None):
-    """outs: optional preallocated (Q, K, Vt, rope_table)."""
+                rope_ref_grid=0, rope_theta=10000.0, grid=(1, 1, 1), n_prefix=0, stream=None, outs=None,
+                table_ready=False):
+    """outs: optional preallocated (Q, K, Vt, rope_table).  The RoPE table is
+    filled first (vitenc_op_rope_table) unless table_ready says outs[3]
+    already holds it."""
     import torch
     D = Y.shape[1]
     hd = D // n_head
@@ -261,10 +274,11 @@ def op_qkv_rope(dtype, Y, qkv_w, qkv_b, B, N, n_head, rope=0, rope_layout=0, rop
         tab = torch.empty(max(nt, 1), dtype=torch.float32, device=Y.device)
     else:
         Q, K, Vt, tab = outs
+    if rope and not table_ready:
+        op_rope_table(hd, grid, rope_layout, rope_interpolate, rope_ref_grid, rope_theta, stream=stream, out=tab)
     check(lib().vitenc_op_qkv_rope(dtype, Y.data_ptr(), qkv_w.data_ptr(), qkv_b.data_ptr(), B, N, D, n_head, rope,
-                                   rope_layout, rope_interpolate, rope_ref_grid, rope_theta, grid[0], grid[1],
-                                   grid[2], n_prefix, tab.data_ptr(), Q.data_ptr(), K.data_ptr(), Vt.data_ptr(),
-                                   _stream(stream)))
+                                   grid[0], grid[1], grid[2], n_prefix, tab.data_ptr() if rope else None,
+                                   Q.data_ptr(), K.data_ptr(), Vt.data_ptr(), _stream(stream)))
     return Q, K, Vt
 
 
