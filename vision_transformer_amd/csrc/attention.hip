@@ -46,6 +46,10 @@ constexpr bool kPipe = VITENC_ATTN_PIPE; // scores of the next tile overlap this
 #define VITENC_ATTN_STAGES 4
 #endif
 constexpr int kStages = VITENC_ATTN_STAGES; // LDS ring depth of the direct-to-LDS kernel
+#ifndef VITENC_ATTN_WAVES
+#define VITENC_ATTN_WAVES 4
+#endif
+constexpr int kLdsWaves = VITENC_ATTN_WAVES; // waves (32 queries each) per workgroup, hd 64
 #ifndef VITENC_ATTN_DOT
 #define VITENC_ATTN_DOT 1
 #endif
@@ -409,8 +413,8 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, Chunk *dst
 }
 __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-template <typename T, int HD, int STAGES>
-__global__ __launch_bounds__(kThreads, 2) void attention_lds_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+template <typename T, int HD, int STAGES, int NWV>
+__global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                     const T *__restrict__ Vt, int N, int H, int ldv,
                                                                     int causal, int p, int S, float scale_log2,
                                                                     T *__restrict__ O) {
@@ -420,7 +424,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_lds_kernel(const T *__r
     constexpr int VCH = BKV / KPC;             // chunks per V^T row of a tile (8)
     constexpr int KRI = 64 / QCH;              // K rows per load instruction
     constexpr int VRI = 64 / VCH;              // V^T rows per load instruction
-    constexpr int NW = kThreads / 64;
+    constexpr int NW = NWV;
+    constexpr int kThreadsL = 64 * NWV, BQL = 32 * NWV; // threads, queries per workgroup
     constexpr int K_INST = BKV / (KRI * NW);   // per wave and tile
     constexpr int V_INST = HD / (VRI * NW);
     constexpr int PER = K_INST + V_INST;
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_lds_kernel(const T *__r
     const int bh = blockIdx.x;
     const int b = bh / H, head = bh - b * H;
     const int qt = gridDim.y - 1 - blockIdx.y; // heavy (late-frame) tiles first
-    const int q0 = qt * BQ;
+    const int q0 = qt * BQL;
     const int D = H * HD;
 
     const T *Qb = Q + (int64_t)bh * N * HD;
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_lds_kernel(const T *__r
     const int w_full_lo = wave_max_i(lo), w_full_hi = wave_min_i(hi);
     int wg_lo, wg_hi, tmp;
     key_interval(q0, N, causal, p, S, wg_lo, tmp);
-    key_interval(min(q0 + BQ - 1, N - 1), N, causal, p, S, tmp, wg_hi);
+    key_interval(min(q0 + BQL - 1, N - 1), N, causal, p, S, tmp, wg_hi);
     if (q0 < p) wg_hi = N;
     const int kt_begin = wg_lo / BKV, kt_end = (int)cdiv(wg_hi, BKV);
     const int ntiles = kt_end - kt_begin;
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_lds_kernel(const T *__r
         if (kb + BKV > N) {
             // ragged last tile: V^T columns of keys >= N hold whatever follows
             // the last token in memory; make them zero
-            for (int e = tid; e < HD * BKV; e += kThreads) {
+            for (int e = tid; e < HD * BKV; e += kThreadsL) {
                 const int d = e / BKV, key = e % BKV;
                 if (kb + key >= N) {
                     T *row = reinterpret_cast<T *>(&sV[stg][d][0]);
@@ -607,8 +612,10 @@ template <typename T, int HD>
 hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal, int p,
                     int S, void *O, hipStream_t s) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, BQ));
-    hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages>), grid, dim3(kThreads), 0, s,
+    // hd 32 tiles are too small to split their loads over more than 4 waves
+    constexpr int NWV = HD == 64 ? kLdsWaves : 4;
+    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, 32 * NWV));
+    hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV>), grid, dim3(64 * NWV), 0, s,
                        reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
                        reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, scale_log2, reinterpret_cast<T *>(O));
     return hipGetLastError();
