@@ -115,7 +115,7 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
 // consecutive rows of one column) because V is stored transposed per head.
 // ri: LDS scratch for BM row descriptors, stage: this wave's staging area.
 // Every thread of the workgroup must call this (it contains a barrier).
-template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, typename AccT>
+template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, bool SWAP, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, float *stage, float2 *lds_tab,
                                               int lds_tab_cap, int m0, int n0, int woff_m, int woff_n, int M, int N,
                                               const EpiArgs &ep) {
@@ -126,7 +126,7 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
     const int lcol = lane & (MI - 1);
     auto vrow = [&](int i) { return MI == 32 ? acc_row(i, lane >> 5) : 4 * (lane >> 4) + i; };
 
-    if constexpr (EPI == EPI_QKV && MI == 32) {
+    if constexpr (EPI == EPI_QKV && MI == 32 && !SWAP) {
         // A tile of V columns only: the accumulators already hold, per lane,
         // one feature and runs of 4 consecutive tokens (slots 4q..4q+3 are rows
         // 8q + 4(l/32) + 0..3), which is V^T's layout: store them directly as
@@ -327,10 +327,23 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
 #pragma clang loop unroll(full)
     for (int fm = 0; fm < FM; ++fm) {
         // stage block row fm of this wave's accumulators
+        if constexpr (SWAP) {
+            // the block holds D^T (weight fragment as MFMA operand A): lane l has
+            // row l % 32 and, per slot group q, 4 consecutive columns 8q + 4(l/32)
+            static_assert(MI == 32, "swapped staging assumes 32x32 blocks");
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-            for (int i = 0; i < NV; ++i) stage[vrow(i) * LD + fn * MI + lcol] = acc[fm][fn][i];
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4 *>(&stage[lcol * LD + fn * MI + 8 * q + 4 * (lane >> 5)]) =
+                        make_float4(acc[fm][fn][4 * q], acc[fm][fn][4 * q + 1], acc[fm][fn][4 * q + 2],
+                                    acc[fm][fn][4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int i = 0; i < NV; ++i) stage[vrow(i) * LD + fn * MI + lcol] = acc[fm][fn][i];
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -518,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     float *stage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * 32 * (WN + 4);
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(smem) - kRiBytes - kStageBytes) / 8;
-    gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN>(acc, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M,
+    gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN, false>(acc, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M,
                                                         N, ep);
 }
 
@@ -535,6 +548,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 // choosing which chunk each lane fetches.  A ring of STAGES LDS stages keeps
 // STAGES - 1 slabs in flight while one is multiplied.  Requires the FAST
 // conditions (K a multiple of the slab width, 16-byte aligned rows).
+#ifndef VITENC_GEMM_SWAP
+#define VITENC_GEMM_SWAP 1
+#endif
+// The direct-to-LDS kernel computes each 32x32 block transposed (weight
+// fragment as MFMA operand A), so that every lane holds runs of 4 consecutive
+// output columns and stages them into LDS with 16-byte writes.
+constexpr bool kSwap = VITENC_GEMM_SWAP;
+
 template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
                                                                      const T *__restrict__ W, int64_t ldw, int M,
@@ -629,7 +650,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                if constexpr (MI == 32) mfma_chunk<T>(acc[fm][fn], a[fm], b[fn]);
+                if constexpr (MI == 32 && kSwap) mfma_chunk<T>(acc[fm][fn], b[fn], a[fm]); // D^T
+                else if constexpr (MI == 32) mfma_chunk<T>(acc[fm][fn], a[fm], b[fn]);
                 else mfma16_chunk<T>(acc[fm][fn], a[fm], b[fn]);
             }
     };
@@ -713,7 +735,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     float *estage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * MI * (WN + 4);
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(lds) - kRiBytes - kStageBytes) / 8;
-    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
+    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, kSwap>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
                                                   ep);
 }
 
