@@ -324,3 +324,130 @@ def make_workload(cfg: EncoderConfig, seed: Optional[int] = None) -> Workload:
                             ones, zeros, ones, zeros, ls1, ls2, st))
     w = Weights(pw, pb, pos, cls, mod, blocks, ones, zeros, wstore)
     return Workload(cfg, pixels, w)
+
+
+# ---------------------------------------------------------------------------
+# masked predictor (the V-JEPA 2 latent predictor that follows the encoder)
+# ---------------------------------------------------------------------------
+@dataclass
+class PredictorConfig:
+    """A masked-latent predictor: context encoder features are projected to
+    embed_dim, joined by a mask token at every target position, put in token
+    order, run through n_layer pre-LN blocks with 3-D RoPE on the token
+    positions, normalised, and the target rows projected back to enc_dim."""
+    name: str
+    embed_dim: int = 384
+    enc_dim: int = 1024
+    n_layer: int = 12
+    n_head: int = 12
+    ffn_dim: int = 1536
+    n_mask_tokens: int = 10
+    ln_eps: float = 1e-6
+    rope_theta: float = 10000.0
+    rope_layout: int = LAYOUT_TILED
+    grid: tuple = (8, 16, 16)
+    batch: int = 2
+    n_ctx: int = 1024
+    n_tgt: int = 1024
+    mask_index: int = 1
+    dtype: int = DTYPE_BF16
+    std_w: float = 0.02
+    std_tok: float = 0.02
+    seed: int = 2000
+
+    @property
+    def head_dim(self) -> int:
+        return self.embed_dim // self.n_head
+
+    @property
+    def n_grid(self) -> int:
+        return self.grid[0] * self.grid[1] * self.grid[2]
+
+    @property
+    def n_tokens(self) -> int:
+        return self.n_ctx + self.n_tgt
+
+    def replace(self, **kw) -> "PredictorConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return PredictorConfig(**d)
+
+    def hparams(self) -> Dict:
+        return dict(embed_dim=self.embed_dim, enc_dim=self.enc_dim, n_layer=self.n_layer, n_head=self.n_head,
+                    ffn_dim=self.ffn_dim, n_mask_tokens=self.n_mask_tokens, ln_eps=self.ln_eps,
+                    rope_theta=self.rope_theta, rope_layout=self.rope_layout, grid=tuple(self.grid),
+                    dtype=self.dtype)
+
+    def flops(self) -> float:
+        M, D, F, De = self.batch * self.n_tokens, self.embed_dim, self.ffn_dim, self.enc_dim
+        per_layer = 2.0 * M * D * (3 * D + D + 2 * F) + 4.0 * D * self.batch * self.n_tokens ** 2
+        return (2.0 * self.batch * self.n_ctx * De * D + self.n_layer * per_layer
+                + 2.0 * self.batch * self.n_tgt * D * De)
+
+
+# V-JEPA 2 ViT-L predictor shape: 12 blocks of width 384, 12 heads of 32, on the
+# 8 x 16 x 16 token grid of a 16-frame 256-px clip, half the tokens as context
+PREDICTOR = PredictorConfig("vjepa2_predictor")
+
+
+@dataclass
+class PredictorWeights:
+    embed_w: np.ndarray          # [embed_dim, enc_dim]
+    embed_b: np.ndarray
+    mask_tokens: np.ndarray      # [n_mask_tokens, embed_dim]
+    blocks: List[Block]
+    norm_w: np.ndarray
+    norm_b: np.ndarray
+    proj_w: np.ndarray           # [enc_dim, embed_dim]
+    proj_b: np.ndarray
+    store: Dict[str, np.ndarray] = field(default_factory=dict)
+
+
+@dataclass
+class PredictorWorkload:
+    cfg: PredictorConfig
+    enc_tokens: np.ndarray       # fp32 [B, n_grid, enc_dim], unit-scale encoder features
+    ctx_ids: np.ndarray          # int32 [B, n_ctx], strictly increasing
+    tgt_ids: np.ndarray          # int32 [B, n_tgt], strictly increasing, disjoint from ctx_ids
+    weights: PredictorWeights
+
+
+def make_predictor_workload(cfg: PredictorConfig, seed: Optional[int] = None) -> PredictorWorkload:
+    """Draw order: encoder features, per item a permutation of the grid (the
+    first n_ctx ids are the context, the next n_tgt the targets), embed
+    weight and bias, mask tokens, the blocks (as the encoder's), proj."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    B, Ng, De, D, F = cfg.batch, cfg.n_grid, cfg.enc_dim, cfg.embed_dim, cfg.ffn_dim
+    assert cfg.n_ctx + cfg.n_tgt <= Ng
+    dt = cfg.dtype
+    enc = rng.standard_normal((B, Ng, De), dtype=np.float32)
+    ctx, tgt = [], []
+    for _ in range(B):
+        perm = rng.permutation(Ng)
+        ctx.append(np.sort(perm[:cfg.n_ctx]))
+        tgt.append(np.sort(perm[cfg.n_ctx:cfg.n_ctx + cfg.n_tgt]))
+    ctx_ids = np.stack(ctx).astype(np.int32).reshape(B, cfg.n_ctx)
+    tgt_ids = np.stack(tgt).astype(np.int32).reshape(B, cfg.n_tgt)
+    st = {}
+    st["embed_w"], embed_w = quantise(_normal(rng, (D, De), cfg.std_w), dt)
+    embed_b = _normal(rng, (D,), cfg.std_w)
+    mask_tokens = _normal(rng, (cfg.n_mask_tokens, D), cfg.std_tok)
+    ones = np.ones(D, np.float32)
+    zeros = np.zeros(D, np.float32)
+    blocks = []
+    for _ in range(cfg.n_layer):
+        bs = {}
+        bs["qkv_w"], qkv_w = quantise(_normal(rng, (3 * D, D), cfg.std_w), dt)
+        qkv_b = _normal(rng, (3 * D,), cfg.std_w)
+        bs["out_w"], out_w = quantise(_normal(rng, (D, D), cfg.std_w), dt)
+        out_b = _normal(rng, (D,), cfg.std_w)
+        bs["up_w"], up_w = quantise(_normal(rng, (F, D), cfg.std_w), dt)
+        up_b = _normal(rng, (F,), cfg.std_w)
+        bs["down_w"], down_w = quantise(_normal(rng, (D, F), cfg.std_w), dt)
+        down_b = _normal(rng, (D,), cfg.std_w)
+        blocks.append(Block(qkv_w, qkv_b, out_w, out_b, up_w, up_b, down_w, down_b,
+                            ones, zeros, ones, zeros, None, None, bs))
+    st["proj_w"], proj_w = quantise(_normal(rng, (De, D), cfg.std_w), dt)
+    proj_b = _normal(rng, (De,), cfg.std_w)
+    w = PredictorWeights(embed_w, embed_b, mask_tokens, blocks, ones, zeros, proj_w, proj_b, st)
+    return PredictorWorkload(cfg, enc, ctx_ids, tgt_ids, w)
