@@ -143,6 +143,75 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
                             int32_t H, int32_t W, void *workspace, size_t ws_bytes,
                             float *out_tokens, float *out_pooled, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Masked-latent predictor (SkyVision.cpp README, V-JEPA 2 backend notes,
+ * "masked-latent predictor"; hyperparameters and tensors of jepa.cpp "GGUF
+ * schema (v1)", section "Predictor (jepa.pred.*)"):
+ *
+ *   x_ctx = enc_tokens[ctx_ids] embed_w^T + embed_b        (enc_dim -> embed_dim)
+ *   x_tgt = mask_tokens[mask_index] at every target id
+ *   x     = [x_ctx; x_tgt] put in increasing token-id order
+ *   per block (the encoder's block, full attention, no prefix token, 3-D RoPE
+ *   at each token's (t, h, w) on the grid, no interpolation):
+ *         x += attn(ln1(x));  x += ffn(ln2(x))
+ *   out   = norm(x) at the target ids, in the order of tgt_ids, proj_w^T + proj_b
+ * ------------------------------------------------------------------------- */
+
+/* embed_dim D (1..4096), enc_dim De (1..65536), n_layer, n_head (head_dim
+ * D/n_head must be 32 or 64), ffn_dim F, n_mask_tokens (>= 1), ln_eps,
+ * rope_theta (> 0), rope_layout TILED or INTERLEAVED, the token grid
+ * grid_t x grid_h x grid_w (1..1023 each) on which ids are numbered in the
+ * encoder's token order (id = (t*grid_h + h)*grid_w + w), dtype as the encoder. */
+typedef struct {
+    int32_t embed_dim, enc_dim, n_layer, n_head, ffn_dim, n_mask_tokens;
+    float ln_eps, rope_theta;
+    int32_t rope_layout, grid_t, grid_h, grid_w;
+    int32_t dtype;
+} vitenc_pred_hparams;
+
+/* embed_w [D, De] and proj_w [De, D] in the model dtype; embed_b [D],
+ * mask_tokens [n_mask_tokens, D], norm_w/norm_b [D], proj_b [De] fp32;
+ * blocks: HOST array of n_layer vitenc_block_weights with the predictor's
+ * widths (D, F; layer scales ignored), copied at creation. */
+typedef struct {
+    const void *embed_w;  const float *embed_b;
+    const float *mask_tokens;
+    const vitenc_block_weights *blocks;
+    const float *norm_w, *norm_b;
+    const void *proj_w;   const float *proj_b;
+} vitenc_pred_weights;
+
+typedef struct vitenc_predictor vitenc_predictor;
+
+/* Refusals as vitenc_model_create: EINVAL for ranges and enum values, ENULL
+ * for a missing weight, EUNSUPPORTED for head_dim other than 32 or 64 or
+ * embed_dim above 4096. */
+vitenc_status vitenc_predictor_create(const vitenc_pred_hparams *hp, const vitenc_pred_weights *w,
+                                      vitenc_predictor **out);
+void vitenc_predictor_destroy(vitenc_predictor *p);
+
+/* Bytes of device workspace vitenc_predict needs for B items of n_ctx context
+ * and n_tgt target ids.  Refusals: ESHAPE (B, n_ctx or n_tgt below 1,
+ * n_ctx + n_tgt above the grid's token count). */
+vitenc_status vitenc_predict_workspace_size(const vitenc_predictor *p, int32_t B, int32_t n_ctx,
+                                            int32_t n_tgt, size_t *bytes);
+
+/* Predicts the encoder features of the target tokens of B items.
+ * enc_tokens: fp32 [B, n_enc, De], the encoder's patch-token features in
+ * token order (n_enc must equal grid_t*grid_h*grid_w); ctx_ids int32
+ * [B, n_ctx] and tgt_ids int32 [B, n_tgt]: per item, each list strictly
+ * increasing, both within [0, n_enc) and disjoint.  The ids are device data
+ * and are NOT checked here (the check would need a synchronisation): ids
+ * that break the contract give unspecified values in out, but every access
+ * stays within the buffers.  mask_index: the mask token that fills the
+ * targets, in [0, n_mask_tokens).  out: fp32 [B, n_tgt, De].  workspace as
+ * vitenc_encode's, of vitenc_predict_workspace_size() bytes.  Refusals: those
+ * of the workspace size, ENULL, ESHAPE (n_enc), EINVAL (mask_index),
+ * EWORKSPACE. */
+vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens, int32_t B, int32_t n_enc,
+                             const int32_t *ctx_ids, int32_t n_ctx, const int32_t *tgt_ids, int32_t n_tgt,
+                             int32_t mask_index, void *workspace, size_t ws_bytes, float *out, void *stream);
+
 /* Thread-local text of the last refusal on this thread ("" if none). */
 const char *vitenc_error_text(void);
 int32_t vitenc_abi_version(void);

@@ -36,14 +36,14 @@ vitenc_status fail(vitenc_status st, const char *fmt, ...) {
     return st;
 }
 void clear_error() { g_error.clear(); }
-} // namespace vitenc
-
-namespace {
 
 vitenc_status device_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return VITENC_OK;
     return fail(VITENC_EDEVICE, "%s: %s", what, hipGetErrorString(e));
 }
+} // namespace vitenc
+
+namespace {
 
 constexpr int64_t kMaxTokens = int64_t(1) << 22;   // per item, as the pages' loader limit
 constexpr int kMaxGrid = 1023;                     // per axis (packed 10-bit positions)
@@ -259,42 +259,17 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
                                     pl.gh, pl.gw, rope_tab, tok_pos, s),
                   "rope tables");
 
+    BlockGeom g;
+    g.dtype = dt; g.B = B; g.N = pl.N; g.D = D; g.F = F; g.n_head = pl.nh; g.head_dim = pl.hd; g.ldv = pl.ldv;
+    g.prefix = pl.p; g.attn_mode = hp.attn_mode; g.tokens_per_frame = pl.gh * pl.gw; g.layer_scale = hp.layer_scale;
+    g.eps = hp.ln_eps;
+    g.rope = hp.rope; g.gt = pl.gt; g.gh = pl.gh; g.gw = pl.gw; g.rope_tab = rope_tab; g.tok_pos = tok_pos;
+    BlockBufs bb;
+    bb.Z = Z; bb.Y = Y; bb.Q = Q; bb.K = Kb; bb.Vt = Vt; bb.O = O; bb.U = U;
     for (int l = 0; l < hp.n_layer; ++l) {
-        const vitenc_block_weights &bw = m->blocks[l];
-        CHECK_DEV(launch_layernorm(dt, Z, bw.ln1_w, bw.ln1_b, hp.ln_eps, M, D, Y, s), "ln1");
-        {
-            EpiArgs ep;
-            ep.bias = bw.qkv_b;
-            ep.Q = Q; ep.K = Kb; ep.Vt = Vt;
-            ep.D = D; ep.head_dim = pl.hd; ep.ldv = pl.ldv;
-            ep.Ntok = pl.N; ep.prefix = pl.p;
-            ep.rope = hp.rope;
-            ep.d_rot = 2 * ((pl.hd / 3) / 2);
-            ep.rope_tab = rope_tab; ep.tok_pos = tok_pos;
-            ep.rope_tab_pairs = (pl.gt + pl.gh + pl.gw) * ep.d_rot;
-            ep.gt = pl.gt; ep.gh = pl.gh;
-            CHECK_DEV(launch_gemm(dt, EPI_QKV, Y, D, bw.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
-        }
-        CHECK_DEV(launch_attention(dt, Q, Kb, Vt, B, pl.N, pl.nh, pl.hd, pl.ldv, hp.attn_mode, pl.p, pl.gh * pl.gw, O, s),
-                  "attention");
-        {
-            EpiArgs ep;
-            ep.bias = bw.out_b; ep.Z = Z; ep.ldz = D;
-            ep.ls = hp.layer_scale ? bw.ls1 : nullptr;
-            CHECK_DEV(launch_gemm(dt, EPI_RESID, O, D, bw.out_w, D, M, D, D, ep, s), "out GEMM");
-        }
-        CHECK_DEV(launch_layernorm(dt, Z, bw.ln2_w, bw.ln2_b, hp.ln_eps, M, D, Y, s), "ln2");
-        {
-            EpiArgs ep;
-            ep.bias = bw.up_b; ep.out = U; ep.ldo = F;
-            CHECK_DEV(launch_gemm(dt, EPI_GELU, Y, D, bw.up_w, D, M, F, D, ep, s), "up GEMM");
-        }
-        {
-            EpiArgs ep;
-            ep.bias = bw.down_b; ep.Z = Z; ep.ldz = D;
-            ep.ls = hp.layer_scale ? bw.ls2 : nullptr;
-            CHECK_DEV(launch_gemm(dt, EPI_RESID, U, F, bw.down_w, F, M, D, F, ep, s), "down GEMM");
-        }
+        const char *what = "block";
+        const hipError_t e = run_block(g, bb, m->blocks[l], s, &what);
+        CHECK_DEV(e, what);
     }
     CHECK_DEV(launch_layernorm(DT_F32, Z, m->w.norm_w, m->w.norm_b, hp.ln_eps, M, D, out_tokens, s), "final norm");
     if (out_pooled) CHECK_DEV(launch_pool(out_tokens, B, pl.N, D, hp.cls_token, pl.p, out_pooled, s), "pool");

@@ -1,0 +1,59 @@
+// The launch sequence of one pre-LN block (jepa.cpp "Architecture", "The
+// shared ViT graph"):  x += ls1 * out(attn(rope(qkv(ln1(x)))));
+// x += ls2 * down(gelu(up(ln2(x)))).  Shared by the encoder and the predictor.
+#include "launch.h"
+
+namespace vitenc {
+
+hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_weights &w, hipStream_t s,
+                     const char **what) {
+    const int M = g.B * g.N, D = g.D, F = g.F;
+    hipError_t e;
+#define STEP(expr, name)                                                                                          \
+    do {                                                                                                          \
+        e = (expr);                                                                                               \
+        if (e != hipSuccess) {                                                                                    \
+            *what = name;                                                                                         \
+            return e;                                                                                             \
+        }                                                                                                         \
+    } while (0)
+    STEP(launch_layernorm(g.dtype, b.Z, w.ln1_w, w.ln1_b, g.eps, M, D, b.Y, s), "ln1");
+    {
+        EpiArgs ep;
+        ep.bias = w.qkv_b;
+        ep.Q = b.Q; ep.K = b.K; ep.Vt = b.Vt;
+        ep.D = D; ep.head_dim = g.head_dim; ep.ldv = g.ldv;
+        ep.Ntok = g.N; ep.prefix = g.prefix;
+        ep.rope = g.rope;
+        ep.d_rot = 2 * ((g.head_dim / 3) / 2);
+        ep.rope_tab = g.rope_tab; ep.tok_pos = g.tok_pos; ep.tok_pos_stride = g.tok_pos_stride;
+        ep.rope_tab_pairs = (g.gt + g.gh + g.gw) * ep.d_rot;
+        ep.gt = g.gt; ep.gh = g.gh;
+        STEP(launch_gemm(g.dtype, EPI_QKV, b.Y, D, w.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
+    }
+    STEP(launch_attention(g.dtype, b.Q, b.K, b.Vt, g.B, g.N, g.n_head, g.head_dim, g.ldv, g.attn_mode, g.prefix,
+                          g.tokens_per_frame, b.O, s),
+         "attention");
+    {
+        EpiArgs ep;
+        ep.bias = w.out_b; ep.Z = b.Z; ep.ldz = D;
+        ep.ls = g.layer_scale ? w.ls1 : nullptr;
+        STEP(launch_gemm(g.dtype, EPI_RESID, b.O, D, w.out_w, D, M, D, D, ep, s), "out GEMM");
+    }
+    STEP(launch_layernorm(g.dtype, b.Z, w.ln2_w, w.ln2_b, g.eps, M, D, b.Y, s), "ln2");
+    {
+        EpiArgs ep;
+        ep.bias = w.up_b; ep.out = b.U; ep.ldo = F;
+        STEP(launch_gemm(g.dtype, EPI_GELU, b.Y, D, w.up_w, D, M, F, D, ep, s), "up GEMM");
+    }
+    {
+        EpiArgs ep;
+        ep.bias = w.down_b; ep.Z = b.Z; ep.ldz = D;
+        ep.ls = g.layer_scale ? w.ls2 : nullptr;
+        STEP(launch_gemm(g.dtype, EPI_RESID, b.U, F, w.down_w, F, M, D, F, ep, s), "down GEMM");
+    }
+#undef STEP
+    return hipSuccess;
+}
+
+} // namespace vitenc

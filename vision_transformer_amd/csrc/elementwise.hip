@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int d, int layout, int 
         tab[2 * idx + 1] = (float)((j & 1) ? sin(ang) : -sin(ang));
     }
     const int np = gt * gh * gw;
-    if (idx < np) {
+    if (tok_pos && idx < np) {
         const int t = idx / (gh * gw), h = (idx / gw) % gh, w = idx % gw;
         tok_pos[idx] = t | (h << 10) | (w << 20);
     }

@@ -169,9 +169,14 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
             RowInfo info{0, 0, 0, {0, 0, 0}, 0};
             if (row < M) {
                 if constexpr (EPI == EPI_PATCH) {
-                    const int b = row / ep.Np, n = row - b * ep.Np;
-                    info.out_row = b * ep.Ntok + ep.prefix + n;
-                    info.pos = ep.prefix + n;
+                    if (ep.row_map) {
+                        info.out_row = ep.row_map[row];
+                        info.pos = 0;
+                    } else {
+                        const int b = row / ep.Np, n = row - b * ep.Np;
+                        info.out_row = b * ep.Ntok + ep.prefix + n;
+                        info.pos = ep.prefix + n;
+                    }
                 } else {
                     const int b = row / ep.Ntok, tok = row - b * ep.Ntok;
                     info.out_row = b;
@@ -179,7 +184,7 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
                     info.pos = 0;
                     info.qk_off = ((int64_t)b * (ep.D / ep.head_dim) * ep.Ntok + tok) * ep.head_dim;
                     if (ep.rope && tok >= ep.prefix) {
-                        const int pk = ep.tok_pos[tok - ep.prefix];
+                        const int pk = ep.tok_pos[(int64_t)b * ep.tok_pos_stride + tok - ep.prefix];
                         info.pos = 1;
                         info.base[0] = (pk & 1023) * ep.d_rot;
                         info.base[1] = (ep.gt + ((pk >> 10) & 1023)) * ep.d_rot;

@@ -10,6 +10,8 @@ namespace vitenc {
 // thread-local refusal text behind vitenc_error_text()
 vitenc_status fail(vitenc_status st, const char *fmt, ...);
 void clear_error();
+// VITENC_OK, or EDEVICE with "what: <HIP error text>"
+vitenc_status device_status(hipError_t e, const char *what);
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 inline int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
@@ -27,10 +29,12 @@ struct EpiArgs {
     float *Z = nullptr;
     int64_t ldz = 0;
     const float *ls = nullptr;
-    // PATCH: GEMM row m = b*Np + n -> token row b*Ntok + prefix + n
+    // PATCH: GEMM row m = b*Np + n -> token row b*Ntok + prefix + n, or
+    // row_map[m] when row_map is set (then pos and mod must be null)
     const float *pos = nullptr;      // fp32 [Ntok, ldz] or null
     const float *mod = nullptr;      // fp32 [ldz] or null
     int Np = 0, Ntok = 0, prefix = 0;
+    const int *row_map = nullptr;
     // QKV: GEMM row m = b*Ntok + tok; column c in [0, 3D)
     void *Q = nullptr, *K = nullptr, *Vt = nullptr;
     int D = 0, head_dim = 0, ldv = 0;
@@ -38,6 +42,7 @@ struct EpiArgs {
     const float *rope_tab = nullptr; // cos / signed sin pairs per (axis, position, j)
     int rope_tab_pairs = 0;          // number of (cos, signed sin) pairs in rope_tab
     const int *tok_pos = nullptr;    // packed (t, h, w) per patch token
+    int tok_pos_stride = 0;          // 0: one position list for all items; else per item
     int gt = 0, gh = 0;              // axis offsets into rope_tab
     // A has 2*kwrap columns whose second half pairs with W's columns again
     // (the split-pixel patch embedding); 0: A and W share K
@@ -71,11 +76,47 @@ hipError_t launch_prefix_rows(const float *cls, const float *pos, const float *m
 hipError_t launch_rope_table(int head_dim, int layout, int interpolate, int ref_grid, float theta,
                              int gt, int gh, int gw, float *rope_tab, int *tok_pos, hipStream_t s);
 
+// masked predictor: merge the sorted context and target id lists of each item
+// into position order (row_ctx / row_tgt: the Z row of each, b*(nc+nt) + rank)
+// and write the packed (t, h, w) of every position-ordered token to tok_pos
+// [B*(nc+nt)]
+hipError_t launch_pred_order(const int *ctx_ids, int nc, const int *tgt_ids, int nt, int B, int gt, int gh, int gw,
+                             int *row_ctx, int *row_tgt, int *tok_pos, hipStream_t s);
+// out row r (dtype out_dtype, stride ldo) = fp32 src row rows[r] when rows is
+// set, else row ids[r] of item r / per_item (src_rows rows per item), D
+// columns; split (16-bit out only): rounded value in [0, D), remainder in [D, 2D)
+hipError_t launch_gather_rows(int out_dtype, const float *src, int64_t lds, const int *rows, const int *ids,
+                              int per_item, int src_rows, int R, int D, bool split, void *out, int64_t ldo,
+                              hipStream_t s);
+// Z row rows[r] = vec (D fp32) for r in [0, R)
+hipError_t launch_fill_rows(const float *vec, const int *rows, int R, int D, float *Z, hipStream_t s);
+hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
+
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N,
                             int H, int head_dim, int ldv, int attn_mode, int n_prefix,
                             int tokens_per_frame, void *O, hipStream_t s);
 
 hipError_t launch_pool(const float *X, int B, int N, int D, int cls, int n_prefix, float *pooled,
                        hipStream_t s);
+
+// One pre-LN block over the fp32 residual stream Z of B items of N tokens
+// (jepa.cpp "Architecture", "The shared ViT graph"): the encoder and the
+// predictor run the same sequence of launches.
+struct BlockGeom {
+    int dtype = 0, B = 0, N = 0, D = 0, F = 0, n_head = 0, head_dim = 0, ldv = 0;
+    int prefix = 0, attn_mode = 0, tokens_per_frame = 0, layer_scale = 0;
+    float eps = 0.0f;
+    int rope = 0, gt = 0, gh = 0, gw = 0;
+    const float *rope_tab = nullptr;
+    const int *tok_pos = nullptr;
+    int tok_pos_stride = 0;          // 0: tok_pos shared by all items
+};
+struct BlockBufs {
+    float *Z = nullptr;              // fp32 [B*N, D]
+    void *Y = nullptr, *Q = nullptr, *K = nullptr, *Vt = nullptr, *O = nullptr, *U = nullptr;
+};
+// *what names the failing launch
+hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_weights &w, hipStream_t s,
+                     const char **what);
 
 } // namespace vitenc

@@ -51,6 +51,18 @@ class Weights(ctypes.Structure):
                 ("norm_b", c_vp)]
 
 
+class PredHparams(ctypes.Structure):
+    _fields_ = [(n, c_i32) for n in ("embed_dim", "enc_dim", "n_layer", "n_head", "ffn_dim", "n_mask_tokens")] + \
+               [("ln_eps", c_f32), ("rope_theta", c_f32)] + \
+               [(n, c_i32) for n in ("rope_layout", "grid_t", "grid_h", "grid_w", "dtype")]
+
+
+class PredWeights(ctypes.Structure):
+    _fields_ = [("embed_w", c_vp), ("embed_b", c_vp), ("mask_tokens", c_vp),
+                ("blocks", ctypes.POINTER(BlockWeights)), ("norm_w", c_vp), ("norm_b", c_vp),
+                ("proj_w", c_vp), ("proj_b", c_vp)]
+
+
 _LIB = None
 
 # exported symbol -> (restype, argtypes)
@@ -70,6 +82,12 @@ SIGNATURES = {
     "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_linear_gelu": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_pool": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vitenc_predictor_create": (c_i32, [ctypes.POINTER(PredHparams), ctypes.POINTER(PredWeights),
+                                        ctypes.POINTER(c_vp)]),
+    "vitenc_predictor_destroy": (None, [c_vp]),
+    "vitenc_predict_workspace_size": (c_i32, [c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
+    "vitenc_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_size, c_vp,
+                               c_vp]),
 }
 
 
@@ -216,6 +234,109 @@ class Encoder:
         ws, out, pooled = self.alloc(B, T, H, W, device=pixels.device)
         self.encode_into(pixels, ws, out, pooled, stream)
         return out, pooled
+
+
+def check_pred_ids(ctx_ids, tgt_ids, n_enc):
+    """The id contract of vitenc_predict, checked on the host: per item each
+    list strictly increasing, within [0, n_enc), and the two disjoint."""
+    c = np.asarray(ctx_ids.cpu() if hasattr(ctx_ids, "cpu") else ctx_ids)
+    t = np.asarray(tgt_ids.cpu() if hasattr(tgt_ids, "cpu") else tgt_ids)
+    if c.ndim != 2 or t.ndim != 2 or c.shape[0] != t.shape[0]:
+        raise ValueError("ctx_ids / tgt_ids must be [B, n] with the same B")
+    for name, a in (("ctx_ids", c), ("tgt_ids", t)):
+        if a.size and (a.min() < 0 or a.max() >= n_enc):
+            raise ValueError(f"{name} outside [0, {n_enc})")
+        if a.shape[1] > 1 and not (np.diff(a, axis=1) > 0).all():
+            raise ValueError(f"{name} not strictly increasing within an item")
+    for b in range(c.shape[0]):
+        if np.intersect1d(c[b], t[b]).size:
+            raise ValueError(f"item {b}: context and target ids overlap")
+
+
+class Predictor:
+    """A masked-latent predictor handle over device-resident weights."""
+
+    def __init__(self, hp: Dict, tensors: Dict, blocks):
+        self.hp = dict(hp)
+        self.tensors = tensors
+        self.blocks = blocks
+        L = lib()
+        self._hp = PredHparams()
+        for name, _ in PredHparams._fields_:
+            setattr(self._hp, name, self.hp.get(name, 0))
+        self._bw = (BlockWeights * len(blocks))()
+        for i, b in enumerate(blocks):
+            for n in BLOCK_FIELDS:
+                setattr(self._bw[i], n, _ptr(b.get(n)))
+        self._w = PredWeights(_ptr(tensors["embed_w"]), _ptr(tensors["embed_b"]), _ptr(tensors["mask_tokens"]),
+                              ctypes.cast(self._bw, ctypes.POINTER(BlockWeights)), _ptr(tensors["norm_w"]),
+                              _ptr(tensors["norm_b"]), _ptr(tensors["proj_w"]), _ptr(tensors["proj_b"]))
+        h = c_vp()
+        check(L.vitenc_predictor_create(ctypes.byref(self._hp), ctypes.byref(self._w), ctypes.byref(h)))
+        self.handle = h
+
+    @staticmethod
+    def hparams_of(cfg) -> Dict:
+        hp = cfg.hparams()
+        gt, gh, gw = hp.pop("grid")
+        hp.update(grid_t=gt, grid_h=gh, grid_w=gw)
+        return hp
+
+    @classmethod
+    def from_workload(cls, wl, device="cuda") -> "Predictor":
+        cfg, w = wl.cfg, wl.weights
+        dt = cfg.dtype
+        t = {"embed_w": to_device(w.store["embed_w"], dt, device), "embed_b": f32_to_device(w.embed_b, device),
+             "mask_tokens": f32_to_device(w.mask_tokens, device), "norm_w": f32_to_device(w.norm_w, device),
+             "norm_b": f32_to_device(w.norm_b, device), "proj_w": to_device(w.store["proj_w"], dt, device),
+             "proj_b": f32_to_device(w.proj_b, device)}
+        blocks = []
+        for b in w.blocks:
+            d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
+                 "up_w": to_device(b.store["up_w"], dt, device), "down_w": to_device(b.store["down_w"], dt, device)}
+            for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b"):
+                d[n] = f32_to_device(getattr(b, n), device)
+            blocks.append(d)
+        return cls(cls.hparams_of(cfg), t, blocks)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().vitenc_predictor_destroy(self.handle)
+            self.handle = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, B, n_ctx, n_tgt) -> int:
+        n = c_size()
+        check(lib().vitenc_predict_workspace_size(self.handle, B, n_ctx, n_tgt, ctypes.byref(n)))
+        return n.value
+
+    def alloc(self, B, n_ctx, n_tgt, device="cuda"):
+        import torch
+        ws = torch.empty(self.workspace_bytes(B, n_ctx, n_tgt), dtype=torch.uint8, device=device)
+        out = torch.empty((B, n_tgt, self.hp["enc_dim"]), dtype=torch.float32, device=device)
+        return ws, out
+
+    def predict_into(self, enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index=1, stream=None, check_ids=True):
+        """enc_tokens fp32 [B, n_enc, enc_dim], ctx_ids / tgt_ids int32 [B, n]
+        on the device.  check_ids copies the ids to the host (a
+        synchronisation) to check their contract before the call."""
+        B, n_enc, _ = enc_tokens.shape
+        if check_ids:
+            check_pred_ids(ctx_ids, tgt_ids, n_enc)
+        check(lib().vitenc_predict(self.handle, enc_tokens.data_ptr(), B, n_enc, ctx_ids.data_ptr(),
+                                   ctx_ids.shape[1], tgt_ids.data_ptr(), tgt_ids.shape[1], mask_index,
+                                   ws.data_ptr(), ws.numel(), out.data_ptr(), _stream(stream)))
+
+    def predict(self, enc_tokens, ctx_ids, tgt_ids, mask_index=1, stream=None):
+        B = enc_tokens.shape[0]
+        ws, out = self.alloc(B, ctx_ids.shape[1], tgt_ids.shape[1], device=enc_tokens.device)
+        self.predict_into(enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index, stream)
+        return out
 
 
 # ---------------------------------------------------------------------------
