@@ -1,7 +1,8 @@
 """Throughput of the ViT encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu-baseline]
-    python bench.py --write-counters FETCH.csv WRITE.csv OUT.txt
+                    [--part all|encoder|predictor]
+    python bench.py --write-counters KERNEL FETCH.csv WRITE.csv OUT.txt
 
 
 A step is one vitenc_encode call over one batch: the V-JEPA-2-style ViT-L
@@ -10,6 +11,10 @@ layers, bf16 with fp32 accumulation, synthetic seeded inputs resident in HBM.
 Prints one JSON line.  The roofline object is measured for the dominant
 kernel by timing its step entry point (the same kernel and launch
 configuration encode uses) with HIP events on the stream it is launched on.
+The line's `predictor` object times the masked-latent predictor that follows
+the encoder (one vitenc_predict call per step) the same way, with its own
+roofline and oracle baseline; `--part predictor` prints that object alone
+(the counter runs of its kernels use it).
 
 Its `traffic` figure comes from a committed counter summary (written by the
 --write-counters mode from two rocprofv3 --pmc runs of this script: one
@@ -62,6 +67,9 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--part", choices=("all", "encoder", "predictor"), default="all",
+                    help="what to time: the encoder (the headline line), the predictor (reported in the "
+                         "line's `predictor` object), or both")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files of this script "
                          "for KERNEL (a kernel-breakdown name)")
@@ -238,11 +246,7 @@ def cpu_baseline(cfg, wl, layers=None):
     """The oracle (unchanged, float64 numpy) on one clip through `layers`
     layers (default: all of them), scaled to the full depth if fewer."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = _oracle_cores()
     layers = layers or cfg.n_layer
     one = cfg.replace(batch=1)
     px = wl.pixels[:1]
@@ -261,6 +265,129 @@ def cpu_baseline(cfg, wl, layers=None):
                       f"layers + final norm, {t3 - t0:.1f} s"}
 
 
+class PredictorShape:
+    """The predictor's blocks as kernel_breakdown sees them: B items of
+    n_ctx + n_tgt tokens, full attention, 3-D RoPE on the grid, no prefix."""
+
+    def __init__(self, cfg):
+        self.name, self.batch, self.n_tokens = cfg.name, cfg.batch, cfg.n_tokens
+        self.embed_dim, self.ffn_dim, self.n_head, self.dtype = cfg.embed_dim, cfg.ffn_dim, cfg.n_head, cfg.dtype
+        self.grid, self.rope_layout, self.rope_theta, self.ln_eps = cfg.grid, cfg.rope_layout, cfg.rope_theta, cfg.ln_eps
+        self.rope, self.rope_interpolate, self.rope_ref_grid, self.n_prefix, self.attn_mode = 1, 0, 0, 0, 0
+        # the timed step ops put the tokens at the grid positions in order, which needs a full grid
+        assert cfg.n_tokens == cfg.n_grid
+
+    def visible_pairs(self):
+        return self.n_tokens * self.n_tokens
+
+
+def cpu_baseline_predictor(cfg, wl):
+    """The predictor oracle (unchanged) on the whole workload: every item
+    through every block (a few seconds of float64 work)."""
+    import oracle
+    cores = _oracle_cores()
+    t0 = time.perf_counter()
+    oracle.predictor_forward(cfg.hparams(), wl.weights, wl.enc_tokens, wl.ctx_ids, wl.tgt_ids, cfg.mask_index)
+    dt = time.perf_counter() - t0
+    return {"value": round(cfg.batch * cfg.n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"the whole workload ({cfg.batch} items x {cfg.n_tokens} tokens, "
+                                        f"{cfg.n_layer} blocks), {dt:.1f} s"}
+
+
+def _oracle_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def roofline_of(bd, workload):
+    """The roofline object of the kernel that takes the most time in one
+    forward (layernorm runs twice per block)."""
+    weight = {"layernorm": 2}
+    dom = max(bd, key=lambda k: bd[k][0] * weight.get(k, 1))
+    d_ms, d_flops, d_bytes = bd[dom]
+    if d_flops > 0:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(d_flops / (d_ms * 1e-3) / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["avg_launch_ms"] = round(d_ms, 5)
+    traffic = read_traffic(dom, workload)
+    roof["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
+    roof["traffic_unit"] = "MB per launch"
+    roof["algorithmic_bytes"] = round(d_bytes / 1e6, 2)
+    return roof
+
+
+def time_steps(step, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    return start.elapsed_time(end) / steps, t_wall * 1e3 / steps
+
+
+def bench_predictor(args, stream):
+    """One vitenc_predict call per step on the full predictor shape: 2 items x
+    (1024 context + 1024 target) tokens of the 8 x 16 x 16 grid, 12 blocks of
+    width 384, bf16; ids and encoder features resident on the device."""
+    import torch
+    from vision_transformer_amd import vitenc as V
+    from vision_transformer_amd import workloads as W
+    cfg = W.PREDICTOR
+    log(f"[bench] predictor {cfg.name}: B={cfg.batch} ctx={cfg.n_ctx} tgt={cfg.n_tgt} D={cfg.embed_dim} "
+        f"L={cfg.n_layer}")
+    wl = W.make_predictor_workload(cfg)
+    pred = V.Predictor.from_workload(wl)
+    V.check_pred_ids(wl.ctx_ids, wl.tgt_ids, cfg.n_grid)
+    enc = torch.from_numpy(wl.enc_tokens).cuda()
+    ctx = torch.from_numpy(wl.ctx_ids).cuda()
+    tgt = torch.from_numpy(wl.tgt_ids).cuda()
+    ws, out = pred.alloc(cfg.batch, cfg.n_ctx, cfg.n_tgt)
+
+    def step():
+        pred.predict_into(enc, ctx, tgt, ws, out, cfg.mask_index, stream, check_ids=False)
+
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    tflops = cfg.flops() / (ms * 1e-3) / 1e12
+    log(f"[bench] predictor {ms:.3f} ms/call, {tflops:.1f} TFLOP/s (wall {wall:.3f} ms/call)")
+
+    def busy():
+        for _ in range(8):
+            step()
+
+    bd = kernel_breakdown(PredictorShape(cfg), pred, args.kernel_reps, stream, busy)
+    log("[bench] predictor per-kernel (ms): " + ", ".join(f"{k}={v[0]:.4f}" for k, v in bd.items()))
+    res = {"workload": cfg.name, "ms_per_call": round(ms, 4),
+           "tokens_per_s": round(cfg.batch * cfg.n_tokens / ms * 1e3, 1),
+           "target_tokens_per_s": round(cfg.batch * cfg.n_tgt / ms * 1e3, 1),
+           "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "config": {"global_batch": cfg.batch, "n_ctx": cfg.n_ctx, "n_tgt": cfg.n_tgt, "grid": list(cfg.grid),
+                      "embed_dim": cfg.embed_dim, "enc_dim": cfg.enc_dim, "layers": cfg.n_layer,
+                      "heads": cfg.n_head},
+           "kernels_ms_per_layer": {k: round(v[0], 5) for k, v in bd.items()},
+           "roofline": roofline_of(bd, cfg.name), "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        log("[bench] predictor cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline_predictor(cfg, wl)
+        log(f"[bench] predictor cpu baseline {res['cpu_baseline']}")
+    pred.close()
+    return res
+
+
 def main():
     args = parse()
     if args.write_counters:
@@ -274,16 +401,18 @@ def main():
     from vision_transformer_amd import vitenc as V
     from vision_transformer_amd import workloads as W
 
+    stream = torch.cuda.current_stream()
+    if args.part == "predictor":
+        print(json.dumps({"predictor": bench_predictor(args, stream)}), flush=True)
+        return
     cfg = W.HEADLINE
     log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
     wl = W.make_workload(cfg)
     enc = V.Encoder.from_workload(wl)
     px = torch.from_numpy(wl.pixels).cuda()
     ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
-    stream = torch.cuda.current_stream()
 
     step = lambda: enc.encode_into(px, ws, out, pooled, stream)
-    graph = None
     if args.graph:
         step()
         torch.cuda.synchronize()
@@ -291,25 +420,11 @@ def main():
         with torch.cuda.graph(graph):
             enc.encode_into(px, ws, out, pooled)
         step = graph.replay
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup})")
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = start.elapsed_time(end) / args.steps
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
     tokens = cfg.batch * cfg.n_tokens
     tflops = cfg.flops() / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/step, {tokens / ms * 1e3:.0f} tokens/s, {tflops:.1f} TFLOP/s "
-        f"(wall {t_wall * 1e3 / args.steps:.3f} ms/step)")
+        f"(wall {wall:.3f} ms/step)")
 
     def busy():
         for _ in range(4):
@@ -318,28 +433,15 @@ def main():
     bd = kernel_breakdown(cfg, enc, args.kernel_reps, stream, busy)
     per_layer = {k: v[0] for k, v in bd.items()}
     log("[bench] per-kernel (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in per_layer.items()))
-    # the dominant kernel over one forward (layernorm runs twice per layer)
-    weight = {"layernorm": 2}
-    dom = max(bd, key=lambda k: bd[k][0] * weight.get(k, 1))
-    d_ms, d_flops, d_bytes = bd[dom]
-    if d_flops > 0:
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(d_flops / (d_ms * 1e-3) / 1e12, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(d_bytes / (d_ms * 1e-3) / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["avg_launch_ms"] = round(d_ms, 5)
-    traffic = read_traffic(dom, cfg.name)
-    roof["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
-    roof["traffic_unit"] = "MB per launch"
-    roof["algorithmic_bytes"] = round(d_bytes / 1e6, 2)
+    roof = roofline_of(bd, cfg.name)
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         cpu = cpu_baseline(cfg, wl)
         log(f"[bench] cpu baseline {cpu}")
+    enc.close()
+    pred = bench_predictor(args, stream) if args.part == "all" else None
 
     line = {
         "metric": "encoder tokens/sec + MFMA TFLOP/s fraction of peak (ViT-L video, bf16, 1 GPU)",
@@ -353,9 +455,9 @@ def main():
         "kernels_ms_per_layer": {k: round(v, 5) for k, v in per_layer.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "predictor": pred,
     }
     print(json.dumps(line), flush=True)
-    enc.close()
 
 
 if __name__ == "__main__":
