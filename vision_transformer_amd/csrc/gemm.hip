@@ -771,19 +771,26 @@ hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, in
 // workgroups over the 256 CUs, else 128 x 128 tiles (8 waves of 64 x 32, up
 // to two workgroups per CU), both with direct-to-LDS slabs.  fp32 and shapes that break the
 // FAST conditions use the register-staged kernel.
-enum TileCfg { TILE_REG = 0, TILE_256x256 = 1, TILE_128x128 = 2, TILE_128x128_DEEP = 3 };
+enum TileCfg { TILE_REG = 0, TILE_256x256 = 1, TILE_128x128 = 2, TILE_128x128_DEEP = 3, TILE_64x64 = 4 };
 
 #ifndef VITENC_DEEP_STAGES
 #define VITENC_DEEP_STAGES 3
+#endif
+#ifndef VITENC_SMALL_TILES
+#define VITENC_SMALL_TILES 1
 #endif
 
 // With at most one 128 x 128 tile per CU (the N = D projections of one clip)
 // occupancy cannot hide the first touch of the weights in HBM: those tiles
 // keep more slabs in flight instead.
+// When 128 x 128 tiles would leave more than half of the CUs idle (the
+// width-384 projections of the predictor), 64 x 64 tiles of 4 waves spread
+// the work instead.
 inline int pick_tile(int M, int N, bool fast, bool fp32) {
     constexpr int kCUs = 256;
     if (!fast || fp32) return TILE_REG;
     if (cdiv(M, 256) * cdiv(N, 256) >= kCUs) return TILE_256x256;
+    if (VITENC_SMALL_TILES && cdiv(M, 128) * cdiv(N, 128) < kCUs / 2) return TILE_64x64;
     if (cdiv(M, 128) * cdiv(N, 128) <= kCUs) return TILE_128x128_DEEP;
     return TILE_128x128;
 }
@@ -804,6 +811,7 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
         case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_128x128_DEEP:
             return launch_lds<T, EPI, 128, 128, 2, 4, 8, VITENC_DEEP_STAGES, 32>(A, lda, W, ldw, M, N, K, ep, s);
+        case TILE_64x64: return launch_lds<T, EPI, 64, 64, 2, 2, 8, 3, 32>(A, lda, W, ldw, M, N, K, ep, s);
         default: break;
         }
     }
