@@ -2,9 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
 benchmark's CPU-baseline leg, never by the library's compute path, with which
-it shares no code.  See oracle/encoder.py (the encoder) and oracle/predictor.py
-(the masked-latent predictor that follows it) for the step-by-step definitions
-and the citations of the passages each one follows.
+it shares no code.  See oracle/encoder.py (the encoder), oracle/predictor.py
+(the masked-latent predictor that follows it) and oracle/head.py (the
+attentive-pool head and classifier) for the step-by-step definitions and the
+citations of the passages each one follows.
 
 Parity status: every function here is pinned by a -m "not gpu" test against
 something other than itself (brute force, a library special case, a closed
@@ -14,3 +15,4 @@ this module) are parity unpinned because the pages print no values for it.
 """
 from .encoder import *  # noqa: F401,F403
 from .predictor import id_positions, predictor_forward  # noqa: F401
+from .head import attentive_pool_forward, cross_attention_pool  # noqa: F401

@@ -451,3 +451,140 @@ def make_predictor_workload(cfg: PredictorConfig, seed: Optional[int] = None) ->
     proj_b = _normal(rng, (De,), cfg.std_w)
     w = PredictorWeights(embed_w, embed_b, mask_tokens, blocks, ones, zeros, proj_w, proj_b, st)
     return PredictorWorkload(cfg, enc, ctx_ids, tgt_ids, w)
+
+
+# ---------------------------------------------------------------------------
+# attentive-pool head + classifier (jepa.cpp "GGUF schema (v1)", "Head
+# (jepa.head.*)"; SkyVision.cpp README, V-JEPA 2 backend notes, the pooler
+# and classifier heads)
+# ---------------------------------------------------------------------------
+@dataclass
+class HeadConfig:
+    """n_pool_layers self-attention blocks over the encoder's output tokens
+    (the encoder block without RoPE or mask), then one learned query attends
+    over them (LayerNorm on keys and values only, no output projection), the
+    query residual and an MLP, and a linear classifier on the pooled token."""
+    name: str
+    embed_dim: int = 1024
+    n_head: int = 16
+    ffn_dim: int = 4096
+    n_pool_layers: int = 3
+    n_classes: int = 174
+    ln_eps: float = 1e-6
+    batch: int = 2
+    n_tokens: int = 2048
+    dtype: int = DTYPE_BF16
+    std_w: float = 0.02
+    std_query: float = 0.02
+    std_qk: float = 0.02         # the cross-attention's q and k weights (sensitised variants raise it)
+    ln_random: bool = False      # draw the cross-attention's two LayerNorms instead of (1, 0)
+    seed: int = 3000
+
+    @property
+    def head_dim(self) -> int:
+        return self.embed_dim // self.n_head
+
+    def replace(self, **kw) -> "HeadConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return HeadConfig(**d)
+
+    def hparams(self) -> Dict:
+        return dict(embed_dim=self.embed_dim, n_head=self.n_head, ffn_dim=self.ffn_dim,
+                    n_pool_layers=self.n_pool_layers, n_classes=self.n_classes, ln_eps=self.ln_eps,
+                    dtype=self.dtype)
+
+    def flops(self) -> float:
+        """Blocks as GEMMs and attention; the cross-attention as the head
+        computes it (the key and value projections folded into the learned
+        query: one pass of dot products for the scores and one weighted sum of
+        the normalised tokens per head); the MLP and classifier as matrix-
+        vector products."""
+        B, N, D, F = self.batch, self.n_tokens, self.embed_dim, self.ffn_dim
+        M = B * N
+        blocks = self.n_pool_layers * (2.0 * M * D * (3 * D + D + 2 * F) + 4.0 * D * B * N * N)
+        xattn = 2.0 * D * D * 2 + 2.0 * M * D * self.n_head * 2 + 2.0 * B * D * D
+        tail = 2.0 * B * (2 * D * F + D * self.n_classes)
+        return blocks + xattn + tail
+
+
+# the attentive-pool classifier of a V-JEPA 2 ViT-L video model (3 pooler
+# blocks, 16 heads of 64, 174 classes) on the 2 x 2048 tokens of two clips
+HEAD = HeadConfig("vjepa2_attentive_pool")
+
+
+@dataclass
+class HeadWeights:
+    blocks: List[Block]
+    query: np.ndarray            # [embed_dim]
+    ln_kv_w: np.ndarray
+    ln_kv_b: np.ndarray
+    q_w: np.ndarray              # [embed_dim, embed_dim]
+    q_b: np.ndarray
+    k_w: np.ndarray
+    k_b: np.ndarray
+    v_w: np.ndarray
+    v_b: np.ndarray
+    ln2_w: np.ndarray
+    ln2_b: np.ndarray
+    up_w: np.ndarray             # [ffn_dim, embed_dim]
+    up_b: np.ndarray
+    down_w: np.ndarray           # [embed_dim, ffn_dim]
+    down_b: np.ndarray
+    cls_w: np.ndarray            # [n_classes, embed_dim]
+    cls_b: np.ndarray
+    store: Dict[str, np.ndarray] = field(default_factory=dict)
+
+
+@dataclass
+class HeadWorkload:
+    cfg: HeadConfig
+    tokens: np.ndarray           # fp32 [B, n_tokens, embed_dim]: the encoder's output features
+    weights: HeadWeights
+
+
+def make_head_workload(cfg: HeadConfig, seed: Optional[int] = None) -> HeadWorkload:
+    """Draw order: the input tokens ~N(0, 1) (the encoder's final-LayerNorm
+    output is unit-scale per token); per pooler block as the encoder's; the
+    query; the cross-attention's q, k, v weights and biases; the MLP; the
+    classifier; last, the two LayerNorms' (gamma, beta) when ln_random."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    B, N, D, F, C = cfg.batch, cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim, cfg.n_classes
+    dt = cfg.dtype
+    tokens = rng.standard_normal((B, N, D), dtype=np.float32)
+    ones = np.ones(D, np.float32)
+    zeros = np.zeros(D, np.float32)
+    blocks = []
+    for _ in range(cfg.n_pool_layers):
+        bs = {}
+        bs["qkv_w"], qkv_w = quantise(_normal(rng, (3 * D, D), cfg.std_w), dt)
+        qkv_b = _normal(rng, (3 * D,), cfg.std_w)
+        bs["out_w"], out_w = quantise(_normal(rng, (D, D), cfg.std_w), dt)
+        out_b = _normal(rng, (D,), cfg.std_w)
+        bs["up_w"], up_w = quantise(_normal(rng, (F, D), cfg.std_w), dt)
+        up_b = _normal(rng, (F,), cfg.std_w)
+        bs["down_w"], down_w = quantise(_normal(rng, (D, F), cfg.std_w), dt)
+        down_b = _normal(rng, (D,), cfg.std_w)
+        blocks.append(Block(qkv_w, qkv_b, out_w, out_b, up_w, up_b, down_w, down_b,
+                            ones, zeros, ones, zeros, None, None, bs))
+    st = {}
+    query = _normal(rng, (D,), cfg.std_query)
+    st["q_w"], q_w = quantise(_normal(rng, (D, D), cfg.std_qk), dt)
+    q_b = _normal(rng, (D,), cfg.std_w)
+    st["k_w"], k_w = quantise(_normal(rng, (D, D), cfg.std_qk), dt)
+    k_b = _normal(rng, (D,), cfg.std_w)
+    st["v_w"], v_w = quantise(_normal(rng, (D, D), cfg.std_w), dt)
+    v_b = _normal(rng, (D,), cfg.std_w)
+    st["up_w"], up_w = quantise(_normal(rng, (F, D), cfg.std_w), dt)
+    up_b = _normal(rng, (F,), cfg.std_w)
+    st["down_w"], down_w = quantise(_normal(rng, (D, F), cfg.std_w), dt)
+    down_b = _normal(rng, (D,), cfg.std_w)
+    st["cls_w"], cls_w = quantise(_normal(rng, (C, D), cfg.std_w), dt)
+    cls_b = _normal(rng, (C,), cfg.std_w)
+    ln = [ones, zeros, ones, zeros]
+    if cfg.ln_random:
+        ln = [np.float32(1) + _normal(rng, (D,), 0.2), _normal(rng, (D,), 0.2),
+              np.float32(1) + _normal(rng, (D,), 0.2), _normal(rng, (D,), 0.2)]
+    w = HeadWeights(blocks, query, ln[0], ln[1], q_w, q_b, k_w, k_b, v_w, v_b, ln[2], ln[3],
+                    up_w, up_b, down_w, down_b, cls_w, cls_b, st)
+    return HeadWorkload(cfg, tokens, w)
