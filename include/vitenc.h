@@ -212,6 +212,70 @@ vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens,
                              const int32_t *ctx_ids, int32_t n_ctx, const int32_t *tgt_ids, int32_t n_tgt,
                              int32_t mask_index, void *workspace, size_t ws_bytes, float *out, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Attentive-pool head and classifier (jepa.cpp "GGUF schema (v1)", "Head
+ * (jepa.head.*)", kind attentive_pool; SkyVision.cpp README, V-JEPA 2 backend
+ * notes, the pooler and classifier heads), on the encoder's output tokens:
+ *
+ *   x = tokens;  per pooler block (the encoder's block, no RoPE, no mask):
+ *         x += attn(ln1(x));  x += ffn(ln2(x))
+ *   kv = ln_kv(x);  q = query Wq^T + bq   (the query is not normalised)
+ *   a  = per head softmax(q_h k_h^T / sqrt(hd)) v_h, k = kv Wk^T + bk,
+ *        v = kv Wv^T + bv, heads concatenated, NO output projection
+ *   y  = query + a;  pooled = y + fc2(gelu(fc1(ln2(y))))
+ *   logits = pooled cls_w^T + cls_b          (no final norm)
+ * ------------------------------------------------------------------------- */
+
+/* embed_dim D (1..4096, a multiple of 4), n_head (D % n_head == 0; with
+ * pooler blocks the head width D/n_head must be 32 or 64), ffn_dim F of the
+ * blocks and of the head's MLP, n_pool_layers (0..1024), n_classes (0: no
+ * classifier), ln_eps, dtype as the encoder. */
+typedef struct {
+    int32_t embed_dim, n_head, ffn_dim, n_pool_layers, n_classes;
+    float ln_eps;
+    int32_t dtype;
+} vitenc_head_hparams;
+
+/* blocks: HOST array of n_pool_layers vitenc_block_weights (layer scales
+ * ignored), copied at creation.  query [D], ln_kv_w/b [D], ln2_w/b [D] fp32,
+ * 16-byte aligned; q_w, k_w, v_w [D, D], up_w [F, D], down_w [D, F],
+ * cls_w [n_classes, D] in the model dtype; biases fp32 (q_b, k_b, v_b, down_b
+ * [D], up_b [F], cls_b [n_classes]).  cls_w / cls_b are required iff
+ * n_classes > 0. */
+typedef struct {
+    const vitenc_block_weights *blocks;
+    const float *query;
+    const float *ln_kv_w, *ln_kv_b;
+    const void *q_w;      const float *q_b;
+    const void *k_w;      const float *k_b;
+    const void *v_w;      const float *v_b;
+    const float *ln2_w, *ln2_b;
+    const void *up_w;     const float *up_b;
+    const void *down_w;   const float *down_b;
+    const void *cls_w;    const float *cls_b;
+} vitenc_head_weights;
+
+typedef struct vitenc_head vitenc_head;
+
+/* Refusals: EINVAL (ranges, enum values, a misaligned fp32 vector), ENULL (a
+ * missing weight), EUNSUPPORTED (D above 4096 or not a multiple of 4; pooler
+ * blocks with a head width other than 32 or 64). */
+vitenc_status vitenc_head_create(const vitenc_head_hparams *hp, const vitenc_head_weights *w,
+                                 vitenc_head **out);
+void vitenc_head_destroy(vitenc_head *h);
+
+/* Bytes of device workspace vitenc_head_forward needs for B items of N
+ * tokens.  Refusals: ESHAPE (B or N below 1, N above 2^22, B*N above 2^30). */
+vitenc_status vitenc_head_workspace_size(const vitenc_head *h, int32_t B, int32_t N, size_t *bytes);
+
+/* tokens: fp32 [B, N, D], 16-byte aligned (the encoder's out_tokens).
+ * pooled: fp32 [B, D], required.  logits: fp32 [B, n_classes] or NULL (no
+ * classifier run).  workspace as vitenc_encode's.  Refusals: those of the
+ * workspace size, ENULL, EINVAL (misaligned tokens), EWORKSPACE. */
+vitenc_status vitenc_head_forward(const vitenc_head *h, const float *tokens, int32_t B, int32_t N,
+                                  void *workspace, size_t ws_bytes, float *pooled, float *logits,
+                                  void *stream);
+
 /* Thread-local text of the last refusal on this thread ("" if none). */
 const char *vitenc_error_text(void);
 int32_t vitenc_abi_version(void);

@@ -158,6 +158,24 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// GELU(x) = x/2 (1 + erf(x / sqrt 2)), with erf from the rational
+// approximation 7.1.26 of Abramowitz & Stegun (Handbook of Mathematical
+// Functions): erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-z^2},
+// t = 1 / (1 + p z), z >= 0, |error| <= 1.5e-7, and erf(-z) = -erf(z).
+__device__ __forceinline__ float gelu_erf(float x) {
+    const float z = fabsf(x) * 0.70710678118654752440f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    poly *= t;
+    const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+    const float erf_abs = fmaf(-poly, e, 1.0f);
+    const float erf = x < 0.0f ? -erf_abs : erf_abs;
+    return 0.5f * x * (1.0f + erf);
+}
+
 __host__ __device__ __forceinline__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 

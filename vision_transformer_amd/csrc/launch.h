@@ -92,6 +92,25 @@ hipError_t launch_gather_rows(int out_dtype, const float *src, int64_t lds, cons
 hipError_t launch_fill_rows(const float *vec, const int *rows, int R, int D, float *Z, hipStream_t s);
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
 
+// attentive-pool head: matrix-vector products for nb <= any items
+// out[b*ldo + r] = act(W[r, :C] . x_{b,r} + bias[r]) + res[b*ldr + r],
+// x_{b,r} = x + b*ldx + (r / rpg)*ldg; W in `dtype`, x, bias, res, out fp32
+hipError_t launch_gemv(int dtype, const void *W, int64_t ldw, const float *bias, const float *x, int64_t ldx, int rpg,
+                       int64_t ldg, int nb, int R, int C, bool gelu, const float *res, int64_t ldr, float *out,
+                       int64_t ldo, hipStream_t s);
+// u [H, D] = (Wk_h^T q_h) / sqrt(hd), ub [H] = (q_h . bk_h) / sqrt(hd)
+hipError_t launch_xattn_fold(int dtype, const void *Wk, const float *bk, const float *q, int D, int H, float *u,
+                             float *ub, hipStream_t s);
+// s [B, H, N] = u_h . LN(z_j) + ub[h]; stats [B*N] = (mean, rstd) of each row; D % 4 == 0, D <= 4096
+hipError_t launch_xattn_scores(const float *Z, int B, int N, int D, const float *ln_w, const float *ln_b, float eps,
+                               const float *u, const float *ub, int H, float *s, float2 *stats, hipStream_t st);
+// s -> p * rstd in place (softmax over each (item, head) row)
+hipError_t launch_xattn_softmax(float *s, const float2 *stats, int B, int N, int H, hipStream_t st);
+// ybar [B, H, D] = sum_j p_j LN(z_j) per head, through partials P [B, xattn_chunks(N), H, D]
+int xattn_chunks(int N);
+hipError_t launch_xattn_pool(const float *Z, const float2 *stats, const float *w, int B, int N, int D, int H,
+                             const float *ln_w, const float *ln_b, float *P, float *ybar, hipStream_t st);
+
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N,
                             int H, int head_dim, int ldv, int attn_mode, int n_prefix,
                             int tokens_per_frame, void *O, hipStream_t s);

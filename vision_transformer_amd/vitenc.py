@@ -63,6 +63,19 @@ class PredWeights(ctypes.Structure):
                 ("proj_w", c_vp), ("proj_b", c_vp)]
 
 
+class HeadHparams(ctypes.Structure):
+    _fields_ = [(n, c_i32) for n in ("embed_dim", "n_head", "ffn_dim", "n_pool_layers", "n_classes")] + \
+               [("ln_eps", c_f32), ("dtype", c_i32)]
+
+
+HEAD_FIELDS = ("query", "ln_kv_w", "ln_kv_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b", "ln2_w", "ln2_b",
+               "up_w", "up_b", "down_w", "down_b", "cls_w", "cls_b")
+
+
+class HeadWeights(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.POINTER(BlockWeights))] + [(n, c_vp) for n in HEAD_FIELDS]
+
+
 _LIB = None
 
 # exported symbol -> (restype, argtypes)
@@ -88,6 +101,10 @@ SIGNATURES = {
     "vitenc_predict_workspace_size": (c_i32, [c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
     "vitenc_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_size, c_vp,
                                c_vp]),
+    "vitenc_head_create": (c_i32, [ctypes.POINTER(HeadHparams), ctypes.POINTER(HeadWeights), ctypes.POINTER(c_vp)]),
+    "vitenc_head_destroy": (None, [c_vp]),
+    "vitenc_head_workspace_size": (c_i32, [c_vp, c_i32, c_i32, ctypes.POINTER(c_size)]),
+    "vitenc_head_forward": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_size, c_vp, c_vp, c_vp]),
 }
 
 
@@ -337,6 +354,80 @@ class Predictor:
         ws, out = self.alloc(B, ctx_ids.shape[1], tgt_ids.shape[1], device=enc_tokens.device)
         self.predict_into(enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index, stream)
         return out
+
+
+class Head:
+    """An attentive-pool head (+ classifier) handle over device-resident
+    weights."""
+
+    def __init__(self, hp: Dict, tensors: Dict, blocks):
+        self.hp = dict(hp)
+        self.tensors = tensors
+        self.blocks = blocks
+        L = lib()
+        self._hp = HeadHparams()
+        for name, _ in HeadHparams._fields_:
+            setattr(self._hp, name, self.hp.get(name, 0))
+        self._bw = (BlockWeights * max(1, len(blocks)))()
+        for i, b in enumerate(blocks):
+            for n in BLOCK_FIELDS:
+                setattr(self._bw[i], n, _ptr(b.get(n)))
+        self._w = HeadWeights(ctypes.cast(self._bw, ctypes.POINTER(BlockWeights)),
+                              *[_ptr(tensors.get(n)) for n in HEAD_FIELDS])
+        h = c_vp()
+        check(L.vitenc_head_create(ctypes.byref(self._hp), ctypes.byref(self._w), ctypes.byref(h)))
+        self.handle = h
+
+    @classmethod
+    def from_workload(cls, wl, device="cuda") -> "Head":
+        cfg, w = wl.cfg, wl.weights
+        dt = cfg.dtype
+        t = {n: f32_to_device(getattr(w, n), device) for n in ("query", "ln_kv_w", "ln_kv_b", "q_b", "k_b", "v_b",
+                                                                 "ln2_w", "ln2_b", "up_b", "down_b", "cls_b")}
+        for n in ("q_w", "k_w", "v_w", "up_w", "down_w", "cls_w"):
+            t[n] = to_device(w.store[n], dt, device)
+        blocks = []
+        for b in w.blocks:
+            d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
+                 "up_w": to_device(b.store["up_w"], dt, device), "down_w": to_device(b.store["down_w"], dt, device)}
+            for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b"):
+                d[n] = f32_to_device(getattr(b, n), device)
+            blocks.append(d)
+        return cls(cfg.hparams(), t, blocks)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            lib().vitenc_head_destroy(self.handle)
+            self.handle = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, B, N) -> int:
+        n = c_size()
+        check(lib().vitenc_head_workspace_size(self.handle, B, N, ctypes.byref(n)))
+        return n.value
+
+    def alloc(self, B, N, device="cuda"):
+        import torch
+        ws = torch.empty(self.workspace_bytes(B, N), dtype=torch.uint8, device=device)
+        pooled = torch.empty((B, self.hp["embed_dim"]), dtype=torch.float32, device=device)
+        logits = torch.empty((B, max(1, self.hp["n_classes"])), dtype=torch.float32, device=device)
+        return ws, pooled, logits
+
+    def forward_into(self, tokens, ws, pooled, logits=None, stream=None):
+        B, N, _ = tokens.shape
+        check(lib().vitenc_head_forward(self.handle, tokens.data_ptr(), B, N, ws.data_ptr(), ws.numel(),
+                                        pooled.data_ptr(), _ptr(logits), _stream(stream)))
+
+    def forward(self, tokens, stream=None):
+        B, N, _ = tokens.shape
+        ws, pooled, logits = self.alloc(B, N, device=tokens.device)
+        self.forward_into(tokens, ws, pooled, logits if self.hp["n_classes"] > 0 else None, stream)
+        return pooled, logits[:, :self.hp["n_classes"]]
 
 
 # ---------------------------------------------------------------------------
