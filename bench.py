@@ -1,7 +1,7 @@
 """Throughput of the ViT encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu-baseline]
-                    [--part all|encoder|predictor]
+                    [--part all|encoder|predictor|head]
     python bench.py --write-counters KERNEL FETCH.csv WRITE.csv OUT.txt
 
 
@@ -13,8 +13,10 @@ kernel by timing its step entry point (the same kernel and launch
 configuration encode uses) with HIP events on the stream it is launched on.
 The line's `predictor` object times the masked-latent predictor that follows
 the encoder (one vitenc_predict call per step) the same way, with its own
-roofline and oracle baseline; `--part predictor` prints that object alone
-(the counter runs of its kernels use it).
+roofline and oracle baseline; `head` does the same for the attentive-pool
+classifier head (one vitenc_head_forward call per step).  `--part predictor`
+or `--part head` prints that object alone (the counter runs of their kernels
+use it).
 
 Its `traffic` figure comes from a committed counter summary (written by the
 --write-counters mode from two rocprofv3 --pmc runs of this script: one
@@ -67,9 +69,9 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--part", choices=("all", "encoder", "predictor"), default="all",
-                    help="what to time: the encoder (the headline line), the predictor (reported in the "
-                         "line's `predictor` object), or both")
+    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head"), default="all",
+                    help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
+                         "head (reported in the line's `predictor` / `head` objects), or all three")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files of this script "
                          "for KERNEL (a kernel-breakdown name)")
@@ -388,6 +390,99 @@ def bench_predictor(args, stream):
     return res
 
 
+class HeadShape:
+    """The attentive-pool head's pooler blocks as kernel_breakdown sees them:
+    B items of N tokens, full attention, no RoPE, no prefix."""
+
+    def __init__(self, cfg):
+        self.name, self.batch, self.n_tokens = cfg.name, cfg.batch, cfg.n_tokens
+        self.embed_dim, self.ffn_dim, self.n_head, self.dtype = cfg.embed_dim, cfg.ffn_dim, cfg.n_head, cfg.dtype
+        self.ln_eps = cfg.ln_eps
+        self.grid, self.rope_layout, self.rope_theta = (1, 1, 1), 0, 10000.0
+        self.rope, self.rope_interpolate, self.rope_ref_grid, self.n_prefix, self.attn_mode = 0, 0, 0, 0, 0
+
+    def visible_pairs(self):
+        return self.n_tokens * self.n_tokens
+
+
+def head_xattn_bytes(cfg):
+    """Algorithmic HBM bytes of the cross-attention and the tail: the tokens
+    read twice (scores, then weighted sums), the q, k, v, fc1, fc2 and
+    classifier weights once, the pooled and logit outputs."""
+    B, N, D, F, C = cfg.batch, cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim, cfg.n_classes
+    es = 4 if cfg.dtype == 0 else 2
+    return 2 * B * N * D * 4 + (3 * D * D + 2 * D * F + C * D) * es + B * (D + C) * 4
+
+
+def cpu_baseline_head(cfg, wl):
+    """The head oracle (unchanged) on the whole workload."""
+    import oracle
+    cores = _oracle_cores()
+    t0 = time.perf_counter()
+    oracle.attentive_pool_forward(cfg.hparams(), wl.weights, wl.tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(cfg.batch * cfg.n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "sample": f"the whole workload ({cfg.batch} items x {cfg.n_tokens} tokens, "
+                                        f"{cfg.n_pool_layers} pooler blocks + cross-attention + classifier), "
+                                        f"{dt:.1f} s"}
+
+
+def bench_head(args, stream):
+    """One vitenc_head_forward call per step on the V-JEPA 2 ViT-L classifier
+    head over the 2 x 2048 output tokens of two clips (3 pooler blocks, 174
+    classes, bf16).  The cross-attention and tail are also timed alone (a
+    second handle without pooler blocks over the same weights)."""
+    import torch
+    from vision_transformer_amd import vitenc as V
+    from vision_transformer_amd import workloads as W
+    cfg = W.HEAD
+    log(f"[bench] head {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_pool_layers} "
+        f"classes={cfg.n_classes}")
+    wl = W.make_head_workload(cfg)
+    head = V.Head.from_workload(wl)
+    bare = V.Head(dict(head.hp, n_pool_layers=0), head.tensors, [])
+    tok = torch.from_numpy(wl.tokens).cuda()
+    ws, pooled, logits = head.alloc(cfg.batch, cfg.n_tokens)
+    ws0, pooled0, logits0 = bare.alloc(cfg.batch, cfg.n_tokens)
+
+    def step():
+        head.forward_into(tok, ws, pooled, logits, stream)
+
+    def step_bare():
+        bare.forward_into(tok, ws0, pooled0, logits0, stream)
+
+    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    ms_x, _ = time_steps(step_bare, args.steps, args.warmup, stream)
+    tflops = cfg.flops() / (ms * 1e-3) / 1e12
+    log(f"[bench] head {ms:.3f} ms/call ({ms_x * 1e3:.1f} us without pooler blocks), {tflops:.1f} TFLOP/s")
+
+    def busy():
+        for _ in range(4):
+            step()
+
+    bd = kernel_breakdown(HeadShape(cfg), head, args.kernel_reps, stream, busy)
+    log("[bench] head per-kernel (ms): " + ", ".join(f"{k}={v[0]:.4f}" for k, v in bd.items()))
+    xb = head_xattn_bytes(cfg)
+    xroof = {"part": "cross-attention + MLP + classifier", "bound": "hbm",
+             "achieved": round(xb / (ms_x * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "algorithmic_bytes": round(xb / 1e6, 2), "ms": round(ms_x, 5)}
+    xroof["frac"] = round(xroof["achieved"] / PEAK_HBM_GBS, 4)
+    res = {"workload": cfg.name, "ms_per_call": round(ms, 4),
+           "tokens_per_s": round(cfg.batch * cfg.n_tokens / ms * 1e3, 1),
+           "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "config": {"global_batch": cfg.batch, "tokens_per_item": cfg.n_tokens, "embed_dim": cfg.embed_dim,
+                      "pool_layers": cfg.n_pool_layers, "heads": cfg.n_head, "classes": cfg.n_classes},
+           "kernels_ms_per_layer": {k: round(v[0], 5) for k, v in bd.items()},
+           "roofline": roofline_of(bd, cfg.name), "xattn_roofline": xroof, "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        log("[bench] head cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline_head(cfg, wl)
+        log(f"[bench] head cpu baseline {res['cpu_baseline']}")
+    bare.close()
+    head.close()
+    return res
+
+
 def main():
     args = parse()
     if args.write_counters:
@@ -404,6 +499,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.part == "predictor":
         print(json.dumps({"predictor": bench_predictor(args, stream)}), flush=True)
+        return
+    if args.part == "head":
+        print(json.dumps({"head": bench_head(args, stream)}), flush=True)
         return
     cfg = W.HEADLINE
     log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
@@ -442,6 +540,7 @@ def main():
         log(f"[bench] cpu baseline {cpu}")
     enc.close()
     pred = bench_predictor(args, stream) if args.part == "all" else None
+    head = bench_head(args, stream) if args.part == "all" else None
 
     line = {
         "metric": "encoder tokens/sec + MFMA TFLOP/s fraction of peak (ViT-L video, bf16, 1 GPU)",
@@ -456,6 +555,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "predictor": pred,
+        "head": head,
     }
     print(json.dumps(line), flush=True)
 

@@ -26,7 +26,32 @@ namespace {
 
 constexpr int kGemvBatch = 8;    // items per matrix-vector launch
 constexpr int kWsumHeads = 16;   // heads per weighted-sum pass (accumulators per lane: 4 per head)
-constexpr int kWsumRows = 32;    // tokens per weighted-sum chunk
+constexpr int kWsumRows = 256;   // tokens per weighted-sum workgroup
+constexpr int kWsumGroups = 16;  // row groups of a weighted-sum workgroup (16 threads of 4 columns each)
+
+// Sum of 64 values over the 64 lanes of a wave for 64 outputs at once: on
+// entry every lane holds a partial of each output v[0..64); on exit lane l
+// returns the total of output l.  Each butterfly step halves the outputs a
+// lane keeps (the half selected by the lane's bit), so 63 shuffles serve all
+// 64 outputs instead of 6 per output.  (One template level per step keeps
+// every index a compile-time constant, so v stays in registers.)
+template <int M>
+__device__ __forceinline__ void butterfly_step(float (&v)[64], int lane) {
+    const bool up = (lane & M) != 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const float send = up ? v[i] : v[i + M];
+        const float keep = up ? v[i + M] : v[i];
+        v[i] = keep + __shfl_xor(send, M, 64);
+    }
+    if constexpr (M > 1) butterfly_step<M / 2>(v, lane);
+}
+__device__ __forceinline__ float transpose_reduce64(float (&v)[64], int lane) {
+    butterfly_step<32>(v, lane);
+    return v[0];
+}
+
+constexpr int pow2_floor(int x) { return x >= 16 ? 16 : x >= 8 ? 8 : x >= 4 ? 4 : x >= 2 ? 2 : 1; }
 
 template <typename T> __device__ __forceinline__ void unpack(const Chunk &c, float *v);
 template <> __device__ __forceinline__ void unpack<float>(const Chunk &c, float *v) {
@@ -66,11 +91,25 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, int6
     float acc[kGemvBatch];
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) acc[b] = 0.0f;
-    for (int c = lane * E; c < C; c += 64 * E) {
+    // four weight chunks in flight per lane before they are used
+    constexpr int U = 4;
+    for (int c0 = lane * E; c0 < C; c0 += U * 64 * E) {
+        Chunk wc[U];
+        if (VEC) {
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int c = c0 + k * 64 * E;
+                wc[k] = c + E <= C ? load_chunk(w + c) : zero_chunk();
+            }
+        }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+        const int c = c0 + k * 64 * E;
+        if (c >= C) break;
         float wv[E];
         const bool full = c + E <= C;
         if (VEC && full) {
-            unpack<T>(load_chunk(w + c), wv);
+            unpack<T>(wc[k], wv);
         } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) wv[e] = c + e < C ? to_f32(w[c + e]) : 0.0f;
@@ -94,6 +133,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, int6
                     if (c + e < C) acc[b] = fmaf(wv[e], xb[e], acc[b]);
             }
         }
+    }
     }
 #pragma unroll
     for (int b = 0; b < kGemvBatch; ++b) {
@@ -121,6 +161,7 @@ __global__ __launch_bounds__(256) void fold_kernel(const T *__restrict__ Wk, int
     const int c = blockIdx.x * 64 + lane;
     float acc = 0.0f;
     if (c < D)
+#pragma unroll 8
         for (int i = g; i < hd; i += 4) acc = fmaf(to_f32(Wk[(int64_t)(h * hd + i) * ldw + c]), q[h * hd + i], acc);
     red[g][lane] = acc;
     __syncthreads();
@@ -133,76 +174,125 @@ __global__ __launch_bounds__(256) void fold_kernel(const T *__restrict__ Wk, int
     }
 }
 
-// First pass, one wave per token row: the key/value LayerNorm in registers
-// (fp32, centred two-pass), then the scores of the workgroup's heads
+// First pass: per token row the key/value LayerNorm in registers (fp32,
+// centred two-pass), then the scores of the workgroup's heads
 // s[(b*H + h)*N + j] = u_h . y_j + ub[h] with u in LDS; head group 0 also
-// stores the row's (mean, rstd).  NE float4s per lane cover D <= 256*NE.
-template <int NE>
+// stores the row's (mean, rstd).  A wave takes RB = 64/HP rows at a time,
+// keeps one partial per (row, head) in each lane, and reduces all 64 of them
+// over the wave in one transposed butterfly.  NE float4s per lane cover
+// D <= 256*NE; HP is a power of two covering the HG heads of a group.
+template <int NE, int HP>
 __global__ __launch_bounds__(256) void xattn_scores_kernel(const float *__restrict__ Z, int M, int N, int D,
                                                            const float *__restrict__ ln_w,
                                                            const float *__restrict__ ln_b, float eps,
                                                            const float *__restrict__ u, const float *__restrict__ ub,
-                                                           int H, int HG, int rows_per_wg, float *__restrict__ s,
+                                                           int H, int HG, float *__restrict__ s,
                                                            float2 *__restrict__ stats) {
+    constexpr int RB = 64 / HP;
     extern __shared__ float su[]; // [HG][D]
     const int h0 = blockIdx.y * HG, nh = min(HG, H - h0);
-    for (int i = threadIdx.x; i < nh * D; i += blockDim.x) su[i] = u[(int64_t)h0 * D + i];
+    {
+        // eight 16-byte loads in flight per thread before their LDS stores
+        const float4 *u4 = reinterpret_cast<const float4 *>(u + (int64_t)h0 * D);
+        float4 *s4 = reinterpret_cast<float4 *>(su);
+        const int n4 = nh * D / 4;
+        for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * 256) {
+            float4 a[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int i = i0 + k * 256;
+                a[k] = i < n4 ? u4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (i0 + k * 256 < n4) s4[i0 + k * 256] = a[k];
+        }
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int D4 = D / 4;
     const float4 *g4 = reinterpret_cast<const float4 *>(ln_w), *b4 = reinterpret_cast<const float4 *>(ln_b);
-    for (int rr = wave; rr < rows_per_wg; rr += 4) {
-        const int row = blockIdx.x * rows_per_wg + rr;
-        if (row >= M) break;
-        const float4 *z = reinterpret_cast<const float4 *>(Z + (int64_t)row * D);
-        float4 v[NE];
-        float sum = 0.0f;
+    const int row0 = (blockIdx.x * 4 + wave) * RB;
+    float part[64];
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int c4 = lane + 64 * i;
-            v[i] = c4 < D4 ? z[c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-        }
-        const float mean = wave_sum(sum) / (float)D;
-        float sq = 0.0f;
+    for (int i = 0; i < 64; ++i) part[i] = 0.0f;
+    // PF rows at a time: their loads all in flight, each normalised in
+    // registers, then every u fragment read from LDS serves all PF rows
+    constexpr int PF = pow2_floor(RB < 16 / NE ? RB : (16 / NE > 0 ? 16 / NE : 1)); // divides RB
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            if (lane + 64 * i < D4) {
-                const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
-                sq += (a * a + b * b) + (c * c + d * d);
+    for (int g0 = 0; g0 < RB; g0 += PF) {
+        float4 y[PF][NE];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int row = row0 + g0 + k;
+            const float4 *z = reinterpret_cast<const float4 *>(Z + (int64_t)min(row, M - 1) * D);
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                const int c4 = lane + 64 * i;
+                y[k][i] = c4 < D4 ? z[c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
         }
-        const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + eps);
 #pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int c4 = lane + 64 * i;
-            if (c4 < D4) {
-                const float4 gw = g4[c4], gb = b4[c4];
-                v[i] = make_float4((v[i].x - mean) * rstd * gw.x + gb.x, (v[i].y - mean) * rstd * gw.y + gb.y,
-                                   (v[i].z - mean) * rstd * gw.z + gb.z, (v[i].w - mean) * rstd * gw.w + gb.w);
-            } else {
-                v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int k = 0; k < PF; ++k) {
+            const int row = row0 + g0 + k;
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NE; ++i) sum += (y[k][i].x + y[k][i].y) + (y[k][i].z + y[k][i].w);
+            const float mean = wave_sum(sum) / (float)D;
+            float sq = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                if (lane + 64 * i < D4) {
+                    const float a = y[k][i].x - mean, b = y[k][i].y - mean, c = y[k][i].z - mean,
+                                d = y[k][i].w - mean;
+                    sq += (a * a + b * b) + (c * c + d * d);
+                }
             }
-        }
-        const int b = row / N, j = row - b * N;
-        for (int h = 0; h < nh; ++h) {
-            const float4 *uh = reinterpret_cast<const float4 *>(su + h * D);
-            float d = 0.0f;
+            const float rstd = 1.0f / sqrtf(wave_sum(sq) / (float)D + eps);
 #pragma unroll
             for (int i = 0; i < NE; ++i) {
                 const int c4 = lane + 64 * i;
                 if (c4 < D4) {
-                    const float4 w4 = uh[c4];
-                    d = fmaf(w4.x, v[i].x, d);
-                    d = fmaf(w4.y, v[i].y, d);
-                    d = fmaf(w4.z, v[i].z, d);
-                    d = fmaf(w4.w, v[i].w, d);
+                    const float4 gw = g4[c4], gb = b4[c4];
+                    y[k][i] = make_float4((y[k][i].x - mean) * rstd * gw.x + gb.x,
+                                          (y[k][i].y - mean) * rstd * gw.y + gb.y,
+                                          (y[k][i].z - mean) * rstd * gw.z + gb.z,
+                                          (y[k][i].w - mean) * rstd * gw.w + gb.w);
                 }
             }
-            d = wave_sum(d);
-            if (lane == 0) s[((int64_t)b * H + h0 + h) * N + j] = d + ub[h0 + h];
+            if (blockIdx.y == 0 && lane == 0 && row < M) stats[row] = make_float2(mean, rstd);
         }
-        if (blockIdx.y == 0 && lane == 0) stats[row] = make_float2(mean, rstd);
+#pragma unroll
+        for (int h = 0; h < HP; ++h) {
+            if (h < nh) {
+                const float4 *uh = reinterpret_cast<const float4 *>(su + h * D);
+                float d[PF];
+#pragma unroll
+                for (int k = 0; k < PF; ++k) d[k] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < NE; ++i) {
+                    const int c4 = lane + 64 * i;
+                    if (c4 < D4) {
+                        const float4 w4 = uh[c4];
+#pragma unroll
+                        for (int k = 0; k < PF; ++k) {
+                            d[k] = fmaf(w4.x, y[k][i].x, d[k]);
+                            d[k] = fmaf(w4.y, y[k][i].y, d[k]);
+                            d[k] = fmaf(w4.z, y[k][i].z, d[k]);
+                            d[k] = fmaf(w4.w, y[k][i].w, d[k]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < PF; ++k) part[(g0 + k) * HP + h] = d[k];
+            }
+        }
+    }
+    const float tot = transpose_reduce64(part, lane);
+    const int r = lane / HP, h = lane - r * HP, row = row0 + r;
+    if (row < M && h < nh) {
+        const int b = row / N, j = row - b * N;
+        s[((int64_t)b * H + h0 + h) * N + j] = tot + ub[h0 + h];
     }
 }
 
@@ -215,6 +305,7 @@ __global__ __launch_bounds__(256) void xattn_softmax_kernel(float *__restrict__ 
     float *row = s + (int64_t)bh * N;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float m = -INFINITY;
+#pragma unroll 8
     for (int j = threadIdx.x; j < N; j += 256) m = fmaxf(m, row[j]);
     m = wave_max(m);
     if (lane == 0) red[wave] = m;
@@ -222,23 +313,27 @@ __global__ __launch_bounds__(256) void xattn_softmax_kernel(float *__restrict__ 
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     float t = 0.0f;
+#pragma unroll 8
     for (int j = threadIdx.x; j < N; j += 256) t += expf(row[j] - m);
     t = wave_sum(t);
     if (lane == 0) red[wave] = t;
     __syncthreads();
     const float inv = 1.0f / (((red[0] + red[1]) + red[2]) + red[3]);
+#pragma unroll 8
     for (int j = threadIdx.x; j < N; j += 256) row[j] = expf(row[j] - m) * inv * stats[(int64_t)b * N + j].y;
 }
 
 // Second pass: P[((b*NC + ch)*H + h)*D + c] = sum over the chunk's tokens j
 // of w[(b*H + h)*N + j] * (Z[b*N + j, c] - mean_j), for up to kWsumHeads
-// heads per workgroup; one float4 column per thread, 1024 columns per
-// workgroup.
+// heads.  A workgroup takes 64 columns (16 float4 columns) of kWsumRows
+// tokens: 16 row groups stride over the tokens, and their partials are summed
+// in LDS in a fixed order.
 __global__ __launch_bounds__(256) void xattn_wsum_kernel(const float *__restrict__ Z, const float2 *__restrict__ stats,
                                                          const float *__restrict__ w, int N, int D, int H, int NC,
                                                          int n_hg, float *__restrict__ P) {
     __shared__ float sw[kWsumHeads][kWsumRows];
     __shared__ float smu[kWsumRows];
+    __shared__ float4 red[kWsumGroups][kWsumHeads][16];
     const int b = blockIdx.z / n_hg, h0 = (blockIdx.z % n_hg) * kWsumHeads;
     const int nh = min(kWsumHeads, H - h0);
     const int ch = blockIdx.y, j0 = ch * kWsumRows, nj = min(kWsumRows, N - j0);
@@ -246,30 +341,55 @@ __global__ __launch_bounds__(256) void xattn_wsum_kernel(const float *__restrict
         const int h = t / kWsumRows, jj = t - h * kWsumRows;
         sw[h][jj] = (h < nh && jj < nj) ? w[((int64_t)b * H + h0 + h) * N + j0 + jj] : 0.0f;
     }
-    if (threadIdx.x < kWsumRows) smu[threadIdx.x] = threadIdx.x < nj ? stats[(int64_t)b * N + j0 + threadIdx.x].x : 0.0f;
+    for (int t = threadIdx.x; t < kWsumRows; t += 256) smu[t] = t < nj ? stats[(int64_t)b * N + j0 + t].x : 0.0f;
     __syncthreads();
-    const int c4 = blockIdx.x * 256 + threadIdx.x;
-    if (c4 >= D / 4) return;
+    const int D4 = D / 4;
+    const int cq = threadIdx.x & 15, rg = threadIdx.x >> 4;
+    const int c4 = blockIdx.x * 16 + cq;
     float4 acc[kWsumHeads];
 #pragma unroll
     for (int h = 0; h < kWsumHeads; ++h) acc[h] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const float4 *z = reinterpret_cast<const float4 *>(Z + ((int64_t)b * N + j0) * D) + c4;
-    for (int jj = 0; jj < nj; ++jj) {
-        float4 d = z[(int64_t)jj * (D / 4)];
-        const float mu = smu[jj];
-        d.x -= mu; d.y -= mu; d.z -= mu; d.w -= mu;
+    if (c4 < D4) {
+        const float4 *z = reinterpret_cast<const float4 *>(Z + ((int64_t)b * N + j0) * D) + c4;
+        // eight rows' loads in flight per thread, then their updates
+        constexpr int U = 8;
+        for (int j0r = rg; j0r < nj; j0r += U * kWsumGroups) {
+            float4 d[U];
 #pragma unroll
-        for (int h = 0; h < kWsumHeads; ++h) {
-            const float p = sw[h][jj];
-            acc[h].x = fmaf(p, d.x, acc[h].x);
-            acc[h].y = fmaf(p, d.y, acc[h].y);
-            acc[h].z = fmaf(p, d.z, acc[h].z);
-            acc[h].w = fmaf(p, d.w, acc[h].w);
+            for (int k = 0; k < U; ++k) {
+                const int jj = j0r + k * kWsumGroups;
+                d[k] = jj < nj ? z[(int64_t)jj * D4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                const int jj = j0r + k * kWsumGroups;
+                if (jj < nj) {
+                    const float mu = smu[jj];
+                    d[k].x -= mu; d[k].y -= mu; d[k].z -= mu; d[k].w -= mu;
+#pragma unroll
+                    for (int h = 0; h < kWsumHeads; ++h) {
+                        const float p = sw[h][jj];
+                        acc[h].x = fmaf(p, d[k].x, acc[h].x);
+                        acc[h].y = fmaf(p, d[k].y, acc[h].y);
+                        acc[h].z = fmaf(p, d[k].z, acc[h].z);
+                        acc[h].w = fmaf(p, d[k].w, acc[h].w);
+                    }
+                }
+            }
         }
     }
 #pragma unroll
-    for (int h = 0; h < kWsumHeads; ++h)
-        if (h < nh) reinterpret_cast<float4 *>(P + (((int64_t)b * NC + ch) * H + h0 + h) * D)[c4] = acc[h];
+    for (int h = 0; h < kWsumHeads; ++h) red[rg][h][cq] = acc[h];
+    __syncthreads();
+    const int h = threadIdx.x >> 4, q = threadIdx.x & 15;
+    float4 t = red[0][h][q];
+#pragma unroll
+    for (int g = 1; g < kWsumGroups; ++g) {
+        const float4 x = red[g][h][q];
+        t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+    }
+    const int c4o = blockIdx.x * 16 + q;
+    if (h < nh && c4o < D4) reinterpret_cast<float4 *>(P + (((int64_t)b * NC + ch) * H + h0 + h) * D)[c4o] = t;
 }
 
 // ybar[(b*H + h)*D + c] = gamma_c * sum_ch P[((b*NC + ch)*H + h)*D + c] + beta_c
@@ -316,11 +436,18 @@ hipError_t gemv_t(const void *W, int64_t ldw, const float *bias, const float *x,
 template <int NE>
 hipError_t scores_t(const float *Z, int M, int N, int D, const float *ln_w, const float *ln_b, float eps,
                     const float *u, const float *ub, int H, float *s, float2 *stats, hipStream_t st) {
-    const int HG = std::max(1, std::min(H, 16384 / D)); // u of HG heads: at most 64 KB of LDS
-    constexpr int kRows = 16;
-    const dim3 grid((unsigned)cdiv(M, kRows), (unsigned)cdiv(H, HG));
-    hipLaunchKernelGGL((xattn_scores_kernel<NE>), grid, dim3(256), (size_t)HG * D * sizeof(float), st, Z, M, N, D,
-                       ln_w, ln_b, eps, u, ub, H, HG, kRows, s, stats);
+    // u of HG heads (at most 16 and 64 KB of LDS) per workgroup
+    const int HG = std::max(1, std::min(std::min(H, 16), 16384 / D));
+    const dim3 block(256);
+    if (HG <= 4) {
+        const dim3 grid((unsigned)cdiv(M, 4 * 16), (unsigned)cdiv(H, HG));
+        hipLaunchKernelGGL((xattn_scores_kernel<NE, 4>), grid, block, (size_t)HG * D * sizeof(float), st, Z, M, N, D,
+                           ln_w, ln_b, eps, u, ub, H, HG, s, stats);
+    } else {
+        const dim3 grid((unsigned)cdiv(M, 4 * 4), (unsigned)cdiv(H, HG));
+        hipLaunchKernelGGL((xattn_scores_kernel<NE, 16>), grid, block, (size_t)HG * D * sizeof(float), st, Z, M, N,
+                           D, ln_w, ln_b, eps, u, ub, H, HG, s, stats);
+    }
     return hipGetLastError();
 }
 
@@ -387,7 +514,7 @@ int xattn_chunks(int N) { return (int)cdiv(N, kWsumRows); }
 hipError_t launch_xattn_pool(const float *Z, const float2 *stats, const float *w, int B, int N, int D, int H,
                              const float *ln_w, const float *ln_b, float *P, float *ybar, hipStream_t st) {
     const int NC = xattn_chunks(N), n_hg = (int)cdiv(H, kWsumHeads);
-    const dim3 grid((unsigned)cdiv(D / 4, 256), (unsigned)NC, (unsigned)(B * n_hg));
+    const dim3 grid((unsigned)cdiv(D / 4, 16), (unsigned)NC, (unsigned)(B * n_hg));
     hipLaunchKernelGGL(xattn_wsum_kernel, grid, dim3(256), 0, st, Z, stats, w, N, D, H, NC, n_hg, P);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
