@@ -233,6 +233,67 @@ def _hp(hp, key, default=None):
     return getattr(hp, key, default)
 
 
+def cubic_weights(t: float, a: float = -0.75):
+    """Cubic-convolution weights of the four taps at offsets -1, 0, 1, 2 from
+    floor(x), t = x - floor(x) (Keys' kernel with a = -0.75):
+      W(s) = (a+2)|s|^3 - (a+3)|s|^2 + 1        for |s| <= 1
+      W(s) = a|s|^3 - 5a|s|^2 + 8a|s| - 4a       for 1 < |s| < 2."""
+    def W(s):
+        s = abs(s)
+        if s <= 1.0:
+            return (a + 2.0) * s ** 3 - (a + 3.0) * s ** 2 + 1.0
+        if s < 2.0:
+            return a * s ** 3 - 5.0 * a * s ** 2 + 8.0 * a * s - 4.0 * a
+        return 0.0
+    return [W(1.0 + t), W(t), W(1.0 - t), W(2.0 - t)]
+
+
+def resample_axis(x: np.ndarray, axis: int, n_out: int, mode: str) -> np.ndarray:
+    """Resample one axis of x to n_out samples, sample centres aligned
+    (align_corners off): output o reads source coordinate
+    c = (o + 1/2) * n_in / n_out - 1/2.  'cubic': the four taps around c with
+    cubic_weights, indices clamped to the axis; 'linear': the two taps around
+    max(c, 0), the upper one clamped to the axis."""
+    n_in = x.shape[axis]
+    x = np.moveaxis(_f64(x), axis, 0)
+    out = np.zeros((n_out,) + x.shape[1:])
+    for o in range(n_out):
+        c = (o + 0.5) * n_in / n_out - 0.5
+        if mode == "cubic":
+            i = math.floor(c)
+            for k, wk in enumerate(cubic_weights(c - i)):
+                out[o] += wk * x[min(max(i - 1 + k, 0), n_in - 1)]
+        else:
+            c = max(c, 0.0)
+            i = math.floor(c)
+            lam = c - i
+            out[o] = (1.0 - lam) * x[min(i, n_in - 1)] + lam * x[min(i + 1, n_in - 1)]
+    return np.moveaxis(out, 0, axis)
+
+
+def interpolate_pos_table(pos: np.ndarray, n_prefix: int, src_grid, dst_grid, mode: int) -> np.ndarray:
+    """A position table built for src_grid = (t, h, w), resampled to dst_grid
+    (jepa.cpp "GGUF schema (v1)", "Encoder tensors": the runtime bicubic /
+    trilinear-interpolates the precomputed table for other grids).  The
+    prefix (CLS) rows are kept.  mode 1: bicubic over (h, w) of a one-frame
+    table; mode 2: trilinear over (t, h, w).  Reading: sample centres aligned
+    (align_corners off), cubic a = -0.75, the separable products of the axis
+    resamplings."""
+    pos = _f64(pos)
+    D = pos.shape[1]
+    t0, h0, w0 = src_grid
+    t1, h1, w1 = dst_grid
+    g = pos[n_prefix:n_prefix + t0 * h0 * w0].reshape(t0, h0, w0, D)
+    if mode == 1:
+        assert t0 == 1 and t1 == 1, "bicubic resampling of a one-frame table"
+        g = resample_axis(resample_axis(g, 1, h1, "cubic"), 2, w1, "cubic")
+    elif mode == 2:
+        g = resample_axis(resample_axis(resample_axis(g, 0, t1, "linear"), 1, h1, "linear"), 2, w1, "linear")
+    else:
+        raise ValueError("unknown interpolation mode")
+    return np.concatenate([pos[:n_prefix], g.reshape(t1 * h1 * w1, D)], axis=0)
+
+
 def assemble_tokens(E: np.ndarray, hp, cls, pos, mod) -> np.ndarray:
     """a3: Z = [cls?; E] (+ pos) (+ mod).  The pos table rows are [CLS?;
     patches] ("GGUF schema (v1)", enc.pos_embed); a CLS with no table gets
@@ -305,11 +366,23 @@ def rope_and_mask(hp, pixels_shape):
     return rope_pos, visible
 
 
+def position_table(hp, w, pixels_shape):
+    """The table the tokens get: the stored one, or its resampling to the
+    input grid when the model interpolates and the grids differ."""
+    if _hp(hp, "pos_type") != POS_TABLE or not _hp(hp, "pos_interp", 0):
+        return w.pos
+    grid, _, p = geometry(hp, pixels_shape)
+    src = (_hp(hp, "pos_grid_t"), _hp(hp, "pos_grid_h"), _hp(hp, "pos_grid_w"))
+    if tuple(src) == tuple(grid):
+        return w.pos
+    return interpolate_pos_table(w.pos, p, src, grid, _hp(hp, "pos_interp"))
+
+
 def embed(hp, w, pixels) -> np.ndarray:
     """a1-a3: patchify, patch GEMM with bias, token assembly."""
     A = patchify(_f64(pixels), _hp(hp, "tubelet_size"), _hp(hp, "patch_size"))
     E = linear(A, w.patch_w, w.patch_b)
-    return assemble_tokens(E, hp, w.cls, w.pos, w.mod)
+    return assemble_tokens(E, hp, w.cls, position_table(hp, w, pixels.shape), w.mod)
 
 
 def pool(out: np.ndarray, hp) -> np.ndarray:

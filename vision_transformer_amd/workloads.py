@@ -40,6 +40,7 @@ import numpy as np
 
 DTYPE_F32, DTYPE_BF16, DTYPE_F16 = 0, 1, 2
 POS_NONE, POS_TABLE = 0, 1
+POS_INTERP_NONE, POS_INTERP_BICUBIC, POS_INTERP_TRILINEAR = 0, 1, 2
 ROPE_NONE, ROPE_3D = 0, 1
 LAYOUT_TILED, LAYOUT_INTERLEAVED = 0, 1
 ATTN_FULL, ATTN_BLOCK_CAUSAL = 0, 1
@@ -60,6 +61,8 @@ class EncoderConfig:
     rope_theta: float = 10000.0
     pos_type: int = POS_NONE
     pos_kind: str = ""            # "learned" | "sincos2d" (table contents only)
+    pos_interp: int = POS_INTERP_NONE
+    pos_grid: Optional[tuple] = None  # the table's (t, h, w) grid; None: the input grid
     rope: int = ROPE_NONE
     rope_layout: int = LAYOUT_TILED
     rope_interpolate: int = 0
@@ -104,6 +107,30 @@ class EncoderConfig:
         return self.n_patches + self.n_prefix
 
     @property
+    def table_grid(self):
+        """The (t, h, w) grid the position table was built for."""
+        return tuple(self.pos_grid) if self.pos_grid is not None else self.grid
+
+    @property
+    def pos_grid_t(self) -> int:
+        return self.table_grid[0] if self.pos_interp else 0
+
+    @property
+    def pos_grid_h(self) -> int:
+        return self.table_grid[1] if self.pos_interp else 0
+
+    @property
+    def pos_grid_w(self) -> int:
+        return self.table_grid[2] if self.pos_interp else 0
+
+    @property
+    def pos_rows(self) -> int:
+        if self.pos_type != POS_TABLE:
+            return 0
+        t, h, w = self.table_grid
+        return t * h * w + self.n_prefix
+
+    @property
     def patch_k(self) -> int:
         return self.in_chans * self.tubelet_size * self.patch_size * self.patch_size
 
@@ -115,8 +142,11 @@ class EncoderConfig:
         keys = ["embed_dim", "n_layer", "n_head", "ffn_dim", "patch_size", "tubelet_size",
                 "in_chans", "ln_eps", "rope_theta", "pos_type", "rope", "rope_layout",
                 "rope_interpolate", "rope_ref_grid", "cls_token", "modality_embed",
-                "layer_scale", "attn_mode", "dtype"]
-        return {k: getattr(self, k) for k in keys}
+                "layer_scale", "attn_mode", "dtype", "pos_interp"]
+        hp = {k: getattr(self, k) for k in keys}
+        hp["pos_rows"] = self.pos_rows
+        hp["pos_grid_t"], hp["pos_grid_h"], hp["pos_grid_w"] = self.table_grid if self.pos_interp else (0, 0, 0)
+        return hp
 
     def flops(self) -> float:
         """Algorithmic FLOPs of one forward: 2*M*N*K per GEMM plus 4*D per
@@ -289,12 +319,13 @@ def make_workload(cfg: EncoderConfig, seed: Optional[int] = None) -> Workload:
     pos = cls = mod = None
     std_tok = cfg.std_w if cfg.std_tok is None else cfg.std_tok
     if cfg.pos_type == POS_TABLE:
+        # the table is built for its own grid (the input grid unless pos_grid says otherwise)
         if cfg.pos_kind == "sincos2d":
-            gt, gh, gw = cfg.grid
+            gt, gh, gw = cfg.table_grid
             assert gt == 1 and not cfg.cls_token
             pos = sincos2d_table(gh, gw, D, w_first=True)
         else:
-            pos = _normal(rng, (cfg.n_tokens, D), cfg.std_w)
+            pos = _normal(rng, (cfg.pos_rows, D), cfg.std_w)
     if cfg.cls_token:
         cls = _normal(rng, (D,), std_tok)
     if cfg.modality_embed:
