@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VITENC_ABI_VERSION 1
+#define VITENC_ABI_VERSION 2
 
 typedef enum {
     VITENC_OK = 0,
@@ -53,6 +53,8 @@ typedef enum {
 
 enum { VITENC_F32 = 0, VITENC_BF16 = 1, VITENC_F16 = 2 };             /* dtype */
 enum { VITENC_POS_NONE = 0, VITENC_POS_TABLE = 1 };                   /* pos_type */
+enum { VITENC_POS_INTERP_NONE = 0, VITENC_POS_INTERP_BICUBIC = 1,
+       VITENC_POS_INTERP_TRILINEAR = 2 };                               /* pos_interp */
 enum { VITENC_ROPE_NONE = 0, VITENC_ROPE_3D = 1 };                    /* rope */
 enum { VITENC_ROPE_TILED = 0, VITENC_ROPE_INTERLEAVED = 1 };          /* rope_layout */
 enum { VITENC_ATTN_FULL = 0, VITENC_ATTN_BLOCK_CAUSAL = 1 };          /* attn_mode */
@@ -61,8 +63,14 @@ enum { VITENC_ATTN_FULL = 0, VITENC_ATTN_BLOCK_CAUSAL = 1 };          /* attn_mo
  *  embed_dim D, n_layer L, n_head H (head_dim = D / H), ffn_dim F,
  *  patch_size P, tubelet_size t, in_chans C, ln_eps (1e-6 for every family),
  *  rope_theta (10000).
- *  pos_type TABLE: pos_embed has pos_rows rows [CLS?; patches]; the encoded
- *    token count must equal pos_rows (no interpolation of the table).
+ *  pos_type TABLE: pos_embed has pos_rows rows [CLS?; patches].  With
+ *    pos_interp NONE the encoded token count must equal pos_rows.  With
+ *    pos_interp BICUBIC or TRILINEAR the table was built for the token grid
+ *    pos_grid_t x pos_grid_h x pos_grid_w (pos_rows = prefix + t*h*w) and is
+ *    resampled to the input's grid when they differ ("GGUF schema (v1)",
+ *    "Encoder tensors": bicubic / trilinear interpolation for other grids):
+ *    sample centres aligned, cubic a = -0.75, indices clamped, prefix rows
+ *    kept; BICUBIC needs a one-frame table and a one-frame token grid.
  *  rope ROPE_3D: 3-D RoPE on q and k of the patch tokens, d = 2*((hd/3)/2)
  *    rotated dims per axis (t, h, w), rope_layout TILED or INTERLEAVED;
  *    rope_interpolate rescales h and w by (rope_ref_grid - 1)/(grid - 1).
@@ -81,6 +89,7 @@ typedef struct {
     int32_t rope, rope_layout, rope_interpolate, rope_ref_grid;
     int32_t cls_token, modality_embed, layer_scale, attn_mode;
     int32_t dtype;
+    int32_t pos_interp, pos_grid_t, pos_grid_h, pos_grid_w;
 } vitenc_hparams;
 
 /* One encoder block ("GGUF schema (v1)", "Encoder tensors", enc.blk.{i}.*).
@@ -353,6 +362,14 @@ vitenc_status vitenc_op_linear_residual(int32_t dtype, const void *A, const void
 /* a9 U[M, Nout] (T) = GELU_erf(A[M, K] W[Nout, K]^T + b). */
 vitenc_status vitenc_op_linear_gelu(int32_t dtype, const void *A, const void *W, const float *b,
                                     int32_t M, int32_t Nout, int32_t K, void *U, void *stream);
+
+/* Position table resampling (the step encode runs for an off-grid input):
+ * out [prefix + dt*dh*dw, D] = pos [prefix + st*sh*sw, D] resampled from grid
+ * (st, sh, sw) to (dt, dh, dw) with mode VITENC_POS_INTERP_BICUBIC (st = dt =
+ * 1) or VITENC_POS_INTERP_TRILINEAR; fp32, prefix rows copied. */
+vitenc_status vitenc_op_pos_resample(const float *pos, int32_t prefix, int32_t D, int32_t st, int32_t sh,
+                                     int32_t sw, int32_t dt, int32_t dh, int32_t dw, int32_t mode, float *out,
+                                     void *stream);
 
 /* a11 pooled feature: pooled[b] = X[b, 0] when cls, else the mean of rows
  * [n_prefix, N) of X[b]; X fp32 [B, N, D]. */

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(V.SIGNATURES), "binding and header disagree"
-    assert L.vitenc_abi_version() == 1
+    assert L.vitenc_abi_version() == 2
 
 
 FAKE = 0x1000  # a non-NULL pointer that is never dereferenced: creation only validates
@@ -91,6 +91,11 @@ def _text():
     (dict(rope=0, attn_mode=1), 1, "block_causal"),
     (dict(rope=0, rope_interpolate=1, rope_ref_grid=16), 1, "rope_interpolate"),
     (dict(pos_type=1, pos_rows=0), 1, "pos_rows"),
+    (dict(pos_type=1, pos_rows=197, pos_interp=3), 1, "pos_interp"),
+    (dict(pos_type=0, pos_interp=1, pos_grid_t=1, pos_grid_h=14, pos_grid_w=14), 1, "without a position table"),
+    (dict(pos_type=1, pos_rows=197, pos_interp=1, pos_grid_t=1, pos_grid_h=0, pos_grid_w=14), 1, "table grid"),
+    (dict(pos_type=1, pos_rows=197, pos_interp=1, pos_grid_t=1, pos_grid_h=14, pos_grid_w=14), 1, "makes 196"),
+    (dict(pos_type=1, pos_rows=392, pos_interp=1, pos_grid_t=2, pos_grid_h=14, pos_grid_w=14), 1, "one-frame"),
     (dict(embed_dim=1024, n_head=8), 6, "head_dim"),
     (dict(embed_dim=8192, n_head=128), 6, "embed_dim"),
 ])
@@ -162,6 +167,37 @@ def test_pos_table_rows_must_match_tokens():
     assert V.lib().vitenc_workspace_size(h, 1, 1, 224, 224, ctypes.byref(n)) == 2
     assert "position table" in _text()
     V.lib().vitenc_model_destroy(h)
+
+
+def test_resampled_table_accepts_other_grids():
+    """A 14x14 table with bicubic resampling encodes any one-frame grid, and
+    refuses a multi-frame one; trilinear takes any grid."""
+    w, keep = _weights(24)
+    L = V.lib()
+    n = ctypes.c_size_t()
+    st, h = _create(_hp(pos_type=1, pos_rows=196, rope=0, tubelet_size=1, pos_interp=1, pos_grid_t=1, pos_grid_h=14,
+                        pos_grid_w=14), w)
+    assert st == 0, _text()
+    assert L.vitenc_workspace_size(h, 1, 1, 224, 224, ctypes.byref(n)) == 0
+    base = n.value
+    assert L.vitenc_workspace_size(h, 1, 1, 256, 320, ctypes.byref(n)) == 0
+    assert n.value > base
+    assert L.vitenc_workspace_size(h, 1, 2, 224, 224, ctypes.byref(n)) == 2 and "bicubic" in _text()
+    L.vitenc_model_destroy(h)
+    st, h = _create(_hp(pos_type=1, pos_rows=8 * 14 * 14, rope=0, tubelet_size=2, pos_interp=2, pos_grid_t=8,
+                        pos_grid_h=14, pos_grid_w=14), w)
+    assert st == 0, _text()
+    assert L.vitenc_workspace_size(h, 1, 8, 256, 256, ctypes.byref(n)) == 0
+    L.vitenc_model_destroy(h)
+
+
+def test_pos_resample_op_refusals():
+    L = V.lib()
+    FAKE = 0x1000
+    assert L.vitenc_op_pos_resample(None, 0, 8, 1, 4, 4, 1, 5, 5, 1, FAKE, None) == 3
+    assert L.vitenc_op_pos_resample(FAKE, 0, 8, 1, 4, 4, 1, 5, 5, 7, FAKE, None) == 1
+    assert L.vitenc_op_pos_resample(FAKE, 0, 8, 2, 4, 4, 1, 5, 5, 1, FAKE, None) == 2
+    assert L.vitenc_op_pos_resample(FAKE, 0, 0, 1, 4, 4, 1, 5, 5, 2, FAKE, None) == 2
 
 
 def test_encode_refusals_before_any_launch(model):

@@ -90,6 +90,23 @@ vitenc_status validate_hparams(const vitenc_hparams *hp) {
         return fail(VITENC_EINVAL, "block_causal attention on a model without a frame grid (rope3d)");
     if (hp->pos_type == VITENC_POS_TABLE && hp->pos_rows <= 0)
         return fail(VITENC_EINVAL, "pos_type TABLE with pos_rows %d", hp->pos_rows);
+    if (hp->pos_interp != VITENC_POS_INTERP_NONE && hp->pos_interp != VITENC_POS_INTERP_BICUBIC &&
+        hp->pos_interp != VITENC_POS_INTERP_TRILINEAR)
+        return fail(VITENC_EINVAL, "unknown pos_interp %d", hp->pos_interp);
+    if (hp->pos_interp != VITENC_POS_INTERP_NONE) {
+        if (hp->pos_type != VITENC_POS_TABLE) return fail(VITENC_EINVAL, "pos_interp set without a position table");
+        if (!in_range(hp->pos_grid_t, 1, kMaxGrid) || !in_range(hp->pos_grid_h, 1, kMaxGrid) ||
+            !in_range(hp->pos_grid_w, 1, kMaxGrid))
+            return fail(VITENC_EINVAL, "position table grid %dx%dx%d outside 1..%d per axis", hp->pos_grid_t,
+                        hp->pos_grid_h, hp->pos_grid_w, kMaxGrid);
+        const int64_t rows = (int64_t)hp->pos_grid_t * hp->pos_grid_h * hp->pos_grid_w + (hp->cls_token ? 1 : 0);
+        if (rows != hp->pos_rows)
+            return fail(VITENC_EINVAL, "pos_rows %d but the table grid %dx%dx%d%s makes %lld", hp->pos_rows,
+                        hp->pos_grid_t, hp->pos_grid_h, hp->pos_grid_w, hp->cls_token ? " + CLS" : "",
+                        (long long)rows);
+        if (hp->pos_interp == VITENC_POS_INTERP_BICUBIC && hp->pos_grid_t != 1)
+            return fail(VITENC_EINVAL, "bicubic position resampling needs a one-frame table");
+    }
     if (hd != 64 && hd != 32)
         return fail(VITENC_EUNSUPPORTED, "head_dim %d: the attention kernel implements 64 and 32", hd);
     if (hp->embed_dim > kMaxEmbed)
@@ -102,7 +119,8 @@ struct Plan {
     int gt, gh, gw, Np, p, N;
     int64_t M;
     int D, F, nh, hd, K, lda, ldv;
-    size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_rope, off_tok, total;
+    size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_rope, off_tok, off_pos, total;
+    bool resample;
 };
 
 vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, int32_t W, Plan &pl) {
@@ -123,8 +141,12 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     pl.N = pl.Np + pl.p;
     pl.M = (int64_t)B * pl.N;
     if (pl.M > (int64_t(1) << 30)) return fail(VITENC_ESHAPE, "B*N = %lld rows exceed 2^30", (long long)pl.M);
-    if (hp.pos_type == VITENC_POS_TABLE && hp.pos_rows != pl.N)
+    pl.resample = hp.pos_interp != VITENC_POS_INTERP_NONE &&
+                  (hp.pos_grid_t != pl.gt || hp.pos_grid_h != pl.gh || hp.pos_grid_w != pl.gw);
+    if (hp.pos_type == VITENC_POS_TABLE && !pl.resample && hp.pos_rows != pl.N)
         return fail(VITENC_ESHAPE, "position table has %d rows but the input makes %d tokens", hp.pos_rows, pl.N);
+    if (pl.resample && hp.pos_interp == VITENC_POS_INTERP_BICUBIC && pl.gt != 1)
+        return fail(VITENC_ESHAPE, "bicubic position resampling of a %d-frame token grid", pl.gt);
     pl.D = hp.embed_dim; pl.F = hp.ffn_dim; pl.nh = hp.n_head; pl.hd = pl.D / pl.nh;
     pl.K = hp.in_chans * hp.tubelet_size * hp.patch_size * hp.patch_size;
     pl.lda = embed_lda(hp.dtype, pl.K);
@@ -147,6 +169,7 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     const int d = 2 * ((pl.hd / 3) / 2);
     pl.off_rope = take((size_t)(pl.gt + pl.gh + pl.gw) * d * 2 * 4);
     pl.off_tok = take((size_t)pl.Np * 4);
+    pl.off_pos = pl.resample ? take((size_t)pl.N * pl.D * 4) : 0;
     pl.total = off;
     return VITENC_OK;
 }
@@ -232,6 +255,16 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
     int *tok_pos = reinterpret_cast<int *>(ws + pl.off_tok);
     const int M = (int)pl.M, D = pl.D, F = pl.F;
 
+    // the position table, resampled to this input's grid when it was built for another
+    const float *pos = hp.pos_type == VITENC_POS_TABLE ? m->w.pos_embed : nullptr;
+    if (pl.resample) {
+        float *pbuf = reinterpret_cast<float *>(ws + pl.off_pos);
+        CHECK_DEV(launch_pos_resample(pos, pl.p, D, hp.pos_grid_t, hp.pos_grid_h, hp.pos_grid_w, pl.gt, pl.gh, pl.gw,
+                                      hp.pos_interp, pbuf, s),
+                  "position resampling");
+        pos = pbuf;
+    }
+
     // a1-a3: tokens
     CHECK_DEV(launch_patchify(dt, pixels, B, pl.C, T, H, W, hp.tubelet_size, hp.patch_size, A, pl.lda, s), "patchify");
     {
@@ -239,7 +272,7 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
         ep.bias = m->w.patch_b;
         ep.Z = Z;
         ep.ldz = D;
-        ep.pos = hp.pos_type == VITENC_POS_TABLE ? m->w.pos_embed : nullptr;
+        ep.pos = pos;
         ep.mod = hp.modality_embed ? m->w.mod_embed : nullptr;
         ep.Np = pl.Np;
         ep.Ntok = pl.N;
@@ -250,7 +283,7 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
                   "patch GEMM");
     }
     if (pl.p)
-        CHECK_DEV(launch_prefix_rows(m->w.cls_token, hp.pos_type == VITENC_POS_TABLE ? m->w.pos_embed : nullptr,
+        CHECK_DEV(launch_prefix_rows(m->w.cls_token, pos,
                                      hp.modality_embed ? m->w.mod_embed : nullptr,
                                      B, pl.N, D, Z, s),
                   "prefix rows");

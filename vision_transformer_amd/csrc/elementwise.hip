@@ -224,6 +224,93 @@ __global__ __launch_bounds__(256) void prefix_rows_kernel(const float *__restric
 }
 
 // ---------------------------------------------------------------------------
+// Position table resampled to another token grid (jepa.cpp "GGUF schema
+// (v1)", "Encoder tensors": tables are built for the training grid and the
+// runtime bicubic / trilinear-interpolates them for other grids).  Output
+// row r < prefix copies input row r; patch row n = (t*dh + h)*dw + w reads
+// source coordinate c = (o + 1/2) * n_in / n_out - 1/2 on each axis:
+//   mode 1 (bicubic, one-frame tables): four taps floor(c) - 1 .. floor(c) + 2
+//     per spatial axis, indices clamped to the axis, with the cubic-
+//     convolution weights (Keys' kernel, a = -0.75) of t = c - floor(c);
+//   mode 2 (trilinear): c clamped below at 0, taps floor(c) and floor(c) + 1
+//     (clamped to the axis) with weights 1 - t and t, on every axis.
+// Coordinates and weights are formed in fp64; the weighted sum in fp32.
+// One workgroup per output row, four columns per thread.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double cubic_w(double s) {
+    constexpr double a = -0.75;
+    s = fabs(s);
+    if (s <= 1.0) return ((a + 2.0) * s - (a + 3.0)) * s * s + 1.0;
+    if (s < 2.0) return ((a * s - 5.0 * a) * s + 8.0 * a) * s - 4.0 * a;
+    return 0.0;
+}
+
+// taps (index, weight) of output sample o on an axis of n_in -> n_out
+template <int MODE>
+__device__ __forceinline__ void axis_taps(int o, int n_in, int n_out, int *idx, float *wt) {
+    double c = ((double)o + 0.5) * (double)n_in / (double)n_out - 0.5;
+    if constexpr (MODE == 1) {
+        const double f = floor(c), t = c - f;
+        const int i = (int)f;
+        const double w[4] = {cubic_w(1.0 + t), cubic_w(t), cubic_w(1.0 - t), cubic_w(2.0 - t)};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            idx[k] = min(max(i - 1 + k, 0), n_in - 1);
+            wt[k] = (float)w[k];
+        }
+    } else {
+        c = fmax(c, 0.0);
+        const double f = floor(c), t = c - f;
+        const int i = (int)f;
+        idx[0] = min(i, n_in - 1);
+        idx[1] = min(i + 1, n_in - 1);
+        wt[0] = (float)(1.0 - t);
+        wt[1] = (float)t;
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void pos_resample_kernel(const float *__restrict__ pos, int prefix, int D, int st,
+                                                           int sh, int sw, int dt, int dh, int dw,
+                                                           float *__restrict__ out) {
+    const int r = blockIdx.x;
+    float *o = out + (int64_t)r * D;
+    if (r < prefix) {
+        for (int c = threadIdx.x; c < D; c += blockDim.x) o[c] = pos[(int64_t)r * D + c];
+        return;
+    }
+    const int n = r - prefix;
+    const int w = n % dw, h = (n / dw) % dh, t = n / (dw * dh);
+    constexpr int NT = MODE == 1 ? 4 : 2;
+    int it[NT], ih[NT], iw[NT];
+    float wt_t[NT], wt_h[NT], wt_w[NT];
+    if constexpr (MODE == 1) {
+        // one-frame table: no temporal taps
+        it[0] = 0; wt_t[0] = 1.0f;
+#pragma unroll
+        for (int k = 1; k < NT; ++k) { it[k] = 0; wt_t[k] = 0.0f; }
+    } else {
+        axis_taps<MODE>(t, st, dt, it, wt_t);
+    }
+    axis_taps<MODE>(h, sh, dh, ih, wt_h);
+    axis_taps<MODE>(w, sw, dw, iw, wt_w);
+    const float *src = pos + (int64_t)prefix * D;
+    for (int c = threadIdx.x; c < D; c += blockDim.x) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int a = 0; a < (MODE == 1 ? 1 : NT); ++a)
+#pragma unroll
+            for (int b = 0; b < NT; ++b)
+#pragma unroll
+                for (int e = 0; e < NT; ++e) {
+                    const int64_t row = ((int64_t)it[a] * sh + ih[b]) * sw + iw[e];
+                    acc = fmaf(wt_t[a] * wt_h[b] * wt_w[e], src[row * D + c], acc);
+                }
+        o[c] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // a6 tables of the 3-D RoPE ("Architecture", "3-D RoPE"): for axis a in
 // (t, h, w), position p and rotated element j in [0, d):
 //   angle = pos_a(p) * omega_k,  omega_k = theta^(-2k/d),
@@ -404,6 +491,21 @@ hipError_t launch_prefix_rows(const float *cls, const float *pos, const float *m
                               float *Z, hipStream_t s) {
     dim3 grid((unsigned)cdiv(D, 256), (unsigned)B);
     hipLaunchKernelGGL(prefix_rows_kernel, grid, dim3(256), 0, s, cls, pos, mod, B, Ntok, D, Z);
+    return hipGetLastError();
+}
+
+hipError_t launch_pos_resample(const float *pos, int prefix, int D, int st, int sh, int sw, int dt, int dh, int dw,
+                               int mode, float *out, hipStream_t s) {
+    const int rows = prefix + dt * dh * dw;
+    if (rows <= 0) return hipSuccess;
+    if (mode == 1)
+        hipLaunchKernelGGL(pos_resample_kernel<1>, dim3((unsigned)rows), dim3(256), 0, s, pos, prefix, D, st, sh, sw, dt,
+                           dh, dw, out);
+    else if (mode == 2)
+        hipLaunchKernelGGL(pos_resample_kernel<2>, dim3((unsigned)rows), dim3(256), 0, s, pos, prefix, D, st, sh, sw, dt,
+                           dh, dw, out);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -72,6 +72,12 @@ hipError_t launch_patchify(int dtype, const float *px, int B, int C, int T, int 
 hipError_t launch_prefix_rows(const float *cls, const float *pos, const float *mod, int B, int Ntok,
                               int D, float *Z, hipStream_t s);
 
+// out [prefix + dt*dh*dw, D] = the position table pos [prefix + st*sh*sw, D]
+// resampled from grid (st, sh, sw) to (dt, dh, dw); mode 1 bicubic (one-frame
+// tables), 2 trilinear; prefix rows copied
+hipError_t launch_pos_resample(const float *pos, int prefix, int D, int st, int sh, int sw, int dt, int dh, int dw,
+                               int mode, float *out, hipStream_t s);
+
 // fills rope_tab (cos, signed sin) for the three axes and tok_pos for every patch token
 hipError_t launch_rope_table(int head_dim, int layout, int interpolate, int ref_grid, float theta,
                              int gt, int gh, int gw, float *rope_tab, int *tok_pos, hipStream_t s);

@@ -67,6 +67,23 @@ vitenc_status vitenc_op_layernorm(int32_t out_dtype, const float *x, const float
                   "layernorm");
 }
 
+vitenc_status vitenc_op_pos_resample(const float *pos, int32_t prefix, int32_t D, int32_t st, int32_t sh,
+                                     int32_t sw, int32_t dt, int32_t dh, int32_t dw, int32_t mode, float *out,
+                                     void *stream) {
+    clear_error();
+    if (!pos || !out) return op_fail(VITENC_ENULL, "pos / out is NULL");
+    if (mode != VITENC_POS_INTERP_BICUBIC && mode != VITENC_POS_INTERP_TRILINEAR)
+        return op_fail(VITENC_EINVAL, "unknown resampling mode %d", mode);
+    if (prefix < 0 || prefix > 1 || D <= 0 || st <= 0 || sh <= 0 || sw <= 0 || dt <= 0 || dh <= 0 || dw <= 0 ||
+        st > 1023 || sh > 1023 || sw > 1023 || dt > 1023 || dh > 1023 || dw > 1023)
+        return op_fail(VITENC_ESHAPE, "bad resampling sizes");
+    if (mode == VITENC_POS_INTERP_BICUBIC && (st != 1 || dt != 1))
+        return op_fail(VITENC_ESHAPE, "bicubic resampling needs one-frame grids");
+    return op_dev(launch_pos_resample(pos, prefix, D, st, sh, sw, dt, dh, dw, mode, out,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                  "position resampling");
+}
+
 int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32_t gw) {
     const int d = 2 * ((head_dim / 3) / 2);
     return (int64_t)(gt + gh + gw) * d * 2 + (int64_t)gt * gh * gw; // cos/sin pairs, then packed positions

@@ -34,7 +34,8 @@ class Hparams(ctypes.Structure):
                [("ln_eps", c_f32), ("rope_theta", c_f32)] + \
                [(n, c_i32) for n in ("pos_type", "pos_rows", "rope", "rope_layout", "rope_interpolate",
                                       "rope_ref_grid", "cls_token", "modality_embed", "layer_scale",
-                                      "attn_mode", "dtype")]
+                                      "attn_mode", "dtype", "pos_interp", "pos_grid_t", "pos_grid_h",
+                                      "pos_grid_w")]
 
 
 BLOCK_FIELDS = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "out_w", "out_b", "ln2_w", "ln2_b", "up_w", "up_b",
@@ -91,6 +92,7 @@ SIGNATURES = {
     "vitenc_op_rope_table": (c_i32, [c_i32] * 4 + [c_f32] + [c_i32] * 3 + [c_vp, c_vp]),
     "vitenc_op_qkv_rope": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 9 + [c_vp] * 5),
     "vitenc_rope_table_floats": (ctypes.c_int64, [c_i32] * 4),
+    "vitenc_op_pos_resample": (c_i32, [c_vp] + [c_i32] * 9 + [c_vp, c_vp]),
     "vitenc_op_attention": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp]),
     "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_linear_gelu": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
@@ -492,6 +494,18 @@ def op_qkv_rope(dtype, Y, qkv_w, qkv_b, B, N, n_head, rope=0, rope_layout=0, rop
                                    grid[0], grid[1], grid[2], n_prefix, tab.data_ptr() if rope else None,
                                    Q.data_ptr(), K.data_ptr(), Vt.data_ptr(), _stream(stream)))
     return Q, K, Vt
+
+
+def op_pos_resample(pos, prefix, src_grid, dst_grid, mode, stream=None, out=None):
+    """pos fp32 [prefix + prod(src_grid), D] -> [prefix + prod(dst_grid), D]."""
+    import torch
+    D = pos.shape[1]
+    rows = prefix + dst_grid[0] * dst_grid[1] * dst_grid[2]
+    if out is None:
+        out = torch.empty((rows, D), dtype=torch.float32, device=pos.device)
+    check(lib().vitenc_op_pos_resample(pos.data_ptr(), prefix, D, *src_grid, *dst_grid, mode, out.data_ptr(),
+                                       _stream(stream)))
+    return out
 
 
 def op_attention(dtype, Q, K, Vt, attn_mode=0, n_prefix=0, tokens_per_frame=0, stream=None, out=None):
