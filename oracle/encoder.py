@@ -345,9 +345,20 @@ def encoder_block(Z: np.ndarray, blk, hp, rope_pos, visible) -> np.ndarray:
     return Z + f
 
 
+def is_image_input(hp, pixels_shape) -> bool:
+    """An image (one frame) goes through the separate one-frame tokenizer
+    when the model has one (jepa.cpp "GGUF schema (v1)", V-JEPA 2.1: a
+    2x16x16 tubelet tokenizer and a 1x16x16 image tokenizer, with a modality
+    vector per input kind).  Reading: the input kind is decided by the frame
+    count, one frame being an image."""
+    return bool(_hp(hp, "image_patch_embed", 0)) and pixels_shape[2] == 1
+
+
 def geometry(hp, pixels_shape):
     B, C, T, H, W = pixels_shape
     P, t = _hp(hp, "patch_size"), _hp(hp, "tubelet_size")
+    if is_image_input(hp, pixels_shape):
+        t = 1
     grid = (T // t, H // P, W // P)
     n_patches = grid[0] * grid[1] * grid[2]
     p = 1 if _hp(hp, "cls_token") else 0
@@ -379,7 +390,13 @@ def position_table(hp, w, pixels_shape):
 
 
 def embed(hp, w, pixels) -> np.ndarray:
-    """a1-a3: patchify, patch GEMM with bias, token assembly."""
+    """a1-a3: patchify, patch GEMM with bias, token assembly (through the
+    image tokenizer and with the image modality vector for an image input of
+    a model that has them)."""
+    if is_image_input(hp, pixels.shape):
+        A = patchify(_f64(pixels), 1, _hp(hp, "patch_size"))
+        E = linear(A, w.patch_img_w, w.patch_img_b)
+        return assemble_tokens(E, hp, w.cls, position_table(hp, w, pixels.shape), w.mod_img)
     A = patchify(_f64(pixels), _hp(hp, "tubelet_size"), _hp(hp, "patch_size"))
     E = linear(A, w.patch_w, w.patch_b)
     return assemble_tokens(E, hp, w.cls, position_table(hp, w, pixels.shape), w.mod)
@@ -394,17 +411,28 @@ def pool(out: np.ndarray, hp) -> np.ndarray:
     return out.mean(axis=1)
 
 
-def encoder_forward(hp, w, pixels, n_layers: Optional[int] = None, return_residual=False):
-    """Full forward: returns (tokens [B, N, D], pooled [B, D]) in float64."""
+def encoder_forward(hp, w, pixels, n_layers: Optional[int] = None, return_residual=False, return_hier=False):
+    """Full forward: returns (tokens [B, N, D], pooled [B, D]) in float64;
+    with return_hier also the hierarchical outputs [n_hier, B, N, D]: the
+    output of block hier_layers[k] through its own norm k ("GGUF schema
+    (v1)", enc.hier_norm.{k}: one norm per hierarchical layer; V-JEPA 2.1)."""
     rope_pos, visible = rope_and_mask(hp, pixels.shape)
     Z = embed(hp, w, pixels)
     L = len(w.blocks) if n_layers is None else n_layers
-    for blk in w.blocks[:L]:
+    hier_layers = list(_hp(hp, "hier_layers", ()) or ())
+    hier = []
+    for l, blk in enumerate(w.blocks[:L]):
         Z = encoder_block(Z, blk, hp, rope_pos, visible)
+        if l in hier_layers:
+            k = hier_layers.index(l)
+            hier.append(layer_norm(Z, w.hier_norm_w[k], w.hier_norm_b[k], _hp(hp, "ln_eps")))
     out = layer_norm(Z, w.norm_w, w.norm_b, _hp(hp, "ln_eps"))
+    res = (out, pool(out, hp))
     if return_residual:
-        return out, pool(out, hp), Z
-    return out, pool(out, hp)
+        res = res + (Z,)
+    if return_hier:
+        res = res + (np.stack(hier) if hier else np.zeros((0,) + out.shape),)
+    return res
 
 
 def encoder_block_rows(Z: np.ndarray, blk, hp, rope_pos, visible, rows: np.ndarray) -> np.ndarray:

@@ -63,6 +63,8 @@ class EncoderConfig:
     pos_kind: str = ""            # "learned" | "sincos2d" (table contents only)
     pos_interp: int = POS_INTERP_NONE
     pos_grid: Optional[tuple] = None  # the table's (t, h, w) grid; None: the input grid
+    image_patch_embed: int = 0        # a separate one-frame tokenizer (and modality vector) for images
+    hier_layers: tuple = ()           # blocks whose outputs are also returned, each with its own norm
     rope: int = ROPE_NONE
     rope_layout: int = LAYOUT_TILED
     rope_interpolate: int = 0
@@ -89,8 +91,17 @@ class EncoderConfig:
         return self.embed_dim // self.n_head
 
     @property
+    def is_image(self) -> bool:
+        """An image input through the separate one-frame tokenizer."""
+        return bool(self.image_patch_embed) and self.frames == 1
+
+    @property
+    def input_tubelet(self) -> int:
+        return 1 if self.is_image else self.tubelet_size
+
+    @property
     def grid(self):
-        return (self.frames // self.tubelet_size, self.height // self.patch_size,
+        return (self.frames // self.input_tubelet, self.height // self.patch_size,
                 self.width // self.patch_size)
 
     @property
@@ -132,7 +143,7 @@ class EncoderConfig:
 
     @property
     def patch_k(self) -> int:
-        return self.in_chans * self.tubelet_size * self.patch_size * self.patch_size
+        return self.in_chans * self.input_tubelet * self.patch_size * self.patch_size
 
     def replace(self, **kw) -> "EncoderConfig":
         return dataclasses.replace(self, **kw)
@@ -145,6 +156,9 @@ class EncoderConfig:
                 "layer_scale", "attn_mode", "dtype", "pos_interp"]
         hp = {k: getattr(self, k) for k in keys}
         hp["pos_rows"] = self.pos_rows
+        hp["image_patch_embed"] = self.image_patch_embed
+        hp["n_hier"] = len(self.hier_layers)
+        hp["hier_layers"] = tuple(self.hier_layers)
         hp["pos_grid_t"], hp["pos_grid_h"], hp["pos_grid_w"] = self.table_grid if self.pos_interp else (0, 0, 0)
         return hp
 
@@ -291,6 +305,13 @@ class Weights:
     norm_w: np.ndarray
     norm_b: np.ndarray
     store: Dict[str, np.ndarray] = field(default_factory=dict)
+    # the separate one-frame tokenizer and its modality vector
+    patch_img_w: Optional[np.ndarray] = None
+    patch_img_b: Optional[np.ndarray] = None
+    mod_img: Optional[np.ndarray] = None
+    # one norm per hierarchical output
+    hier_norm_w: List[np.ndarray] = field(default_factory=list)
+    hier_norm_b: List[np.ndarray] = field(default_factory=list)
 
 
 @dataclass
@@ -312,7 +333,8 @@ def make_workload(cfg: EncoderConfig, seed: Optional[int] = None) -> Workload:
     pixels = rng.standard_normal((B, C, T, H, W), dtype=np.float32)
 
     wstore = {}
-    pw_s, pw = quantise(_normal(rng, (D, cfg.patch_k), cfg.std_w), dt)
+    kvid = cfg.in_chans * cfg.tubelet_size * cfg.patch_size * cfg.patch_size
+    pw_s, pw = quantise(_normal(rng, (D, kvid), cfg.std_w), dt)
     wstore["patch_w"] = pw_s
     pb = _normal(rng, (D,), cfg.std_w)
 
@@ -354,6 +376,16 @@ def make_workload(cfg: EncoderConfig, seed: Optional[int] = None) -> Workload:
         blocks.append(Block(qkv_w, qkv_b, out_w, out_b, up_w, up_b, down_w, down_b,
                             ones, zeros, ones, zeros, ls1, ls2, st))
     w = Weights(pw, pb, pos, cls, mod, blocks, ones, zeros, wstore)
+    # drawn last, so that the draws above do not depend on these options
+    if cfg.image_patch_embed:
+        kimg = cfg.in_chans * cfg.patch_size * cfg.patch_size
+        wstore["patch_img_w"], w.patch_img_w = quantise(_normal(rng, (D, kimg), cfg.std_w), dt)
+        w.patch_img_b = _normal(rng, (D,), cfg.std_w)
+        if cfg.modality_embed:
+            w.mod_img = _normal(rng, (D,), std_tok)
+    for _ in cfg.hier_layers:
+        w.hier_norm_w.append((1.0 + 0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32))
+        w.hier_norm_b.append((0.1 * rng.standard_normal(D, dtype=np.float32)).astype(np.float32))
     return Workload(cfg, pixels, w)
 
 
