@@ -53,6 +53,8 @@ typedef enum {
 
 enum { VITENC_F32 = 0, VITENC_BF16 = 1, VITENC_F16 = 2 };             /* dtype */
 enum { VITENC_POS_NONE = 0, VITENC_POS_TABLE = 1 };                   /* pos_type */
+#define VITENC_MAX_HIER 8  /* hierarchical outputs at most */
+
 enum { VITENC_POS_INTERP_NONE = 0, VITENC_POS_INTERP_BICUBIC = 1,
        VITENC_POS_INTERP_TRILINEAR = 2 };                               /* pos_interp */
 enum { VITENC_ROPE_NONE = 0, VITENC_ROPE_3D = 1 };                    /* rope */
@@ -80,7 +82,15 @@ enum { VITENC_ATTN_FULL = 0, VITENC_ATTN_BLOCK_CAUSAL = 1 };          /* attn_mo
  *  attn_mode BLOCK_CAUSAL: key j visible to query i iff frame(i) >= frame(j);
  *    the CLS row sees every key, no patch query sees the CLS key.
  *  dtype: F32 (true fp32 arithmetic throughout), BF16 or F16 (matrices and
- *    activations in that type, fp32 accumulation, fp32 residual stream). */
+ *    activations in that type, fp32 accumulation, fp32 residual stream).
+ *  image_patch_embed: the model also has a one-frame tokenizer (V-JEPA 2.1,
+ *    "GGUF schema (v1)", enc.patch_embed_img): a one-frame input (T == 1) goes
+ *    through it (tubelet 1, token grid 1 x H/P x W/P) and gets the image
+ *    modality vector instead of the video one.
+ *  n_hier, hier_layers: hierarchical outputs ("GGUF schema (v1)",
+ *    jepa.enc.hier_layers / enc.hier_norm.{k}): output k is the residual
+ *    stream after block hier_layers[k] through its own norm k; the layer ids
+ *    strictly increase within [0, n_layer); at most VITENC_MAX_HIER. */
 typedef struct {
     int32_t embed_dim, n_layer, n_head, ffn_dim;
     int32_t patch_size, tubelet_size, in_chans;
@@ -90,6 +100,8 @@ typedef struct {
     int32_t cls_token, modality_embed, layer_scale, attn_mode;
     int32_t dtype;
     int32_t pos_interp, pos_grid_t, pos_grid_h, pos_grid_w;
+    int32_t image_patch_embed;
+    int32_t n_hier, hier_layers[VITENC_MAX_HIER];
 } vitenc_hparams;
 
 /* One encoder block ("GGUF schema (v1)", "Encoder tensors", enc.blk.{i}.*).
@@ -112,12 +124,18 @@ typedef struct {
  * fp32 iff pos_type TABLE; cls_token [D] fp32 iff cls_token; mod_embed [D]
  * fp32 iff modality_embed; blocks: HOST array of n_layer entries (copied by
  * vitenc_model_create; the device pointers inside are borrowed);
- * norm_w/norm_b [D] fp32 (the final LayerNorm). */
+ * norm_w/norm_b [D] fp32 (the final LayerNorm).  With image_patch_embed:
+ * patch_img_w [D, C*P*P] (model dtype) and patch_img_b [D], and mod_embed_img
+ * [D] iff modality_embed (mod_embed is then the video vector).  hier_norm_w/b
+ * [k] [D] fp32 for k < n_hier. */
 typedef struct {
     const void *patch_w;  const float *patch_b;
     const float *pos_embed, *cls_token, *mod_embed;
     const vitenc_block_weights *blocks;
     const float *norm_w, *norm_b;
+    const void *patch_img_w;  const float *patch_img_b;
+    const float *mod_embed_img;
+    const float *hier_norm_w[VITENC_MAX_HIER], *hier_norm_b[VITENC_MAX_HIER];
 } vitenc_weights;
 
 typedef struct vitenc_model vitenc_model;
@@ -284,6 +302,12 @@ vitenc_status vitenc_head_workspace_size(const vitenc_head *h, int32_t B, int32_
 vitenc_status vitenc_head_forward(const vitenc_head *h, const float *tokens, int32_t B, int32_t N,
                                   void *workspace, size_t ws_bytes, float *pooled, float *logits,
                                   void *stream);
+
+/* vitenc_encode that also writes the hierarchical outputs: out_hier NULL
+ * or fp32 [n_hier, B, N, D] (output k at offset k*B*N*D). */
+vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int32_t B, int32_t T,
+                                 int32_t H, int32_t W, void *workspace, size_t ws_bytes,
+                                 float *out_tokens, float *out_pooled, float *out_hier, void *stream);
 
 /* Thread-local text of the last refusal on this thread ("" if none). */
 const char *vitenc_error_text(void);

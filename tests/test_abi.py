@@ -191,6 +191,40 @@ def test_resampled_table_accepts_other_grids():
     L.vitenc_model_destroy(h)
 
 
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(image_patch_embed=2), 1, "image_patch_embed"),
+    (dict(n_hier=9), 1, "n_hier"),
+    (dict(n_hier=2, hier_layers=(5, 5)), 1, "strictly increase"),
+    (dict(n_hier=1, hier_layers=(24,)), 1, "strictly increase"),
+])
+def test_hier_and_image_refusals(kw, status, needle):
+    w, _keep = _weights(24)
+    st, h = _create(_hp(**kw), w)
+    assert st == status and needle in _text(), _text()
+
+
+def test_image_tokenizer_and_hier_norm_pointers_required():
+    w, _keep = _weights(24)
+    st, _ = _create(_hp(image_patch_embed=1), w)
+    assert st == 3 and "patch_img_w" in _text()
+    w.patch_img_w = w.patch_img_b = 0x1000
+    st, _ = _create(_hp(image_patch_embed=1, modality_embed=1), w)
+    assert st == 3 and "mod_embed_img" in _text()
+    st, _ = _create(_hp(n_hier=2, hier_layers=(3, 7)), w)
+    assert st == 3 and "hier norm 0" in _text()
+    w.hier_norm_w[0] = w.hier_norm_b[0] = w.hier_norm_w[1] = w.hier_norm_b[1] = 0x1000
+    st, h = _create(_hp(n_hier=2, hier_layers=(3, 7), image_patch_embed=1), w)
+    assert st == 0, _text()
+    n = ctypes.c_size_t()
+    # one frame goes through the image tokenizer; a tubelet-2 model without one refuses it
+    assert V.lib().vitenc_workspace_size(h, 1, 1, 256, 256, ctypes.byref(n)) == 0
+    V.lib().vitenc_model_destroy(h)
+    st, h = _create(_hp(), w)
+    assert st == 0
+    assert V.lib().vitenc_workspace_size(h, 1, 1, 256, 256, ctypes.byref(n)) == 2 and "tubelet" in _text()
+    V.lib().vitenc_model_destroy(h)
+
+
 def test_pos_resample_op_refusals():
     L = V.lib()
     FAKE = 0x1000

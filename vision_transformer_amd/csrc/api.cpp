@@ -107,6 +107,15 @@ vitenc_status validate_hparams(const vitenc_hparams *hp) {
         if (hp->pos_interp == VITENC_POS_INTERP_BICUBIC && hp->pos_grid_t != 1)
             return fail(VITENC_EINVAL, "bicubic position resampling needs a one-frame table");
     }
+    if (hp->image_patch_embed != 0 && hp->image_patch_embed != 1)
+        return fail(VITENC_EINVAL, "image_patch_embed %d is not 0 or 1", hp->image_patch_embed);
+    if (!in_range(hp->n_hier, 0, VITENC_MAX_HIER))
+        return fail(VITENC_EINVAL, "n_hier %d outside 0..%d", hp->n_hier, VITENC_MAX_HIER);
+    for (int k = 0; k < hp->n_hier; ++k) {
+        if (!in_range(hp->hier_layers[k], 0, hp->n_layer - 1) || (k > 0 && hp->hier_layers[k] <= hp->hier_layers[k - 1]))
+            return fail(VITENC_EINVAL, "hier_layers must strictly increase within [0, n_layer): entry %d is %d", k,
+                        hp->hier_layers[k]);
+    }
     if (hd != 64 && hd != 32)
         return fail(VITENC_EUNSUPPORTED, "head_dim %d: the attention kernel implements 64 and 32", hd);
     if (hp->embed_dim > kMaxEmbed)
@@ -115,6 +124,8 @@ vitenc_status validate_hparams(const vitenc_hparams *hp) {
 }
 
 struct Plan {
+    bool image;
+    int tub;
     int B, C, T, H, W;
     int gt, gh, gw, Np, p, N;
     int64_t M;
@@ -127,11 +138,14 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     const vitenc_hparams &hp = m->hp;
     if (B <= 0 || T <= 0 || H <= 0 || W <= 0)
         return fail(VITENC_ESHAPE, "non-positive input shape B=%d T=%d H=%d W=%d", B, T, H, W);
-    if (T % hp.tubelet_size) return fail(VITENC_ESHAPE, "T=%d not a multiple of tubelet_size %d", T, hp.tubelet_size);
+    // a one-frame input of a model with an image tokenizer goes through it
+    pl.image = hp.image_patch_embed && T == 1;
+    pl.tub = pl.image ? 1 : hp.tubelet_size;
+    if (T % pl.tub) return fail(VITENC_ESHAPE, "T=%d not a multiple of tubelet_size %d", T, pl.tub);
     if (H % hp.patch_size || W % hp.patch_size)
         return fail(VITENC_ESHAPE, "H=%d / W=%d not multiples of patch_size %d", H, W, hp.patch_size);
     pl.B = B; pl.C = hp.in_chans; pl.T = T; pl.H = H; pl.W = W;
-    pl.gt = T / hp.tubelet_size; pl.gh = H / hp.patch_size; pl.gw = W / hp.patch_size;
+    pl.gt = T / pl.tub; pl.gh = H / hp.patch_size; pl.gw = W / hp.patch_size;
     if (pl.gt > kMaxGrid || pl.gh > kMaxGrid || pl.gw > kMaxGrid)
         return fail(VITENC_ESHAPE, "token grid %dx%dx%d exceeds %d per axis", pl.gt, pl.gh, pl.gw, kMaxGrid);
     const int64_t np = (int64_t)pl.gt * pl.gh * pl.gw;
@@ -148,7 +162,7 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     if (pl.resample && hp.pos_interp == VITENC_POS_INTERP_BICUBIC && pl.gt != 1)
         return fail(VITENC_ESHAPE, "bicubic position resampling of a %d-frame token grid", pl.gt);
     pl.D = hp.embed_dim; pl.F = hp.ffn_dim; pl.nh = hp.n_head; pl.hd = pl.D / pl.nh;
-    pl.K = hp.in_chans * hp.tubelet_size * hp.patch_size * hp.patch_size;
+    pl.K = hp.in_chans * pl.tub * hp.patch_size * hp.patch_size;
     pl.lda = embed_lda(hp.dtype, pl.K);
     pl.ldv = (int)rup(pl.N, 64);
     const size_t es = (size_t)dtype_size(hp.dtype);
@@ -209,6 +223,12 @@ vitenc_status vitenc_model_create(const vitenc_hparams *hp, const vitenc_weights
             if (!p) return fail(VITENC_ENULL, "block %d: a required tensor is NULL", i);
         if (hp->layer_scale && (!b.ls1 || !b.ls2)) return fail(VITENC_ENULL, "block %d: ls1 / ls2 is NULL", i);
     }
+    if (hp->image_patch_embed) {
+        if (!w->patch_img_w || !w->patch_img_b) return fail(VITENC_ENULL, "patch_img_w / patch_img_b is NULL");
+        if (hp->modality_embed && !w->mod_embed_img) return fail(VITENC_ENULL, "mod_embed_img is NULL");
+    }
+    for (int k = 0; k < hp->n_hier; ++k)
+        if (!w->hier_norm_w[k] || !w->hier_norm_b[k]) return fail(VITENC_ENULL, "hier norm %d is NULL", k);
     vitenc_model *m = new vitenc_model;
     m->hp = *hp;
     m->w = *w;
@@ -233,6 +253,12 @@ vitenc_status vitenc_workspace_size(const vitenc_model *m, int32_t B, int32_t T,
 
 vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t B, int32_t T, int32_t H, int32_t W,
                             void *workspace, size_t ws_bytes, float *out_tokens, float *out_pooled, void *stream) {
+    return vitenc_encode_hier(m, pixels, B, T, H, W, workspace, ws_bytes, out_tokens, out_pooled, nullptr, stream);
+}
+
+vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int32_t B, int32_t T, int32_t H,
+                                 int32_t W, void *workspace, size_t ws_bytes, float *out_tokens, float *out_pooled,
+                                 float *out_hier, void *stream) {
     g_error.clear();
     if (!m) return fail(VITENC_ENULL, "model is NULL");
     if (!pixels || !out_tokens) return fail(VITENC_ENULL, "pixels / out_tokens is NULL");
@@ -266,25 +292,27 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
     }
 
     // a1-a3: tokens
-    CHECK_DEV(launch_patchify(dt, pixels, B, pl.C, T, H, W, hp.tubelet_size, hp.patch_size, A, pl.lda, s), "patchify");
+    CHECK_DEV(launch_patchify(dt, pixels, B, pl.C, T, H, W, pl.tub, hp.patch_size, A, pl.lda, s), "patchify");
+    const float *mod = !hp.modality_embed ? nullptr : pl.image ? m->w.mod_embed_img : m->w.mod_embed;
     {
         EpiArgs ep;
-        ep.bias = m->w.patch_b;
+        ep.bias = pl.image ? m->w.patch_img_b : m->w.patch_b;
         ep.Z = Z;
         ep.ldz = D;
         ep.pos = pos;
-        ep.mod = hp.modality_embed ? m->w.mod_embed : nullptr;
+        ep.mod = mod;
         ep.Np = pl.Np;
         ep.Ntok = pl.N;
         ep.prefix = pl.p;
         const bool split = pl.lda == 2 * pl.K;
         ep.kwrap = split ? pl.K : 0;
-        CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda, m->w.patch_w, pl.K, B * pl.Np, D, split ? 2 * pl.K : pl.K, ep, s),
+        CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda, pl.image ? m->w.patch_img_w : m->w.patch_w, pl.K, B * pl.Np, D,
+                              split ? 2 * pl.K : pl.K, ep, s),
                   "patch GEMM");
     }
     if (pl.p)
         CHECK_DEV(launch_prefix_rows(m->w.cls_token, pos,
-                                     hp.modality_embed ? m->w.mod_embed : nullptr,
+                                     mod,
                                      B, pl.N, D, Z, s),
                   "prefix rows");
     if (hp.rope)
@@ -299,10 +327,18 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
     g.rope = hp.rope; g.gt = pl.gt; g.gh = pl.gh; g.gw = pl.gw; g.rope_tab = rope_tab; g.tok_pos = tok_pos;
     BlockBufs bb;
     bb.Z = Z; bb.Y = Y; bb.Q = Q; bb.K = Kb; bb.Vt = Vt; bb.O = O; bb.U = U;
+    int k_hier = 0;
     for (int l = 0; l < hp.n_layer; ++l) {
         const char *what = "block";
         const hipError_t e = run_block(g, bb, m->blocks[l], s, &what);
         CHECK_DEV(e, what);
+        if (k_hier < hp.n_hier && hp.hier_layers[k_hier] == l) {
+            if (out_hier)
+                CHECK_DEV(launch_layernorm(DT_F32, Z, m->w.hier_norm_w[k_hier], m->w.hier_norm_b[k_hier], hp.ln_eps, M,
+                                           D, out_hier + (int64_t)k_hier * M * D, s),
+                          "hierarchical norm");
+            ++k_hier;
+        }
     }
     CHECK_DEV(launch_layernorm(DT_F32, Z, m->w.norm_w, m->w.norm_b, hp.ln_eps, M, D, out_tokens, s), "final norm");
     if (out_pooled) CHECK_DEV(launch_pool(out_tokens, B, pl.N, D, hp.cls_token, pl.p, out_pooled, s), "pool");

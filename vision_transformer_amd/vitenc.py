@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libvitenc.so")
 c_i32, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
 F32, BF16, F16 = 0, 1, 2
+MAX_HIER = 8
 STATUS = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "ENULL", 4: "EWORKSPACE", 5: "EDEVICE", 6: "EUNSUPPORTED"}
 
 
@@ -35,7 +36,8 @@ class Hparams(ctypes.Structure):
                [(n, c_i32) for n in ("pos_type", "pos_rows", "rope", "rope_layout", "rope_interpolate",
                                       "rope_ref_grid", "cls_token", "modality_embed", "layer_scale",
                                       "attn_mode", "dtype", "pos_interp", "pos_grid_t", "pos_grid_h",
-                                      "pos_grid_w")]
+                                      "pos_grid_w", "image_patch_embed", "n_hier")] + \
+               [("hier_layers", c_i32 * MAX_HIER)]
 
 
 BLOCK_FIELDS = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "out_w", "out_b", "ln2_w", "ln2_b", "up_w", "up_b",
@@ -49,7 +51,8 @@ class BlockWeights(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [("patch_w", c_vp), ("patch_b", c_vp), ("pos_embed", c_vp), ("cls_token", c_vp),
                 ("mod_embed", c_vp), ("blocks", ctypes.POINTER(BlockWeights)), ("norm_w", c_vp),
-                ("norm_b", c_vp)]
+                ("norm_b", c_vp), ("patch_img_w", c_vp), ("patch_img_b", c_vp), ("mod_embed_img", c_vp),
+                ("hier_norm_w", c_vp * MAX_HIER), ("hier_norm_b", c_vp * MAX_HIER)]
 
 
 class PredHparams(ctypes.Structure):
@@ -87,6 +90,7 @@ SIGNATURES = {
     "vitenc_model_destroy": (None, [c_vp]),
     "vitenc_workspace_size": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
     "vitenc_encode": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp, c_vp, c_vp]),
+    "vitenc_encode_hier": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp, c_vp, c_vp, c_vp]),
     "vitenc_op_embed": (c_i32, [c_i32, c_vp] + [c_i32] * 7 + [c_vp] * 5 + [c_i32, c_vp, c_vp, c_vp]),
     "vitenc_op_layernorm": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_f32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_rope_table": (c_i32, [c_i32] * 4 + [c_f32] + [c_i32] * 3 + [c_vp, c_vp]),
@@ -168,7 +172,11 @@ def f32_to_device(arr, device="cuda"):
 def make_hparams(hp: Dict) -> Hparams:
     h = Hparams()
     for name, _ in Hparams._fields_:
-        setattr(h, name, hp.get(name, 0))
+        if name == "hier_layers":
+            layers = list(hp.get("hier_layers", ()) or ())
+            h.hier_layers[:] = (layers + [0] * MAX_HIER)[:MAX_HIER]
+        else:
+            setattr(h, name, hp.get(name, 0))
     return h
 
 
@@ -185,10 +193,15 @@ class Encoder:
         for i, b in enumerate(blocks):
             for n in BLOCK_FIELDS:
                 setattr(self._bw[i], n, _ptr(b.get(n)))
+        hw = list(tensors.get("hier_norm_w", []))
+        hb = list(tensors.get("hier_norm_b", []))
         self._w = Weights(_ptr(tensors["patch_w"]), _ptr(tensors["patch_b"]), _ptr(tensors.get("pos")),
                           _ptr(tensors.get("cls")), _ptr(tensors.get("mod")),
                           ctypes.cast(self._bw, ctypes.POINTER(BlockWeights)), _ptr(tensors["norm_w"]),
-                          _ptr(tensors["norm_b"]))
+                          _ptr(tensors["norm_b"]), _ptr(tensors.get("patch_img_w")),
+                          _ptr(tensors.get("patch_img_b")), _ptr(tensors.get("mod_img")),
+                          (c_vp * MAX_HIER)(*([_ptr(t) for t in hw] + [None] * (MAX_HIER - len(hw)))),
+                          (c_vp * MAX_HIER)(*([_ptr(t) for t in hb] + [None] * (MAX_HIER - len(hb)))))
         h = c_vp()
         check(L.vitenc_model_create(ctypes.byref(self._hp), ctypes.byref(self._w), ctypes.byref(h)))
         self.handle = h
@@ -203,6 +216,12 @@ class Encoder:
              "pos": f32_to_device(w.pos, device), "cls": f32_to_device(w.cls, device),
              "mod": f32_to_device(w.mod, device), "norm_w": f32_to_device(w.norm_w, device),
              "norm_b": f32_to_device(w.norm_b, device)}
+        if getattr(w, "patch_img_w", None) is not None:
+            t["patch_img_w"] = to_device(w.store["patch_img_w"], dt, device)
+            t["patch_img_b"] = f32_to_device(w.patch_img_b, device)
+            t["mod_img"] = f32_to_device(w.mod_img, device)
+        t["hier_norm_w"] = [f32_to_device(x, device) for x in getattr(w, "hier_norm_w", [])]
+        t["hier_norm_b"] = [f32_to_device(x, device) for x in getattr(w, "hier_norm_b", [])]
         blocks = []
         for b in w.blocks:
             d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
@@ -230,8 +249,8 @@ class Encoder:
 
     def tokens(self, T, H, W) -> int:
         hp = self.hp
-        return (T // hp["tubelet_size"]) * (H // hp["patch_size"]) * (W // hp["patch_size"]) + \
-            (1 if hp["cls_token"] else 0)
+        tub = 1 if (hp.get("image_patch_embed") and T == 1) else hp["tubelet_size"]
+        return (T // tub) * (H // hp["patch_size"]) * (W // hp["patch_size"]) + (1 if hp["cls_token"] else 0)
 
     def alloc(self, B, T, H, W, device="cuda"):
         """Workspace and outputs for a [B, C, T, H, W] input."""
@@ -243,10 +262,15 @@ class Encoder:
         pooled = torch.empty((B, D), dtype=torch.float32, device=device)
         return ws, out, pooled
 
-    def encode_into(self, pixels, ws, out, pooled=None, stream=None):
+    def encode_into(self, pixels, ws, out, pooled=None, stream=None, hier=None):
+        """hier: None, or fp32 [n_hier, B, N, D] for the hierarchical outputs."""
         B, C, T, H, W = pixels.shape
-        check(lib().vitenc_encode(self.handle, pixels.data_ptr(), B, T, H, W, ws.data_ptr(), ws.numel(),
-                                  out.data_ptr(), _ptr(pooled), _stream(stream)))
+        if hier is None:
+            check(lib().vitenc_encode(self.handle, pixels.data_ptr(), B, T, H, W, ws.data_ptr(), ws.numel(),
+                                      out.data_ptr(), _ptr(pooled), _stream(stream)))
+        else:
+            check(lib().vitenc_encode_hier(self.handle, pixels.data_ptr(), B, T, H, W, ws.data_ptr(), ws.numel(),
+                                           out.data_ptr(), _ptr(pooled), hier.data_ptr(), _stream(stream)))
 
     def encode(self, pixels, stream=None):
         B, C, T, H, W = pixels.shape
