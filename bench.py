@@ -1,7 +1,7 @@
 """Throughput of the ViT encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu-baseline]
-                    [--part all|encoder|predictor|head]
+                    [--part all|encoder|predictor|head|variants]
     python bench.py --write-counters KERNEL FETCH.csv WRITE.csv OUT.txt
 
 
@@ -14,9 +14,11 @@ configuration encode uses) with HIP events on the stream it is launched on.
 The line's `predictor` object times the masked-latent predictor that follows
 the encoder (one vitenc_predict call per step) the same way, with its own
 roofline and oracle baseline; `head` does the same for the attentive-pool
-classifier head (one vitenc_head_forward call per step).  `--part predictor`
-or `--part head` prints that object alone (the counter runs of their kernels
-use it).
+classifier head (one vitenc_head_forward call per step); `variants` times
+encoder options on their own inputs (a resampled position table, the one-frame
+image tokenizer with hierarchical outputs).  `--part predictor`, `--part head`
+or `--part variants` prints that object alone (the counter runs of their
+kernels use it).
 
 Its `traffic` figure comes from a committed counter summary (written by the
 --write-counters mode from two rocprofv3 --pmc runs of this script: one
@@ -69,7 +71,7 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head"), default="all",
+    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head", "variants"), default="all",
                     help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
                          "head (reported in the line's `predictor` / `head` objects), or all three")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
@@ -483,6 +485,60 @@ def bench_head(args, stream):
     return res
 
 
+def bench_variants(args, stream):
+    """Encoder options on their own inputs, each one encode call per step:
+    the ViT-L image encoder at 256x256 with its 14x14 sincos table resampled
+    bicubically (batch 8), and a V-JEPA 2.1 ViT-g image at 384x384 through the
+    one-frame tokenizer with four hierarchical outputs (batch 4).  The
+    resampling step is also timed alone against HBM bandwidth."""
+    import torch
+    from vision_transformer_amd import vitenc as V
+    from vision_transformer_amd import workloads as W
+    cases = [
+        W.CONFIGS[1].replace(name="ijepa_vit_l_256_resampled", height=256, width=256,
+                             pos_interp=W.POS_INTERP_BICUBIC, pos_grid=(1, 14, 14)),
+        W.CONFIGS[3].replace(name="vjepa21_vit_g_image_384_hier4", frames=1, batch=4, image_patch_embed=1,
+                             hier_layers=(9, 19, 29, 39)),
+    ]
+    res = {}
+    for cfg in cases:
+        log(f"[bench] variant {cfg.name}: B={cfg.batch} grid={cfg.grid} L={cfg.n_layer}")
+        wl = W.make_workload(cfg)
+        enc = V.Encoder.from_workload(wl)
+        px = torch.from_numpy(wl.pixels).cuda()
+        ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
+        hier = None
+        if cfg.hier_layers:
+            hier = torch.empty((len(cfg.hier_layers),) + tuple(out.shape), dtype=torch.float32, device="cuda")
+        ms, _ = time_steps(lambda: enc.encode_into(px, ws, out, pooled, stream, hier=hier), max(5, args.steps // 2),
+                           args.warmup, stream)
+        tokens = cfg.batch * cfg.n_tokens
+        r = {"ms_per_step": round(ms, 4), "tokens_per_s": round(tokens / ms * 1e3, 1),
+             "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
+             "config": {"global_batch": cfg.batch, "grid": list(cfg.grid), "layers": cfg.n_layer,
+                        "embed_dim": cfg.embed_dim, "table_grid": list(cfg.table_grid) if cfg.pos_interp else None,
+                        "hier_layers": list(cfg.hier_layers)}}
+        if cfg.pos_interp:
+            tab = torch.from_numpy(wl.weights.pos).cuda()
+            dst = torch.empty((cfg.n_tokens, cfg.embed_dim), dtype=torch.float32, device="cuda")
+            reps = 50
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            V.op_pos_resample(tab, cfg.n_prefix, cfg.table_grid, cfg.grid, cfg.pos_interp, out=dst)
+            e0.record(stream)
+            for _ in range(reps):
+                V.op_pos_resample(tab, cfg.n_prefix, cfg.table_grid, cfg.grid, cfg.pos_interp, out=dst)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            nbytes = (tab.numel() + dst.numel()) * 4
+            r["pos_resample"] = {"us": round(us, 2), "bound": "hbm", "algorithmic_bytes": nbytes,
+                                 "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS}
+        res[cfg.name] = r
+        log(f"[bench] variant {cfg.name}: {r}")
+        enc.close()
+    return res
+
+
 def main():
     args = parse()
     if args.write_counters:
@@ -502,6 +558,9 @@ def main():
         return
     if args.part == "head":
         print(json.dumps({"head": bench_head(args, stream)}), flush=True)
+        return
+    if args.part == "variants":
+        print(json.dumps({"variants": bench_variants(args, stream)}), flush=True)
         return
     cfg = W.HEADLINE
     log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
@@ -541,6 +600,7 @@ def main():
     enc.close()
     pred = bench_predictor(args, stream) if args.part == "all" else None
     head = bench_head(args, stream) if args.part == "all" else None
+    variants = bench_variants(args, stream) if args.part == "all" else None
 
     line = {
         "metric": "encoder tokens/sec + MFMA TFLOP/s fraction of peak (ViT-L video, bf16, 1 GPU)",
@@ -556,6 +616,7 @@ def main():
         "cpu_baseline": cpu,
         "predictor": pred,
         "head": head,
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 
