@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (MFMA / packed vector)
 COPY_BYTES = 256 << 20        # plain device copy used to calibrate the HBM byte counters
 CSRC = os.path.join(ROOT, "vision_transformer_amd", "csrc")
 # kernel-breakdown name -> (pattern of its device kernel's mangled name, sources it is compiled from).
@@ -71,7 +72,7 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head", "variants"), default="all",
+    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head", "variants", "configs"), default="all",
                     help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
                          "head (reported in the line's `predictor` / `head` objects), or all three")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
@@ -536,6 +537,50 @@ def bench_variants(args, stream):
         res[cfg.name] = r
         log(f"[bench] variant {cfg.name}: {r}")
         enc.close()
+    # the small fp32 ViT-Ti image (257 tokens, about 90 short kernels): eager
+    # calls against replays of the call captured once into a HIP graph
+    cfg = W.CONFIGS[0]
+    wl = W.make_workload(cfg)
+    enc = V.Encoder.from_workload(wl)
+    px = torch.from_numpy(wl.pixels).cuda()
+    ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
+    eager, _ = time_steps(lambda: enc.encode_into(px, ws, out, pooled, stream), args.steps, args.warmup, stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enc.encode_into(px, ws, out, pooled)
+    replay, _ = time_steps(g.replay, args.steps, args.warmup, stream)
+    res[cfg.name + "_graph"] = {"eager_ms": round(eager, 4), "graph_replay_ms": round(replay, 4),
+                                "tokens_per_s_graph": round(cfg.batch * cfg.n_tokens / replay * 1e3, 1),
+                                "tflops_fp32_graph": round(cfg.flops() / (replay * 1e-3) / 1e12, 2)}
+    log(f"[bench] variant {cfg.name} graph: {res[cfg.name + '_graph']}")
+    enc.close()
+    return res
+
+
+def bench_configs(args, stream):
+    """Every encoder workload at its own shape (the five the metric's
+    configuration list names), one encode call per step: throughput and the
+    fraction of the MFMA peak of its arithmetic type."""
+    import torch
+    from vision_transformer_amd import vitenc as V
+    from vision_transformer_amd import workloads as W
+    res = {}
+    for cfg in W.CONFIGS:
+        wl = W.make_workload(cfg)
+        enc = V.Encoder.from_workload(wl)
+        px = torch.from_numpy(wl.pixels).cuda()
+        ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
+        steps = 3 if cfg.n_tokens * cfg.batch > 10000 else max(5, args.steps // 2)
+        ms, _ = time_steps(lambda: enc.encode_into(px, ws, out, pooled, stream), steps, 1, stream)
+        tf = cfg.flops() / (ms * 1e-3) / 1e12
+        peak = PEAK_FP32_TFLOPS if cfg.dtype == W.DTYPE_F32 else PEAK_BF16_TFLOPS
+        res[cfg.name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.batch * cfg.n_tokens / ms * 1e3, 1),
+                         "tflops": round(tf, 2), "peak_tflops": peak, "mfma_frac": round(tf / peak, 4),
+                         "dtype": "f32" if cfg.dtype == W.DTYPE_F32 else "bf16", "steps": steps}
+        log(f"[bench] config {cfg.name}: {res[cfg.name]}")
+        enc.close()
+        del wl, px, ws, out, pooled
+        torch.cuda.empty_cache()
     return res
 
 
@@ -561,6 +606,9 @@ def main():
         return
     if args.part == "variants":
         print(json.dumps({"variants": bench_variants(args, stream)}), flush=True)
+        return
+    if args.part == "configs":
+        print(json.dumps({"configs": bench_configs(args, stream)}), flush=True)
         return
     cfg = W.HEADLINE
     log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
@@ -601,6 +649,7 @@ def main():
     pred = bench_predictor(args, stream) if args.part == "all" else None
     head = bench_head(args, stream) if args.part == "all" else None
     variants = bench_variants(args, stream) if args.part == "all" else None
+    configs = bench_configs(args, stream) if args.part == "all" else None
 
     line = {
         "metric": "encoder tokens/sec + MFMA TFLOP/s fraction of peak (ViT-L video, bf16, 1 GPU)",
@@ -617,6 +666,7 @@ def main():
         "predictor": pred,
         "head": head,
         "variants": variants,
+        "all_configs": configs,
     }
     print(json.dumps(line), flush=True)
 

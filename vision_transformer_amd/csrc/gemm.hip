@@ -765,13 +765,20 @@ enum TileCfg { TILE_REG = 0, TILE_256x256 = 1, TILE_128x128 = 2, TILE_128x128_DE
 // With at most one 128 x 128 tile per CU (the N = D projections of one clip)
 // occupancy cannot hide the first touch of the weights in HBM: those tiles
 // keep more slabs in flight instead.
-// When 128 x 128 tiles would leave more than half of the CUs idle (the
+// 256 x 256 tiles are skipped when they would need a nearly empty second
+// round.  When 128 x 128 tiles would leave more than half of the CUs idle (the
 // width-384 projections of the predictor), 64 x 64 tiles of 4 waves spread
 // the work instead.
 inline int pick_tile(int M, int N, bool fast, bool fp32) {
     constexpr int kCUs = 256;
     if (!fast || fp32) return TILE_REG;
-    if (cdiv(M, 256) * cdiv(N, 256) >= kCUs) return TILE_256x256;
+    {
+        const int64_t t256 = cdiv(M, 256) * cdiv(N, 256);
+        // a second round of 256x256 tiles that is mostly empty (M = 4097: one
+        // CLS row past 4096) costs more than the smaller tiles
+        if (t256 >= kCUs && !(t256 % kCUs != 0 && t256 % kCUs < kCUs / 4)) return TILE_256x256;
+        if (t256 >= kCUs && cdiv(M, 128) * cdiv(N, 128) > kCUs) return TILE_128x128;
+    }
     if (VITENC_SMALL_TILES && cdiv(M, 128) * cdiv(N, 128) < kCUs / 2) return TILE_64x64;
     if (cdiv(M, 128) * cdiv(N, 128) <= kCUs) return TILE_128x128_DEEP;
     return TILE_128x128;
