@@ -371,11 +371,19 @@ int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32
  * O = softmax(Q K^T / sqrt(hd) + mask) V with Q, K, Vt in the layouts of
  * vitenc_op_qkv_rope; O: T [B, N, H*hd] (heads concatenated).  attn_mode
  * FULL or BLOCK_CAUSAL with frames of `tokens_per_frame` patch tokens after
- * n_prefix prefix tokens. */
+ * n_prefix prefix tokens (0 <= n_prefix < N).  scratch: fp32 device memory
+ * of vitenc_attention_scratch_floats() floats for the prefix rows (their
+ * partial results over runs of keys), NULL when that is 0; contents undefined
+ * on entry and exit. */
 vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt,
                                   int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
                                   int32_t attn_mode, int32_t n_prefix,
-                                  int32_t tokens_per_frame, void *O, void *stream);
+                                  int32_t tokens_per_frame, float *scratch, void *O, void *stream);
+
+/* Floats of scratch vitenc_op_attention needs for these sizes (0 without
+ * prefix rows; -1 for invalid sizes). */
+int64_t vitenc_attention_scratch_floats(int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
+                                        int32_t n_prefix);
 
 /* a8/a10 projection with bias, layer scale and residual: Z[M, Nout] (fp32)
  * += ls * (A[M, K] W[Nout, K]^T + b); ls may be NULL (= 1). */

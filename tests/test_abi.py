@@ -254,8 +254,13 @@ def test_step_entry_point_refusals():
     assert L.vitenc_op_layernorm(9, FAKE, FAKE, FAKE, 1e-6, 4, 64, FAKE, None) == 1
     assert L.vitenc_op_layernorm(0, None, FAKE, FAKE, 1e-6, 4, 64, FAKE, None) == 3
     assert L.vitenc_op_layernorm(0, FAKE, FAKE, FAKE, 1e-6, 4, 5000, FAKE, None) == 6
-    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 48, 0, 0, 0, FAKE, None) == 6
-    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 1, 0, 0, FAKE, None) == 2
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 48, 0, 0, 0, None, FAKE, None) == 6
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 1, 0, 0, None, FAKE, None) == 2
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 0, 64, 0, None, FAKE, None) == 2
+    # prefix rows need the scratch
+    assert L.vitenc_attention_scratch_floats(1, 257, 2, 64, 1) == 2 * 2 * 66
+    assert L.vitenc_attention_scratch_floats(1, 256, 2, 64, 0) == 0
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 257, 2, 64, 0, 1, 0, None, FAKE, None) == 3
     assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 2, 2, 2, 0,
                                 FAKE, FAKE, FAKE, FAKE, None) == 2          # 8 patches + 0 prefix != 17
     assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 8, 64, 1, 1, 2, 2, 2, 0,

@@ -160,6 +160,9 @@ def test_qkv_rope(gpu_lib, dtype, case):
     dict(B=2, H=1, N=4 * 36, hd=64, mode=1, p=0, S=36),
     dict(B=1, H=1, N=1 + 3 * 100, hd=32, mode=1, p=1, S=100),
     dict(B=1, H=1, N=1 + 6 * 4, hd=64, mode=1, p=1, S=4),
+    dict(B=1, H=2, N=257, hd=64, mode=0, p=1, S=0),
+    dict(B=1, H=2, N=1 + 4 * 256, hd=64, mode=1, p=1, S=256),
+    dict(B=2, H=1, N=1 + 33, hd=32, mode=0, p=1, S=0),
 ])
 def test_attention(gpu_lib, dtype, case):
     from vision_transformer_amd import vitenc as V

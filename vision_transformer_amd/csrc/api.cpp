@@ -130,7 +130,7 @@ struct Plan {
     int gt, gh, gw, Np, p, N;
     int64_t M;
     int D, F, nh, hd, K, lda, ldv;
-    size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_rope, off_tok, off_pos, total;
+    size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_rope, off_tok, off_pos, off_attn, total;
     bool resample;
 };
 
@@ -184,6 +184,7 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     pl.off_rope = take((size_t)(pl.gt + pl.gh + pl.gw) * d * 2 * 4);
     pl.off_tok = take((size_t)pl.Np * 4);
     pl.off_pos = pl.resample ? take((size_t)pl.N * pl.D * 4) : 0;
+    pl.off_attn = take((size_t)attention_scratch_floats(B, pl.N, pl.nh, pl.hd, pl.p) * 4);
     pl.total = off;
     return VITENC_OK;
 }
@@ -327,6 +328,7 @@ vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int
     g.rope = hp.rope; g.gt = pl.gt; g.gh = pl.gh; g.gw = pl.gw; g.rope_tab = rope_tab; g.tok_pos = tok_pos;
     BlockBufs bb;
     bb.Z = Z; bb.Y = Y; bb.Q = Q; bb.K = Kb; bb.Vt = Vt; bb.O = O; bb.U = U;
+    bb.attn_scratch = reinterpret_cast<float *>(ws + pl.off_attn);
     int k_hier = 0;
     for (int l = 0; l < hp.n_layer; ++l) {
         const char *what = "block";

@@ -90,8 +90,8 @@ __device__ __forceinline__ void key_interval(int q, int N, int causal, int p, in
 template <typename T, int HD>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                 const T *__restrict__ Vt, int N, int H, int ldv,
-                                                                int causal, int p, int S, float scale_log2,
-                                                                T *__restrict__ O) {
+                                                                int causal, int p, int S, int q_begin,
+                                                                float scale_log2, T *__restrict__ O) {
     constexpr int KPC = Elem<T>::kPerChunk;
     constexpr int QCH = HD / KPC;     // 16-byte chunks per q/k row
     constexpr int KCH = BKV / KPC;    // 16-byte chunks per V^T row of a tile
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
     const int bh = blockIdx.x;                 // item * H + head
     const int b = bh / H, head = bh - b * H;
     const int qt = gridDim.y - 1 - blockIdx.y; // heavy (late-frame) tiles first
-    const int q0 = qt * BQ;
+    const int q0 = q_begin + qt * BQ;
     const int D = H * HD;
 
     const T *Qb = Q + (int64_t)bh * N * HD;
@@ -119,7 +119,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
     const int qrow = q0 + wave * 32 + l32;
     int lo, hi;
     key_interval(min(qrow, N - 1), N, causal, p, S, lo, hi);
-    const int w_lo = wave_min_i(lo), w_hi = wave_max_i(hi);
+    // a wave whose queries all lie past the end (in the last, partial query
+    // tile) takes an empty interval: it joins the tile loads and barriers but
+    // computes nothing
+    const bool live = q0 + wave * 32 < N;
+    const int w_lo = live ? wave_min_i(lo) : N, w_hi = live ? wave_max_i(hi) : 0;
     const int w_full_lo = wave_max_i(lo), w_full_hi = wave_min_i(hi);
 
     // workgroup key range (intervals are monotone in the query index)
@@ -416,8 +420,8 @@ __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 
 template <typename T, int HD, int STAGES, int NWV>
 __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                     const T *__restrict__ Vt, int N, int H, int ldv,
-                                                                    int causal, int p, int S, float scale_log2,
-                                                                    T *__restrict__ O) {
+                                                                    int causal, int p, int S, int q_begin,
+                                                                    float scale_log2, T *__restrict__ O) {
     static_assert(sizeof(T) == 2, "16-bit types");
     constexpr int KPC = 8;
     constexpr int QCH = HD / KPC;              // chunks per K row (8 or 4)
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     const int bh = blockIdx.x;
     const int b = bh / H, head = bh - b * H;
     const int qt = gridDim.y - 1 - blockIdx.y; // heavy (late-frame) tiles first
-    const int q0 = qt * BQL;
+    const int q0 = q_begin + qt * BQL;
     const int D = H * HD;
 
     const T *Qb = Q + (int64_t)bh * N * HD;
@@ -456,7 +460,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     const int qrow = q0 + wave * 32 + l32;
     int lo, hi;
     key_interval(min(qrow, N - 1), N, causal, p, S, lo, hi);
-    const int w_lo = wave_min_i(lo), w_hi = wave_max_i(hi);
+    // a wave whose queries all lie past the end (in the last, partial query
+    // tile) takes an empty interval: it joins the tile loads and barriers but
+    // computes nothing
+    const bool live = q0 + wave * 32 < N;
+    const int w_lo = live ? wave_min_i(lo) : N, w_hi = live ? wave_max_i(hi) : 0;
     const int w_full_lo = wave_max_i(lo), w_full_hi = wave_min_i(hi);
     int wg_lo, wg_hi, tmp;
     key_interval(q0, N, causal, p, S, wg_lo, tmp);
@@ -607,60 +615,197 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     }
 }
 
+// Prefix (CLS) query rows.  They see every key in both masks (the CLS row is
+// open), and a tile of 32*NWV queries holding a single prefix query would
+// cost as much as a full tile, so the tiled kernels start at the first patch
+// query and the prefix rows are computed here, split over the keys: one
+// workgroup per (prefix row, head, run of kPrefixKeys keys) stores the
+// fp32 scores of its keys (16-byte K row loads) in LDS, turns them into
+// weights against the run's own max, and multiplies them into V (each thread
+// one output dim of one key group, 16-byte runs of V^T); the partial
+// (max, sum, o[HD]) goes to scratch, and a second kernel merges the runs of a
+// row in order (online-softmax rescaling).
+constexpr int kPrefixThreads = 256;
+constexpr int kPrefixKeys = 256;
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kPrefixThreads) void prefix_partial_kernel(const T *__restrict__ Q,
+                                                                        const T *__restrict__ K,
+                                                                        const T *__restrict__ Vt, int N, int ldv,
+                                                                        int p, float scale_log2,
+                                                                        float *__restrict__ part) {
+    constexpr int KPC = Elem<T>::kPerChunk;
+    constexpr int NW = kPrefixThreads / 64;
+    constexpr int G = kPrefixThreads / HD;   // key groups of the PV step
+    constexpr int VE = 16 / (int)sizeof(T);  // keys per 16-byte V^T load
+    static_assert(kPrefixKeys <= kPrefixThreads, "one key per thread");
+    __shared__ float ss[kPrefixKeys];
+    __shared__ float sq[HD];
+    __shared__ float red[NW];
+    __shared__ float so[G][HD];
+    const int row = blockIdx.x, bh = row / p, pq = row - bh * p;
+    const int run = blockIdx.y, c0 = run * kPrefixKeys, n = min(kPrefixKeys, N - c0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int d = tid % HD, grp = tid / HD;
+    if (tid < HD) sq[tid] = to_f32(Q[((int64_t)bh * N + pq) * HD + tid]) * scale_log2;
+    __syncthreads();
+    float sc = -INFINITY;
+    if (tid < n) {
+        sc = 0.0f;
+        const T *kr = K + ((int64_t)bh * N + c0 + tid) * HD;
+#pragma unroll
+        for (int c = 0; c < HD / KPC; ++c) {
+            const Chunk ch = load_chunk(kr + c * KPC);
+            const T *e = reinterpret_cast<const T *>(&ch);
+#pragma unroll
+            for (int u = 0; u < KPC; ++u) sc = fmaf(sq[c * KPC + u], to_f32(e[u]), sc);
+        }
+    }
+    const float mw = wave_max(sc);
+    if (lane == 0) red[wave] = mw;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w]);
+    const float wgt = tid < n ? __builtin_amdgcn_exp2f(sc - m) : 0.0f;
+    ss[tid] = wgt;
+    const float lw = wave_sum(wgt);
+    __syncthreads();
+    if (lane == 0) red[wave] = lw;
+    const T *vrow = Vt + ((int64_t)bh * HD + d) * ldv + c0;
+    float acc = 0.0f;
+    const int full = n / VE * VE;
+    for (int k = grp * VE; k < full; k += G * VE) {
+        const Chunk ch = load_chunk(vrow + k);
+        const T *e = reinterpret_cast<const T *>(&ch);
+#pragma unroll
+        for (int u = 0; u < VE; ++u) acc = fmaf(ss[k + u], to_f32(e[u]), acc);
+    }
+    for (int k = full + grp; k < n; k += G) acc = fmaf(ss[k], to_f32(vrow[k]), acc);
+    so[grp][d] = acc;
+    __syncthreads();
+    float *out = part + ((int64_t)row * gridDim.y + run) * (HD + 2);
+    if (tid < HD) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g2 = 0; g2 < G; ++g2) t += so[g2][tid];
+        out[2 + tid] = t;
+    }
+    if (tid == 0) {
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) l += red[w];
+        out[0] = m;
+        out[1] = l;
+    }
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(64) void prefix_merge_kernel(const float *__restrict__ part, int runs, int N, int H,
+                                                          int p, T *__restrict__ O) {
+    const int row = blockIdx.x, bh = row / p, pq = row - bh * p;
+    const int b = bh / H, head = bh - b * H;
+    const float *pr = part + (int64_t)row * runs * (HD + 2);
+    float M = -INFINITY;
+    for (int r = 0; r < runs; ++r) M = fmaxf(M, pr[(int64_t)r * (HD + 2)]);
+    for (int dd = threadIdx.x; dd < HD; dd += blockDim.x) {
+        float L = 0.0f, acc = 0.0f;
+        for (int r = 0; r < runs; ++r) {
+            const float *q = pr + (int64_t)r * (HD + 2);
+            const float f = __builtin_amdgcn_exp2f(q[0] - M);
+            L = fmaf(q[1], f, L);
+            acc = fmaf(q[2 + dd], f, acc);
+        }
+        O[((int64_t)b * N + pq) * H * HD + head * HD + dd] = from_f32<T>(L > 0.0f ? acc / L : 0.0f);
+    }
+}
+
+// the first query row the tiled kernels cover: the prefix rows go to
+// prefix_attention_kernel (all of them: a model has at most a few)
+inline int query_begin(int N, int p) { return p < N ? p : 0; }
+
+template <typename T, int HD>
+hipError_t launch_prefix(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int qb,
+                         float scale_log2, float *scratch, void *O, hipStream_t s) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || qb == 0) return e;
+    if (!scratch) return hipErrorInvalidValue;
+    const int runs = (int)cdiv(N, kPrefixKeys), rows = B * H * qb;
+    hipLaunchKernelGGL((prefix_partial_kernel<T, HD>), dim3((unsigned)rows, (unsigned)runs), dim3(kPrefixThreads), 0,
+                       s, reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
+                       reinterpret_cast<const T *>(Vt), N, ldv, qb, scale_log2, scratch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((prefix_merge_kernel<T, HD>), dim3((unsigned)rows), dim3(64), 0, s, scratch, runs, N, H, qb,
+                       reinterpret_cast<T *>(O));
+    return hipGetLastError();
+}
+
 // 16-bit types: the direct-to-LDS kernel; fp32: the register-staged one
 template <typename T, int HD>
 hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal, int p,
-                    int S, void *O, hipStream_t s) {
+                    int S, float *scratch, void *O, hipStream_t s) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
     // hd 32 tiles are too small to split their loads over more than 4 waves
     constexpr int NWV = HD == 64 ? kLdsWaves : 4;
-    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, 32 * NWV));
+    const int qb = query_begin(N, p);
+    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, 32 * NWV));
     hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV>), grid, dim3(64 * NWV), 0, s,
                        reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
-                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, scale_log2, reinterpret_cast<T *>(O));
-    return hipGetLastError();
+                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2,
+                       reinterpret_cast<T *>(O));
+    return launch_prefix<T, HD>(Q, K, Vt, B, N, H, ldv, qb, scale_log2, scratch, O, s);
 }
 
 template <>
 hipError_t launch_t<float, 64>(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal,
-                               int p, int S, void *O, hipStream_t s) {
-    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, BQ));
+                               int p, int S, float *scratch, void *O, hipStream_t s) {
+    const int qb = query_begin(N, p);
+    const float scale_log2 = 1.4426950408889634f / 8.0f;
+    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, BQ));
     hipLaunchKernelGGL((attention_kernel<float, 64>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
                        reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
-                       S, 1.4426950408889634f / 8.0f, reinterpret_cast<float *>(O));
-    return hipGetLastError();
+                       S, qb, scale_log2, reinterpret_cast<float *>(O));
+    return launch_prefix<float, 64>(Q, K, Vt, B, N, H, ldv, qb, scale_log2, scratch, O, s);
 }
 
 template <>
 hipError_t launch_t<float, 32>(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int causal,
-                               int p, int S, void *O, hipStream_t s) {
-    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N, BQ));
+                               int p, int S, float *scratch, void *O, hipStream_t s) {
+    const int qb = query_begin(N, p);
+    const float scale_log2 = 1.4426950408889634f / sqrtf(32.0f);
+    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, BQ));
     hipLaunchKernelGGL((attention_kernel<float, 32>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
                        reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
-                       S, 1.4426950408889634f / sqrtf(32.0f), reinterpret_cast<float *>(O));
-    return hipGetLastError();
+                       S, qb, scale_log2, reinterpret_cast<float *>(O));
+    return launch_prefix<float, 32>(Q, K, Vt, B, N, H, ldv, qb, scale_log2, scratch, O, s);
 }
 
 template <typename T>
 hipError_t launch_hd(int head_dim, const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv,
-                     int causal, int p, int S, void *O, hipStream_t s) {
-    if (head_dim == 64) return launch_t<T, 64>(Q, K, Vt, B, N, H, ldv, causal, p, S, O, s);
-    if (head_dim == 32) return launch_t<T, 32>(Q, K, Vt, B, N, H, ldv, causal, p, S, O, s);
+                     int causal, int p, int S, float *scratch, void *O, hipStream_t s) {
+    if (head_dim == 64) return launch_t<T, 64>(Q, K, Vt, B, N, H, ldv, causal, p, S, scratch, O, s);
+    if (head_dim == 32) return launch_t<T, 32>(Q, K, Vt, B, N, H, ldv, causal, p, S, scratch, O, s);
     return hipErrorInvalidValue;
 }
 
 } // namespace
 
+int64_t attention_scratch_floats(int B, int N, int H, int head_dim, int n_prefix) {
+    const int qb = query_begin(N, n_prefix);
+    return (int64_t)B * H * qb * cdiv(N, kPrefixKeys) * (head_dim + 2);
+}
+
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N, int H,
-                            int head_dim, int ldv, int attn_mode, int n_prefix, int tokens_per_frame, void *O,
-                            hipStream_t s) {
+                            int head_dim, int ldv, int attn_mode, int n_prefix, int tokens_per_frame,
+                            float *scratch, void *O, hipStream_t s) {
     if (B <= 0 || N <= 0) return hipSuccess;
     const int causal = attn_mode == 1;
     const int S = tokens_per_frame > 0 ? tokens_per_frame : 1;
     switch (dtype) {
-    case DT_F32: return launch_hd<float>(head_dim, Q, K, Vt, B, N, H, ldv, causal, n_prefix, S, O, s);
-    case DT_BF16: return launch_hd<bf16_t>(head_dim, Q, K, Vt, B, N, H, ldv, causal, n_prefix, S, O, s);
-    case DT_F16: return launch_hd<f16_t>(head_dim, Q, K, Vt, B, N, H, ldv, causal, n_prefix, S, O, s);
+    case DT_F32: return launch_hd<float>(head_dim, Q, K, Vt, B, N, H, ldv, causal, n_prefix, S, scratch, O, s);
+    case DT_BF16: return launch_hd<bf16_t>(head_dim, Q, K, Vt, B, N, H, ldv, causal, n_prefix, S, scratch, O, s);
+    case DT_F16: return launch_hd<f16_t>(head_dim, Q, K, Vt, B, N, H, ldv, causal, n_prefix, S, scratch, O, s);
     }
     return hipErrorInvalidValue;
 }

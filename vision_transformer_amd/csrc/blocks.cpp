@@ -32,7 +32,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         STEP(launch_gemm(g.dtype, EPI_QKV, b.Y, D, w.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
     }
     STEP(launch_attention(g.dtype, b.Q, b.K, b.Vt, g.B, g.N, g.n_head, g.head_dim, g.ldv, g.attn_mode, g.prefix,
-                          g.tokens_per_frame, b.O, s),
+                          g.tokens_per_frame, b.attn_scratch, b.O, s),
          "attention");
     {
         EpiArgs ep;

@@ -117,9 +117,12 @@ int xattn_chunks(int N);
 hipError_t launch_xattn_pool(const float *Z, const float2 *stats, const float *w, int B, int N, int D, int H,
                              const float *ln_w, const float *ln_b, float *P, float *ybar, hipStream_t st);
 
+// scratch: fp32, attention_scratch_floats(...) floats (the prefix rows' partial
+// results); may be NULL when n_prefix is 0
+int64_t attention_scratch_floats(int B, int N, int H, int head_dim, int n_prefix);
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N,
                             int H, int head_dim, int ldv, int attn_mode, int n_prefix,
-                            int tokens_per_frame, void *O, hipStream_t s);
+                            int tokens_per_frame, float *scratch, void *O, hipStream_t s);
 
 hipError_t launch_pool(const float *X, int B, int N, int D, int cls, int n_prefix, float *pooled,
                        hipStream_t s);
@@ -139,6 +142,7 @@ struct BlockGeom {
 struct BlockBufs {
     float *Z = nullptr;              // fp32 [B*N, D]
     void *Y = nullptr, *Q = nullptr, *K = nullptr, *Vt = nullptr, *O = nullptr, *U = nullptr;
+    float *attn_scratch = nullptr;   // attention_scratch_floats(...) floats when prefix > 0
 };
 // *what names the failing launch
 hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_weights &w, hipStream_t s,

@@ -135,18 +135,25 @@ vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w
     return op_dev(launch_gemm(dtype, EPI_QKV, Y, D, qkv_w, D, B * N, 3 * D, D, ep, s), "qkv GEMM");
 }
 
+int64_t vitenc_attention_scratch_floats(int32_t B, int32_t N, int32_t n_head, int32_t head_dim, int32_t n_prefix) {
+    if (B <= 0 || N <= 0 || n_head <= 0 || head_dim <= 0 || n_prefix < 0 || n_prefix > N) return -1;
+    return attention_scratch_floats(B, N, n_head, head_dim, n_prefix);
+}
+
 vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt, int32_t B, int32_t N,
                                   int32_t n_head, int32_t head_dim, int32_t attn_mode, int32_t n_prefix,
-                                  int32_t tokens_per_frame, void *O, void *stream) {
+                                  int32_t tokens_per_frame, float *scratch, void *O, void *stream) {
     clear_error();
     if (!dtype_ok(dtype)) return op_fail(VITENC_EINVAL, "unknown dtype %d", dtype);
     if (!Q || !K || !Vt || !O) return op_fail(VITENC_ENULL, "a required pointer is NULL");
     if (B <= 0 || N <= 0 || n_head <= 0) return op_fail(VITENC_ESHAPE, "bad sizes");
     if (head_dim != 64 && head_dim != 32) return op_fail(VITENC_EUNSUPPORTED, "head_dim %d", head_dim);
-    if (attn_mode == 1 && (tokens_per_frame <= 0 || n_prefix < 0 || n_prefix >= N))
-        return op_fail(VITENC_ESHAPE, "block-causal geometry");
+    if (n_prefix < 0 || n_prefix >= N) return op_fail(VITENC_ESHAPE, "n_prefix %d outside [0, N)", n_prefix);
+    if (attn_mode == 1 && tokens_per_frame <= 0) return op_fail(VITENC_ESHAPE, "block-causal geometry");
+    if (attention_scratch_floats(B, N, n_head, head_dim, n_prefix) > 0 && !scratch)
+        return op_fail(VITENC_ENULL, "scratch is NULL but the prefix rows need it");
     return op_dev(launch_attention(dtype, Q, K, Vt, B, N, n_head, head_dim, (N + 63) / 64 * 64, attn_mode, n_prefix,
-                                   tokens_per_frame, O, reinterpret_cast<hipStream_t>(stream)),
+                                   tokens_per_frame, scratch, O, reinterpret_cast<hipStream_t>(stream)),
                   "attention");
 }
 

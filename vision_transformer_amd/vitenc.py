@@ -97,7 +97,8 @@ SIGNATURES = {
     "vitenc_op_qkv_rope": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 9 + [c_vp] * 5),
     "vitenc_rope_table_floats": (ctypes.c_int64, [c_i32] * 4),
     "vitenc_op_pos_resample": (c_i32, [c_vp] + [c_i32] * 9 + [c_vp, c_vp]),
-    "vitenc_op_attention": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp]),
+    "vitenc_op_attention": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp, c_vp]),
+    "vitenc_attention_scratch_floats": (ctypes.c_int64, [c_i32] * 5),
     "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_linear_gelu": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_pool": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
@@ -532,12 +533,18 @@ def op_pos_resample(pos, prefix, src_grid, dst_grid, mode, stream=None, out=None
     return out
 
 
-def op_attention(dtype, Q, K, Vt, attn_mode=0, n_prefix=0, tokens_per_frame=0, stream=None, out=None):
+def op_attention(dtype, Q, K, Vt, attn_mode=0, n_prefix=0, tokens_per_frame=0, stream=None, out=None,
+                 scratch=None):
+    """scratch: None (allocated here when the prefix rows need it) or fp32
+    with at least vitenc_attention_scratch_floats() elements."""
     import torch
     B, H, N, hd = Q.shape
     O = torch.empty((B, N, H * hd), dtype=torch_dtype(dtype), device=Q.device) if out is None else out
+    nf = lib().vitenc_attention_scratch_floats(B, N, H, hd, n_prefix)
+    if scratch is None and nf > 0:
+        scratch = torch.empty(nf, dtype=torch.float32, device=Q.device)
     check(lib().vitenc_op_attention(dtype, Q.data_ptr(), K.data_ptr(), Vt.data_ptr(), B, N, H, hd, attn_mode,
-                                    n_prefix, tokens_per_frame, O.data_ptr(), _stream(stream)))
+                                    n_prefix, tokens_per_frame, _ptr(scratch), O.data_ptr(), _stream(stream)))
     return O
 
 
