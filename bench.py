@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="replay the step as a captured HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--only", metavar="KERNEL", default=None,
+                    help="launch only this kernel of the encoder layer (a kernel-breakdown name) --kernel-reps "
+                         "times at the headline shape and exit (for counter runs)")
     ap.add_argument("--part", choices=("all", "encoder", "predictor", "head", "variants", "configs"), default="all",
                     help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
                          "head (reported in the line's `predictor` / `head` objects), or all three")
@@ -160,7 +163,7 @@ def read_traffic(dominant, workload):
     return total
 
 
-def kernel_breakdown(cfg, enc, reps, stream, busy):
+def kernel_breakdown(cfg, enc, reps, stream, busy, only=None):
     """The kernels of one encoder layer, launched in encode's order through
     their C-ABI entry points at the encode shapes, each bracketed by a pair of
     HIP events on `stream`.  Repetition r uses the weights of layer r mod L,
@@ -217,6 +220,13 @@ def kernel_breakdown(cfg, enc, reps, stream, busy):
         ]
 
     seqs = [layer(enc.blocks[r % len(enc.blocks)]) for r in range(reps)]
+    if only is not None:
+        for seq in seqs:
+            for name, fn in seq:
+                if name == only:
+                    fn()
+        torch.cuda.synchronize()
+        return {}
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in seq] for seq in seqs]
     first, last = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     busy()
@@ -614,6 +624,10 @@ def main():
     log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
     wl = W.make_workload(cfg)
     enc = V.Encoder.from_workload(wl)
+    if args.only:
+        kernel_breakdown(cfg, enc, args.kernel_reps, stream, lambda: None, only=args.only)
+        print(json.dumps({"only": args.only, "launches": args.kernel_reps}), flush=True)
+        return
     px = torch.from_numpy(wl.pixels).cuda()
     ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
 
