@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VITENC_ABI_VERSION 2
+#define VITENC_ABI_VERSION 3
 
 typedef enum {
     VITENC_OK = 0,
@@ -60,6 +60,7 @@ enum { VITENC_POS_INTERP_NONE = 0, VITENC_POS_INTERP_BICUBIC = 1,
 enum { VITENC_ROPE_NONE = 0, VITENC_ROPE_3D = 1 };                    /* rope */
 enum { VITENC_ROPE_TILED = 0, VITENC_ROPE_INTERLEAVED = 1 };          /* rope_layout */
 enum { VITENC_ATTN_FULL = 0, VITENC_ATTN_BLOCK_CAUSAL = 1 };          /* attn_mode */
+enum { VITENC_WEIGHTS_PLAIN = 0, VITENC_WEIGHTS_MXFP8 = 1 };          /* weight_format */
 
 /* Encoder hyperparameters (jepa.cpp "GGUF schema (v1)", "Encoder (jepa.enc.*)").
  *  embed_dim D, n_layer L, n_head H (head_dim = D / H), ffn_dim F,
@@ -90,7 +91,14 @@ enum { VITENC_ATTN_FULL = 0, VITENC_ATTN_BLOCK_CAUSAL = 1 };          /* attn_mo
  *  n_hier, hier_layers: hierarchical outputs ("GGUF schema (v1)",
  *    jepa.enc.hier_layers / enc.hier_norm.{k}): output k is the residual
  *    stream after block hier_layers[k] through its own norm k; the layer ids
- *    strictly increase within [0, n_layer); at most VITENC_MAX_HIER. */
+ *    strictly increase within [0, n_layer); at most VITENC_MAX_HIER.
+ *  weight_format MXFP8: the four block matrices (qkv, out, up, down) are
+ *    stored in 8 bits ("GGUF schema (v1)", "Quantization rules": the
+ *    attention and FFN matrices are the quantised ones, everything else keeps
+ *    its type): every 32 consecutive weights of a row share a power-of-two
+ *    scale and each weight is an E4M3 code; see vitenc_quantize_mxfp8 for
+ *    the exact format.  Needs dtype BF16 and embed_dim, ffn_dim multiples of
+ *    64; the GEMMs expand the codes to bf16 exactly and run as in BF16. */
 typedef struct {
     int32_t embed_dim, n_layer, n_head, ffn_dim;
     int32_t patch_size, tubelet_size, in_chans;
@@ -102,13 +110,18 @@ typedef struct {
     int32_t pos_interp, pos_grid_t, pos_grid_h, pos_grid_w;
     int32_t image_patch_embed;
     int32_t n_hier, hier_layers[VITENC_MAX_HIER];
+    int32_t weight_format;
 } vitenc_hparams;
 
 /* One encoder block ("GGUF schema (v1)", "Encoder tensors", enc.blk.{i}.*).
  * Matrices in the model dtype: qkv_w [3D, D] with rows [q; k; v] and head h
  * at rows [h*hd, (h+1)*hd) of each block; out_w [D, D]; up_w [F, D];
  * down_w [D, F].  fp32 vectors: ln1_w/b, ln2_w/b [D], qkv_b [3D], out_b [D],
- * up_b [F], down_b [D]; ls1/ls2 [D] required iff layer_scale, else ignored. */
+ * up_b [F], down_b [D]; ls1/ls2 [D] required iff layer_scale, else ignored.
+ * With weight_format MXFP8 the four matrices hold E4M3 codes (one byte per
+ * weight, same shapes, 16-byte aligned) and qkv_s, out_s, up_s, down_s their
+ * block scales as written by vitenc_quantize_mxfp8; otherwise the *_s
+ * pointers are ignored (and the predictor and head never read them). */
 typedef struct {
     const float *ln1_w, *ln1_b;
     const void *qkv_w;   const float *qkv_b;
@@ -117,6 +130,7 @@ typedef struct {
     const void *up_w;    const float *up_b;
     const void *down_w;  const float *down_b;
     const float *ls1, *ls2;
+    const uint8_t *qkv_s, *out_s, *up_s, *down_s;
 } vitenc_block_weights;
 
 /* Encoder weights.  patch_w [D, C*t*P*P] (the strided convolution flattened in
@@ -309,6 +323,23 @@ vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int
                                  int32_t H, int32_t W, void *workspace, size_t ws_bytes,
                                  float *out_tokens, float *out_pooled, float *out_hier, void *stream);
 
+/* The 8-bit block weight format of weight_format MXFP8 (the quantised
+ * matrices of "GGUF schema (v1)", "Quantization rules", whose q8_0 blocks are
+ * 32 consecutive weights of a row sharing one scale).  w: fp32 [rows, cols]
+ * (finite values), cols % 64 == 0.  For the block j of row r (weights
+ * [32j, 32j+32)) with largest magnitude amax the scale is 2^e, e the smallest
+ * integer with amax <= 448 * 2^e, clamped to [-117, 117] (an all-zero block:
+ * -117), and each weight becomes the E4M3 code (sign, 4 exponent bits of bias
+ * 7, 3 mantissa bits; exponent field 0: subnormals m/8 * 2^-6; largest 448)
+ * nearest to w / 2^e, ties to the even mantissa, sign bit = sign of w.  The
+ * weight the GEMMs use is code * 2^e, exact in bf16.
+ * codes: uint8 [rows, cols]; scales: uint8 [cols/64][rows][2], the byte
+ * e + 127 of block j of row r at ((j/2)*rows + r)*2 + j%2 (rows*cols/32
+ * bytes).  w and codes 16-byte aligned.  Refusals: ENULL, ESHAPE (sizes),
+ * EINVAL (alignment). */
+vitenc_status vitenc_quantize_mxfp8(const float *w, int32_t rows, int32_t cols, uint8_t *codes,
+                                    uint8_t *scales, void *stream);
+
 /* Thread-local text of the last refusal on this thread ("" if none). */
 const char *vitenc_error_text(void);
 int32_t vitenc_abi_version(void);
@@ -394,6 +425,15 @@ vitenc_status vitenc_op_linear_residual(int32_t dtype, const void *A, const void
 /* a9 U[M, Nout] (T) = GELU_erf(A[M, K] W[Nout, K]^T + b). */
 vitenc_status vitenc_op_linear_gelu(int32_t dtype, const void *A, const void *W, const float *b,
                                     int32_t M, int32_t Nout, int32_t K, void *U, void *stream);
+
+/* a8-a10 with 8-bit weights: the projections of vitenc_op_linear_residual
+ * (epi 0: Z fp32 [M, Nout] += ls * (A W^T + b)) and vitenc_op_linear_gelu
+ * (epi 1: U bf16 [M, Nout] = GELU_erf(A W^T + b)) with A bf16 [M, K] and W
+ * given as codes [Nout, K] and scales in the format of vitenc_quantize_mxfp8
+ * (K % 64 == 0, Nout % 8 == 0, A and codes 16-byte aligned); out is Z or U. */
+vitenc_status vitenc_op_linear_mxfp8(int32_t epi, const void *A, const uint8_t *codes,
+                                     const uint8_t *scales, const float *b, const float *ls,
+                                     int32_t M, int32_t Nout, int32_t K, void *out, void *stream);
 
 /* Position table resampling (the step encode runs for an off-grid input):
  * out [prefix + dt*dh*dw, D] = pos [prefix + st*sh*sw, D] resampled from grid

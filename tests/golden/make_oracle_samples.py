@@ -1,7 +1,10 @@
 """Writes the oracle's full-depth outputs of the five encoder workloads at
-sampled token rows (plus the pooled feature) to tests/golden/oracle_<name>.npz.
+sampled token rows (plus the pooled feature) to tests/golden/oracle_<name>.npz,
+and those of the ViT-L/16 image workload with its block matrices in the 8-bit
+block format (items 0 and 7, quantised by oracle/quant.py) to
+tests/golden/oracle_<name>_mxfp8.npz.
 
-    python tests/golden/make_oracle_samples.py [name ...]
+    python tests/golden/make_oracle_samples.py [name ...]   (name_mxfp8 for the latter)
 
 Calls only oracle/ and the seeded workload generator; nothing here comes from
 the GPU path.  The full forwards take from seconds (ViT-Ti) to most of an
@@ -48,6 +51,19 @@ def main(names):
         np.savez_compressed(path, rows=rows, tokens=out[:, rows].astype(np.float64), pooled=pooled,
                             n_layer=cfg.n_layer, seed=cfg.seed)
         print(f"{cfg.name}: {time.time() - t0:.1f} s -> {path}", flush=True)
+    cfg = W.CONFIGS[1].replace(weight_format=W.WEIGHTS_MXFP8)
+    name = cfg.name + "_mxfp8"
+    if not names or name in names:
+        t0 = time.time()
+        wl = W.make_workload(cfg)
+        items = [0, 7]
+        w = oracle.quant.dequantized_weights(wl.weights)
+        out, pooled = oracle.encoder_forward(cfg.replace(batch=len(items)), w, wl.pixels[items])
+        rows = sample_rows(cfg)
+        path = os.path.join(HERE, f"oracle_{name}.npz")
+        np.savez_compressed(path, items=np.array(items), rows=rows, tokens=out[:, rows].astype(np.float64),
+                            pooled=pooled, n_layer=cfg.n_layer, seed=cfg.seed)
+        print(f"{name}: {time.time() - t0:.1f} s -> {path}", flush=True)
 
 
 if __name__ == "__main__":

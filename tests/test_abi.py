@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(V.SIGNATURES), "binding and header disagree"
-    assert L.vitenc_abi_version() == 2
+    assert L.vitenc_abi_version() == 3
 
 
 FAKE = 0x1000  # a non-NULL pointer that is never dereferenced: creation only validates
@@ -287,3 +287,48 @@ def test_error_text_is_thread_local(model):
     t.start(); t.join()
     assert seen["text"] == ""
     assert "non-positive" in _text()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(weight_format=2), 1, "weight_format"),
+    (dict(weight_format=1, dtype=0), 6, "BF16"),
+    (dict(weight_format=1, dtype=2), 6, "BF16"),
+    (dict(weight_format=1, ffn_dim=4000), 1, "multiples of 64"),
+])
+def test_weight_format_refusals(kw, status, needle):
+    w, _keep = _weights(24)
+    st, h = _create(_hp(**kw), w)
+    assert st == status and needle in _text(), _text()
+
+
+def test_8bit_block_scales_and_alignment_required():
+    w, bw = _weights(24)
+    st, h = _create(_hp(weight_format=1), w)
+    assert st == 0, _text()
+    V.lib().vitenc_model_destroy(h)
+    bw[3].up_s = None
+    st, _ = _create(_hp(weight_format=1), w)
+    assert st == 3 and "block 3" in _text() and "scale" in _text()
+    bw[3].up_s = FAKE
+    bw[5].down_w = FAKE + 8
+    st, _ = _create(_hp(weight_format=1), w)
+    assert st == 1 and "block 5" in _text() and "16-byte" in _text()
+    # plain weights ignore the scale pointers
+    bw[5].down_w = FAKE
+    bw[0].qkv_s = None
+    st, h = _create(_hp(), w)
+    assert st == 0
+    V.lib().vitenc_model_destroy(h)
+
+
+def test_8bit_entry_point_refusals():
+    L = V.lib()
+    assert L.vitenc_quantize_mxfp8(None, 8, 64, FAKE, FAKE, None) == 3
+    assert L.vitenc_quantize_mxfp8(FAKE, 8, 96, FAKE, FAKE, None) == 2 and "64" in _text()
+    assert L.vitenc_quantize_mxfp8(FAKE, 0, 64, FAKE, FAKE, None) == 2
+    assert L.vitenc_quantize_mxfp8(FAKE + 4, 8, 64, FAKE, FAKE, None) == 1 and "aligned" in _text()
+    assert L.vitenc_op_linear_mxfp8(2, FAKE, FAKE, FAKE, FAKE, None, 4, 8, 64, FAKE, None) == 1
+    assert L.vitenc_op_linear_mxfp8(0, FAKE, FAKE, None, FAKE, None, 4, 8, 64, FAKE, None) == 3
+    assert L.vitenc_op_linear_mxfp8(0, FAKE, FAKE, FAKE, FAKE, None, 4, 8, 96, FAKE, None) == 2
+    assert L.vitenc_op_linear_mxfp8(1, FAKE, FAKE, FAKE, FAKE, None, 4, 12, 64, FAKE, None) == 2
+    assert L.vitenc_op_linear_mxfp8(1, FAKE + 2, FAKE, FAKE, FAKE, None, 4, 8, 64, FAKE, None) == 1

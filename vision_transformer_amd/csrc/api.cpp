@@ -116,6 +116,14 @@ vitenc_status validate_hparams(const vitenc_hparams *hp) {
             return fail(VITENC_EINVAL, "hier_layers must strictly increase within [0, n_layer): entry %d is %d", k,
                         hp->hier_layers[k]);
     }
+    if (hp->weight_format != VITENC_WEIGHTS_PLAIN && hp->weight_format != VITENC_WEIGHTS_MXFP8)
+        return fail(VITENC_EINVAL, "unknown weight_format %d", hp->weight_format);
+    if (hp->weight_format == VITENC_WEIGHTS_MXFP8) {
+        if (hp->dtype != VITENC_BF16) return fail(VITENC_EUNSUPPORTED, "8-bit weights run with dtype BF16 only");
+        if (hp->embed_dim % 64 || hp->ffn_dim % 64)
+            return fail(VITENC_EINVAL, "8-bit weights need embed_dim and ffn_dim multiples of 64 (got %d, %d)",
+                        hp->embed_dim, hp->ffn_dim);
+    }
     if (hd != 64 && hd != 32)
         return fail(VITENC_EUNSUPPORTED, "head_dim %d: the attention kernel implements 64 and 32", hd);
     if (hp->embed_dim > kMaxEmbed)
@@ -223,6 +231,13 @@ vitenc_status vitenc_model_create(const vitenc_hparams *hp, const vitenc_weights
         for (const void *p : req)
             if (!p) return fail(VITENC_ENULL, "block %d: a required tensor is NULL", i);
         if (hp->layer_scale && (!b.ls1 || !b.ls2)) return fail(VITENC_ENULL, "block %d: ls1 / ls2 is NULL", i);
+        if (hp->weight_format == VITENC_WEIGHTS_MXFP8) {
+            if (!b.qkv_s || !b.out_s || !b.up_s || !b.down_s)
+                return fail(VITENC_ENULL, "block %d: a block scale pointer is NULL (8-bit weights)", i);
+            for (const void *c : {b.qkv_w, b.out_w, b.up_w, b.down_w})
+                if (reinterpret_cast<uintptr_t>(c) % 16)
+                    return fail(VITENC_EINVAL, "block %d: 8-bit weight codes must be 16-byte aligned", i);
+        }
     }
     if (hp->image_patch_embed) {
         if (!w->patch_img_w || !w->patch_img_b) return fail(VITENC_ENULL, "patch_img_w / patch_img_b is NULL");
@@ -324,6 +339,7 @@ vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int
     BlockGeom g;
     g.dtype = dt; g.B = B; g.N = pl.N; g.D = D; g.F = F; g.n_head = pl.nh; g.head_dim = pl.hd; g.ldv = pl.ldv;
     g.prefix = pl.p; g.attn_mode = hp.attn_mode; g.tokens_per_frame = pl.gh * pl.gw; g.layer_scale = hp.layer_scale;
+    g.wq = hp.weight_format == VITENC_WEIGHTS_MXFP8;
     g.eps = hp.ln_eps;
     g.rope = hp.rope; g.gt = pl.gt; g.gh = pl.gh; g.gw = pl.gw; g.rope_tab = rope_tab; g.tok_pos = tok_pos;
     BlockBufs bb;

@@ -1,6 +1,8 @@
 // The launch sequence of one pre-LN block (jepa.cpp "Architecture", "The
 // shared ViT graph"):  x += ls1 * out(attn(rope(qkv(ln1(x)))));
 // x += ls2 * down(gelu(up(ln2(x)))).  Shared by the encoder and the predictor.
+// With g.wq the four matrices are 8-bit codes whose block scales come from
+// the block weights' *_s pointers (the GEMM expands them to bf16 exactly).
 #include "launch.h"
 
 namespace vitenc {
@@ -29,6 +31,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.rope_tab = g.rope_tab; ep.tok_pos = g.tok_pos; ep.tok_pos_stride = g.tok_pos_stride;
         ep.rope_tab_pairs = (g.gt + g.gh + g.gw) * ep.d_rot;
         ep.gt = g.gt; ep.gh = g.gh;
+        if (g.wq) ep.wscale = w.qkv_s;
         STEP(launch_gemm(g.dtype, EPI_QKV, b.Y, D, w.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
     }
     STEP(launch_attention(g.dtype, b.Q, b.K, b.Vt, g.B, g.N, g.n_head, g.head_dim, g.ldv, g.attn_mode, g.prefix,
@@ -38,18 +41,21 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         EpiArgs ep;
         ep.bias = w.out_b; ep.Z = b.Z; ep.ldz = D;
         ep.ls = g.layer_scale ? w.ls1 : nullptr;
+        if (g.wq) ep.wscale = w.out_s;
         STEP(launch_gemm(g.dtype, EPI_RESID, b.O, D, w.out_w, D, M, D, D, ep, s), "out GEMM");
     }
     STEP(launch_layernorm(g.dtype, b.Z, w.ln2_w, w.ln2_b, g.eps, M, D, b.Y, s), "ln2");
     {
         EpiArgs ep;
         ep.bias = w.up_b; ep.out = b.U; ep.ldo = F;
+        if (g.wq) ep.wscale = w.up_s;
         STEP(launch_gemm(g.dtype, EPI_GELU, b.Y, D, w.up_w, D, M, F, D, ep, s), "up GEMM");
     }
     {
         EpiArgs ep;
         ep.bias = w.down_b; ep.Z = b.Z; ep.ldz = D;
         ep.ls = g.layer_scale ? w.ls2 : nullptr;
+        if (g.wq) ep.wscale = w.down_s;
         STEP(launch_gemm(g.dtype, EPI_RESID, b.U, F, w.down_w, F, M, D, F, ep, s), "down GEMM");
     }
 #undef STEP

@@ -543,11 +543,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 // output columns and stages them into LDS with 16-byte writes.
 constexpr bool kSwap = VITENC_GEMM_SWAP;
 
-template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI>
+//
+// WQ (8-bit weights, bf16 activations): W holds one E4M3 byte per weight and
+// every 32 weights of a row share a power-of-two scale (EpiArgs::wscale).  A
+// weight row of the slab is then NCH/2 chunks; each lane reads the 16 codes
+// of its row for k in [32t + 16g, 32t + 16g + 16) (t: the 32-weight block of
+// the slab, g = lane / 32) and expands 8 of them per MFMA k-step into bf16
+// with the scaled conversion, which multiplies by the block's 2^e exactly.
+// The activation chunk of a step is picked to hold the same k indices (chunk
+// 4t + 2g + h at step 2t + h).  The scale bytes of a slab (2 per weight row,
+// contiguous over the rows in the [K/64][N][2] layout) come along with it:
+// wave 0 issues one more direct-to-LDS load per slab.
+template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI, bool WQ>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
-                                                                     const T *__restrict__ W, int64_t ldw, int M,
+                                                                     const void *__restrict__ W, int64_t ldw, int M,
                                                                      int N, int K, int tiles_n, int a_bytes,
-                                                                     int b_bytes, EpiArgs ep) {
+                                                                     int b_bytes, int s_bytes, EpiArgs ep) {
     constexpr int KPC = Elem<T>::kPerChunk;
     constexpr int BK = NCH * KPC;
     constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -556,13 +567,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     using AccT = typename std::conditional<MI == 32, f32x16, f32x4>::type;
     constexpr int NV = MI == 32 ? 16 : 4;
     constexpr int RPI = 64 / NCH;                       // slab rows per load instruction
-    constexpr int AI = BM / (RPI * NW), BI = BN / (RPI * NW); // load instructions per wave and slab
-    constexpr int SROWS = BM + BN;                      // LDS rows per stage
+    constexpr int WCH = WQ ? NCH / 2 : NCH;             // chunks per weight row of a slab
+    constexpr int RPW = 64 / WCH;                       // weight rows per load instruction
+    constexpr int AI = BM / (RPI * NW), BI = BN / (RPW * NW); // load instructions per wave and slab
+    constexpr int SC_CH = WQ ? 64 : 0;                  // scale bytes of a slab: one 1 KB load
+    constexpr int STAGE_CH = BM * NCH + BN * WCH + SC_CH; // chunks per LDS stage
     static_assert(NCH == 4 || NCH == 8, "slab of 64 or 128 bytes per row");
-    static_assert(WM % MI == 0 && WN % MI == 0 && AI * RPI * NW == BM && BI * RPI * NW == BN, "tile");
+    static_assert(WM % MI == 0 && WN % MI == 0 && AI * RPI * NW == BM && BI * RPW * NW == BN, "tile");
     static_assert(MI == 32 || MI == 16, "MFMA tile");
+    static_assert(!WQ || (std::is_same<T, bf16_t>::value && MI == 32 && NCH == 8 && 2 * BN <= 1024),
+                  "8-bit weights: bf16 activations, 32x32 MFMAs, 64-k slabs");
 
-    __shared__ Chunk lds[STAGES][SROWS][NCH];
+    __shared__ Chunk lds[STAGES * STAGE_CH];
+    auto lA = [&](int stage, int r, int c) -> Chunk & { return lds[stage * STAGE_CH + r * NCH + c]; };
+    auto lW = [&](int stage, int r, int c) -> Chunk & { return lds[stage * STAGE_CH + BM * NCH + r * WCH + c]; };
+    auto lS = [&](int stage) { return reinterpret_cast<const uint16_t *>(&lds[stage * STAGE_CH + BM * NCH + BN * WCH]); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
@@ -579,30 +598,42 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     // its parity (8-chunk rows), or not at (4-chunk rows), so two lane
     // offsets cover every instruction.
     constexpr uint32_t ES = sizeof(T);
+    constexpr uint32_t WES = WQ ? 1 : sizeof(T); // bytes per weight
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)W, 0, b_bytes, 0x00020000);
     const int lrow = lane / NCH, lch = lane % NCH;
     const int sw0 = swz<NCH>(lrow), sw1 = swz<NCH>(lrow + RPI); // row parity 0 / 1 of 8-row blocks
     const uint32_t va0 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw0) * KPC) * ES);
     const uint32_t va1 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw1) * KPC) * ES);
-    const uint32_t vb0 = (uint32_t)(((int64_t)(n0 + wave * BI * RPI + lrow) * ldw + (lch ^ sw0) * KPC) * ES);
-    const uint32_t vb1 = (uint32_t)(((int64_t)(n0 + wave * BI * RPI + lrow) * ldw + (lch ^ sw1) * KPC) * ES);
+    const int wrow = lane / WCH, wch = lane % WCH;
+    const int ws0 = swz<WCH>(wrow), ws1 = swz<WCH>(wrow + RPW);
+    const uint32_t vb0 = (uint32_t)((int64_t)(n0 + wave * BI * RPW + wrow) * ldw * WES + (wch ^ ws0) * 16);
+    const uint32_t vb1 = (uint32_t)((int64_t)(n0 + wave * BI * RPW + wrow) * ldw * WES + (wch ^ ws1) * 16);
     const int kw = ep.kwrap ? ep.kwrap : K; // W columns
+    const __amdgpu_buffer_rsrc_t rss =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(WQ ? ep.wscale : nullptr), 0, WQ ? s_bytes : 0, 0x00020000);
     auto issue = [&](int stage, int k0) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int row = (wave * AI + j) * RPI;
             const uint32_t soff = (uint32_t)((k0 + (int64_t)j * RPI * lda) * ES);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t *)&lds[stage][row][0], 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t *)&lA(stage, row, 0), 16,
                                                      ((row / RPI) & 1) ? va1 : va0, soff, 0, 0);
         }
         const int kb = k0 >= kw ? k0 - kw : k0; // W column of A column k0
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
-            const int row = (wave * BI + j) * RPI;
-            const uint32_t soff = (uint32_t)((kb + (int64_t)j * RPI * ldw) * ES);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t *)&lds[stage][BM + row][0], 16,
-                                                     (((BM + row) / RPI) & 1) ? vb1 : vb0, soff, 0, 0);
+            const int row = (wave * BI + j) * RPW;
+            const uint32_t soff = (uint32_t)((kb + (int64_t)j * RPW * ldw) * WES);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t *)&lW(stage, row, 0), 16,
+                                                     ((row / RPW) & 1) ? vb1 : vb0, soff, 0, 0);
+        }
+        if constexpr (WQ) {
+            // scale bytes of rows n0 .. n0 + BN for this slab: [k0/64][n][2]
+            if (wave == 0)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_void_t *)lS(stage), 16,
+                                                         (uint32_t)(lane * 16 + 2 * n0),
+                                                         (uint32_t)((int64_t)(k0 / 64) * 2 * N), 0, 0);
         }
     };
 
@@ -619,17 +650,42 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     constexpr int KSUB = MI == 32 ? NCH / 2 : NCH / 4;
     const int lr = lane & (MI - 1);
     const int lq = MI == 32 ? (lane >> 5) : (lane >> 4);
+    Chunk wraw[WQ ? FN : 1]; // WQ: the 16 codes of the current 32-weight block
+    uint32_t wsc[WQ ? FN : 1]; // WQ: the two scale bytes of the slab
     auto frags = [&](Chunk *a, Chunk *b, int stage, int s) {
-        const int cc = (MI == 32 ? 2 : 4) * s + lq;
+        if constexpr (WQ) {
+            const int t = s >> 1, h = s & 1;
+            const int cc = 4 * t + 2 * lq + h;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int r = wm * WM + fm * MI + lr;
-            a[fm] = lds[stage][r][cc ^ swz<NCH>(r)];
-        }
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * WM + fm * MI + lr;
+                a[fm] = lA(stage, r, cc ^ swz<NCH>(r));
+            }
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int r = BM + wn * WN + fn * MI + lr;
-            b[fn] = lds[stage][r][cc ^ swz<NCH>(r)];
+            for (int fn = 0; fn < FN; ++fn) {
+                const int r = wn * WN + fn * MI + lr;
+                if (s == 0) wsc[fn] = lS(stage)[r];
+                if (h == 0) wraw[fn] = lW(stage, r, (2 * t + lq) ^ swz<WCH>(r));
+                // E8M0 byte -> fp32 2^(byte - 127); the conversion uses its exponent
+                const float sc = __builtin_bit_cast(float, ((wsc[fn] >> (8 * t)) & 0xFFu) << 23);
+                const uint32_t lo = wraw[fn].w[2 * h], hi = wraw[fn].w[2 * h + 1];
+                b[fn].w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+                b[fn].w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+                b[fn].w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+                b[fn].w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
+            }
+        } else {
+            const int cc = (MI == 32 ? 2 : 4) * s + lq;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * WM + fm * MI + lr;
+                a[fm] = lA(stage, r, cc ^ swz<NCH>(r));
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int r = wn * WN + fn * MI + lr;
+                b[fn] = lW(stage, r, cc ^ swz<NCH>(r));
+            }
         }
     };
     auto mfmas = [&](const Chunk *a, const Chunk *b) {
@@ -652,18 +708,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     // wave's part of the slab is visible and every wave has finished reading
     // what it read before.  (STAGES - 1 is at most 7, so `later` is at most 6
     // wherever a later slab exists.)
-    constexpr int PER = AI + BI; // load instructions per wave and slab
-    static_assert(STAGES >= 2 && STAGES <= 8 && (STAGES - 1) * PER <= 63, "vmcnt range");
-    auto wait_slab = [&](int later) {
+    constexpr int PER = AI + BI; // load instructions per wave and slab (wave 0: + 1 with WQ)
+    static_assert(STAGES >= 2 && STAGES <= 8 && (STAGES - 1) * (PER + 1) <= 63, "vmcnt range");
+    auto wait_n = [&](auto per_c, int later) {
+        constexpr int P = decltype(per_c)::value;
         switch (later) {
         case 0: vm_wait<0>(); break;
-        case 1: vm_wait<PER>(); break;
-        case 2: vm_wait<(STAGES > 2 ? 2 * PER : 0)>(); break;
-        case 3: vm_wait<(STAGES > 3 ? 3 * PER : 0)>(); break;
-        case 4: vm_wait<(STAGES > 4 ? 4 * PER : 0)>(); break;
-        case 5: vm_wait<(STAGES > 5 ? 5 * PER : 0)>(); break;
-        default: vm_wait<(STAGES > 6 ? 6 * PER : 0)>(); break;
+        case 1: vm_wait<P>(); break;
+        case 2: vm_wait<(STAGES > 2 ? 2 * P : 0)>(); break;
+        case 3: vm_wait<(STAGES > 3 ? 3 * P : 0)>(); break;
+        case 4: vm_wait<(STAGES > 4 ? 4 * P : 0)>(); break;
+        case 5: vm_wait<(STAGES > 5 ? 5 * P : 0)>(); break;
+        default: vm_wait<(STAGES > 6 ? 6 * P : 0)>(); break;
         }
+    };
+    auto wait_slab = [&](int later) {
+        if (WQ && wave == 0) wait_n(std::integral_constant<int, PER + 1>{}, later);
+        else wait_n(std::integral_constant<int, PER>{}, later);
         __syncthreads();
     };
 
@@ -714,7 +775,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
         }
     }
     __syncthreads();
-    char *sbase = reinterpret_cast<char *>(&lds[0][0][0]);
+    char *sbase = reinterpret_cast<char *>(&lds[0]);
     constexpr int kRiBytes = (BM * (int)sizeof(RowInfo) + 255) / 256 * 256;
     constexpr int kStageBytes = NW * MI * (WN + 4) * 4;
     static_assert(kRiBytes + kStageBytes <= (int)sizeof(lds), "epilogue staging exceeds LDS");
@@ -737,14 +798,16 @@ hipError_t launch_t(const void *A, int64_t lda, const void *W, int64_t ldw, int 
     return hipGetLastError();
 }
 
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI>
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, bool WQ = false>
 hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K, const EpiArgs &ep,
                       hipStream_t s) {
     const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
-    hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(64 * WGM * WGN), 0, s, reinterpret_cast<const T *>(A), lda,
-                       reinterpret_cast<const T *>(W), ldw, M, N, K, tiles_n,
-                       (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * sizeof(T)), ep);
+    const int64_t wbytes = WQ ? 1 : (int64_t)sizeof(T);
+    hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, WQ>),
+                       dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WGM * WGN), 0, s,
+                       reinterpret_cast<const T *>(A), lda, W, ldw, M, N, K, tiles_n,
+                       (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * wbytes),
+                       WQ ? (int)((int64_t)(K / 64) * N * 2) : 0, ep);
     return hipGetLastError();
 }
 
@@ -794,6 +857,24 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
     // tile of overhang) below 2 GiB
     const bool small = ((int64_t)M + 256) * lda * (int64_t)sizeof(T) < INT32_MAX &&
                        ((int64_t)N + 256) * ldw * (int64_t)sizeof(T) < INT32_MAX;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if (ep.wscale) {
+            // 8-bit weights: the direct-to-LDS kernel only (conditions checked by the caller)
+            const bool wfast = fast && small && K % 64 == 0 && N % 8 == 0 && ep.kwrap == 0 && ldw % 16 == 0;
+            if (!wfast) return hipErrorInvalidValue;
+            switch (pick_tile(M, N, true, false)) {
+            case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32, true>(A, lda, W, ldw, M, N, K, ep, s);
+            case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 4, 8, 2, 32, true>(A, lda, W, ldw, M, N, K, ep, s);
+            case TILE_128x128_DEEP:
+                return launch_lds<T, EPI, 128, 128, 2, 4, 8, VITENC_DEEP_STAGES, 32, true>(A, lda, W, ldw, M, N, K,
+                                                                                          ep, s);
+            case TILE_64x64: return launch_lds<T, EPI, 64, 64, 2, 2, 8, 3, 32, true>(A, lda, W, ldw, M, N, K, ep, s);
+            default: return hipErrorInvalidValue;
+            }
+        }
+    } else {
+        if (ep.wscale) return hipErrorInvalidValue;
+    }
     if constexpr (!std::is_same<T, float>::value) {
         switch (pick_tile(M, N, fast && small, false)) {
         case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);

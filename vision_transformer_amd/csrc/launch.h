@@ -47,6 +47,11 @@ struct EpiArgs {
     // A has 2*kwrap columns whose second half pairs with W's columns again
     // (the split-pixel patch embedding); 0: A and W share K
     int kwrap = 0;
+    // 8-bit weights (bf16 GEMMs only): when set, W holds E4M3 codes [N, K]
+    // (ldw in bytes) and wscale the E8M0 exponent byte of every 32-weight
+    // block, laid out [K/64][N][2] (the two blocks of a 64-column slab of a
+    // row side by side); needs K % 64 == 0, N % 8 == 0, no kwrap
+    const uint8_t *wscale = nullptr;
 };
 
 // Patch embedding in a 16-bit type with K a multiple of 64 stores each pixel
@@ -61,6 +66,11 @@ inline int embed_lda(int dtype, int K) {
 
 hipError_t launch_gemm(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw,
                        int M, int N, int K, const EpiArgs &ep, hipStream_t s);
+
+// codes [rows, cols] E4M3 and scales [cols/64][rows][2] E8M0 of the fp32
+// matrix w [rows, cols] (cols % 64 == 0; w and codes 16-byte aligned)
+hipError_t launch_mxfp8_quantize(const float *w, int rows, int cols, uint8_t *codes, uint8_t *scales,
+                                 hipStream_t s);
 
 hipError_t launch_layernorm(int out_dtype, const float *x, const float *w, const float *b, float eps,
                             int M, int D, void *y, hipStream_t s);
@@ -138,6 +148,7 @@ struct BlockGeom {
     const float *rope_tab = nullptr;
     const int *tok_pos = nullptr;
     int tok_pos_stride = 0;          // 0: tok_pos shared by all items
+    int wq = 0;                      // the four block matrices are 8-bit codes with block scales
 };
 struct BlockBufs {
     float *Z = nullptr;              // fp32 [B*N, D]

@@ -181,6 +181,40 @@ vitenc_status vitenc_op_linear_gelu(int32_t dtype, const void *A, const void *W,
                   "linear gelu");
 }
 
+vitenc_status vitenc_op_linear_mxfp8(int32_t epi, const void *A, const uint8_t *codes, const uint8_t *scales,
+                                     const float *b, const float *ls, int32_t M, int32_t Nout, int32_t K, void *out,
+                                     void *stream) {
+    clear_error();
+    if (epi != 0 && epi != 1) return op_fail(VITENC_EINVAL, "unknown epilogue %d", epi);
+    if (!A || !codes || !scales || !b || !out) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (M < 0 || Nout <= 0 || K <= 0) return op_fail(VITENC_ESHAPE, "bad sizes");
+    if (K % 64 || Nout % 8) return op_fail(VITENC_ESHAPE, "8-bit weights need K %% 64 == 0 and Nout %% 8 == 0");
+    if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(codes) % 16)
+        return op_fail(VITENC_EINVAL, "A and codes must be 16-byte aligned");
+    EpiArgs ep;
+    ep.bias = b;
+    ep.wscale = scales;
+    if (epi == 0) {
+        ep.ls = ls; ep.Z = reinterpret_cast<float *>(out); ep.ldz = Nout;
+    } else {
+        ep.out = out; ep.ldo = Nout;
+    }
+    return op_dev(launch_gemm(VITENC_BF16, epi == 0 ? EPI_RESID : EPI_GELU, A, K, codes, K, M, Nout, K, ep,
+                              reinterpret_cast<hipStream_t>(stream)),
+                  "linear (8-bit weights)");
+}
+
+vitenc_status vitenc_quantize_mxfp8(const float *w, int32_t rows, int32_t cols, uint8_t *codes, uint8_t *scales,
+                                    void *stream) {
+    clear_error();
+    if (!w || !codes || !scales) return op_fail(VITENC_ENULL, "a required pointer is NULL");
+    if (rows <= 0 || cols <= 0 || cols % 64) return op_fail(VITENC_ESHAPE, "need rows > 0 and cols a multiple of 64");
+    if (reinterpret_cast<uintptr_t>(w) % 16 || reinterpret_cast<uintptr_t>(codes) % 16)
+        return op_fail(VITENC_EINVAL, "w and codes must be 16-byte aligned");
+    return op_dev(launch_mxfp8_quantize(w, rows, cols, codes, scales, reinterpret_cast<hipStream_t>(stream)),
+                  "quantize");
+}
+
 vitenc_status vitenc_op_pool(const float *X, int32_t B, int32_t N, int32_t D, int32_t cls, int32_t n_prefix,
                              float *pooled, void *stream) {
     clear_error();

@@ -37,11 +37,13 @@ class Hparams(ctypes.Structure):
                                       "rope_ref_grid", "cls_token", "modality_embed", "layer_scale",
                                       "attn_mode", "dtype", "pos_interp", "pos_grid_t", "pos_grid_h",
                                       "pos_grid_w", "image_patch_embed", "n_hier")] + \
-               [("hier_layers", c_i32 * MAX_HIER)]
+               [("hier_layers", c_i32 * MAX_HIER), ("weight_format", c_i32)]
 
 
 BLOCK_FIELDS = ("ln1_w", "ln1_b", "qkv_w", "qkv_b", "out_w", "out_b", "ln2_w", "ln2_b", "up_w", "up_b",
-                "down_w", "down_b", "ls1", "ls2")
+                "down_w", "down_b", "ls1", "ls2", "qkv_s", "out_s", "up_s", "down_s")
+WEIGHTS_PLAIN, WEIGHTS_MXFP8 = 0, 1
+QUANT_MATRICES = ("qkv_w", "out_w", "up_w", "down_w")   # stored in 8 bits with WEIGHTS_MXFP8
 
 
 class BlockWeights(ctypes.Structure):
@@ -102,6 +104,8 @@ SIGNATURES = {
     "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_linear_gelu": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_pool": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vitenc_op_linear_mxfp8": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "vitenc_quantize_mxfp8": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "vitenc_predictor_create": (c_i32, [ctypes.POINTER(PredHparams), ctypes.POINTER(PredWeights),
                                         ctypes.POINTER(c_vp)]),
     "vitenc_predictor_destroy": (None, [c_vp]),
@@ -224,9 +228,15 @@ class Encoder:
         t["hier_norm_w"] = [f32_to_device(x, device) for x in getattr(w, "hier_norm_w", [])]
         t["hier_norm_b"] = [f32_to_device(x, device) for x in getattr(w, "hier_norm_b", [])]
         blocks = []
+        wq = hp.get("weight_format", WEIGHTS_PLAIN) == WEIGHTS_MXFP8
         for b in w.blocks:
-            d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
-                 "up_w": to_device(b.store["up_w"], dt, device), "down_w": to_device(b.store["down_w"], dt, device)}
+            d = {}
+            for n in QUANT_MATRICES:
+                if wq:
+                    # fp32 matrices quantised on the device into codes and block scales
+                    d[n], d[n[:-2] + "_s"] = quantize_mxfp8(f32_to_device(b.store[n], device))
+                else:
+                    d[n] = to_device(b.store[n], dt, device)
             for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b", "ls1", "ls2"):
                 d[n] = f32_to_device(getattr(b, n), device)
             blocks.append(d)
@@ -335,9 +345,15 @@ class Predictor:
              "norm_b": f32_to_device(w.norm_b, device), "proj_w": to_device(w.store["proj_w"], dt, device),
              "proj_b": f32_to_device(w.proj_b, device)}
         blocks = []
+        wq = hp.get("weight_format", WEIGHTS_PLAIN) == WEIGHTS_MXFP8
         for b in w.blocks:
-            d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
-                 "up_w": to_device(b.store["up_w"], dt, device), "down_w": to_device(b.store["down_w"], dt, device)}
+            d = {}
+            for n in QUANT_MATRICES:
+                if wq:
+                    # fp32 matrices quantised on the device into codes and block scales
+                    d[n], d[n[:-2] + "_s"] = quantize_mxfp8(f32_to_device(b.store[n], device))
+                else:
+                    d[n] = to_device(b.store[n], dt, device)
             for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b"):
                 d[n] = f32_to_device(getattr(b, n), device)
             blocks.append(d)
@@ -414,9 +430,15 @@ class Head:
         for n in ("q_w", "k_w", "v_w", "up_w", "down_w", "cls_w"):
             t[n] = to_device(w.store[n], dt, device)
         blocks = []
+        wq = hp.get("weight_format", WEIGHTS_PLAIN) == WEIGHTS_MXFP8
         for b in w.blocks:
-            d = {"qkv_w": to_device(b.store["qkv_w"], dt, device), "out_w": to_device(b.store["out_w"], dt, device),
-                 "up_w": to_device(b.store["up_w"], dt, device), "down_w": to_device(b.store["down_w"], dt, device)}
+            d = {}
+            for n in QUANT_MATRICES:
+                if wq:
+                    # fp32 matrices quantised on the device into codes and block scales
+                    d[n], d[n[:-2] + "_s"] = quantize_mxfp8(f32_to_device(b.store[n], device))
+                else:
+                    d[n] = to_device(b.store[n], dt, device)
             for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b"):
                 d[n] = f32_to_device(getattr(b, n), device)
             blocks.append(d)
@@ -564,6 +586,28 @@ def op_linear_gelu(dtype, A, W, b, stream=None, out=None):
     check(lib().vitenc_op_linear_gelu(dtype, A.data_ptr(), W.data_ptr(), b.data_ptr(), M, Nout, K, U.data_ptr(),
                                       _stream(stream)))
     return U
+
+
+def quantize_mxfp8(w, stream=None):
+    """fp32 device matrix [rows, cols] -> (codes uint8 [rows, cols], scale
+    bytes uint8 [cols/64, rows, 2]) in the format of vitenc_quantize_mxfp8."""
+    import torch
+    rows, cols = w.shape
+    w = w.contiguous()
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((cols // 64, rows, 2), dtype=torch.uint8, device=w.device)
+    check(lib().vitenc_quantize_mxfp8(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                      _stream(stream)))
+    return codes, scales
+
+
+def op_linear_mxfp8(epi, A, codes, scales, b, out, ls=None, stream=None):
+    """epi 0: out (fp32 Z) += ls * (A W^T + b); epi 1: out (bf16) = GELU(A W^T + b)."""
+    M, K = A.shape
+    Nout = codes.shape[0]
+    check(lib().vitenc_op_linear_mxfp8(epi, A.data_ptr(), codes.data_ptr(), scales.data_ptr(), b.data_ptr(),
+                                       _ptr(ls), M, Nout, K, out.data_ptr(), _stream(stream)))
+    return out
 
 
 def op_pool(X, cls, n_prefix, stream=None):

@@ -28,7 +28,9 @@ receives exactly the first k blocks of the full config.
 
 Matrices of bf16/f16 configs are rounded to that type with round-to-nearest-
 even; the rounded values (held exactly in fp32) are what both the GPU and the
-oracle consume.  Vectors, norms and tables stay fp32.
+oracle consume.  Vectors, norms and tables stay fp32.  With weight_format 1
+(8-bit block weights) the four block matrices stay fp32 and each side
+quantises them with its own quantiser.
 """
 from __future__ import annotations
 
@@ -44,6 +46,7 @@ POS_INTERP_NONE, POS_INTERP_BICUBIC, POS_INTERP_TRILINEAR = 0, 1, 2
 ROPE_NONE, ROPE_3D = 0, 1
 LAYOUT_TILED, LAYOUT_INTERLEAVED = 0, 1
 ATTN_FULL, ATTN_BLOCK_CAUSAL = 0, 1
+WEIGHTS_PLAIN, WEIGHTS_MXFP8 = 0, 1
 
 
 @dataclass
@@ -74,6 +77,7 @@ class EncoderConfig:
     layer_scale: int = 0
     attn_mode: int = ATTN_FULL
     dtype: int = DTYPE_BF16
+    weight_format: int = 0            # 1: the four block matrices in the 8-bit block format
     # input geometry
     batch: int = 1
     frames: int = 1
@@ -160,6 +164,7 @@ class EncoderConfig:
         hp["n_hier"] = len(self.hier_layers)
         hp["hier_layers"] = tuple(self.hier_layers)
         hp["pos_grid_t"], hp["pos_grid_h"], hp["pos_grid_w"] = self.table_grid if self.pos_interp else (0, 0, 0)
+        hp["weight_format"] = self.weight_format
         return hp
 
     def flops(self) -> float:
@@ -356,18 +361,21 @@ def make_workload(cfg: EncoderConfig, seed: Optional[int] = None) -> Workload:
     ones = np.ones(D, np.float32)
     zeros = np.zeros(D, np.float32)
     blocks = []
+    # 8-bit block weights are quantised from the fp32 draws (by each side's own
+    # quantiser), so those four matrices keep their fp32 values here
+    mdt = DTYPE_F32 if cfg.weight_format == WEIGHTS_MXFP8 else dt
     for _ in range(cfg.n_layer):
         st = {}
         qkv = _normal(rng, (3 * D, D), cfg.std_w)
         if cfg.std_qk is not None:
             qkv[: 2 * D] *= np.float32(cfg.std_qk / cfg.std_w)
-        st["qkv_w"], qkv_w = quantise(qkv, dt)
+        st["qkv_w"], qkv_w = quantise(qkv, mdt)
         qkv_b = _normal(rng, (3 * D,), cfg.std_w)
-        st["out_w"], out_w = quantise(_normal(rng, (D, D), cfg.std_w), dt)
+        st["out_w"], out_w = quantise(_normal(rng, (D, D), cfg.std_w), mdt)
         out_b = _normal(rng, (D,), cfg.std_w)
-        st["up_w"], up_w = quantise(_normal(rng, (F, D), cfg.std_w), dt)
+        st["up_w"], up_w = quantise(_normal(rng, (F, D), cfg.std_w), mdt)
         up_b = _normal(rng, (F,), cfg.std_w)
-        st["down_w"], down_w = quantise(_normal(rng, (D, F), cfg.std_w), dt)
+        st["down_w"], down_w = quantise(_normal(rng, (D, F), cfg.std_w), mdt)
         down_b = _normal(rng, (D,), cfg.std_w)
         ls1 = ls2 = None
         if cfg.layer_scale:
