@@ -1,7 +1,7 @@
 """Throughput of the ViT encoder forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--graph] [--no-cpu-baseline]
-                    [--part all|encoder|predictor|head|variants]
+                    [--part all|encoder|predictor|head|variants|configs|weights8]
     python bench.py --write-counters KERNEL FETCH.csv WRITE.csv OUT.txt
 
 
@@ -16,9 +16,10 @@ the encoder (one vitenc_predict call per step) the same way, with its own
 roofline and oracle baseline; `head` does the same for the attentive-pool
 classifier head (one vitenc_head_forward call per step); `variants` times
 encoder options on their own inputs (a resampled position table, the one-frame
-image tokenizer with hierarchical outputs).  `--part predictor`, `--part head`
-or `--part variants` prints that object alone (the counter runs of their
-kernels use it).
+image tokenizer with hierarchical outputs); `all_configs` times every encoder
+workload; `weights8` compares 8-bit block weights with bf16 weights on the
+ViT-L/16 image encoder.  `--part NAME` prints that object alone (the counter
+runs of their kernels use it).
 
 Its `traffic` figure comes from a committed counter summary (written by the
 --write-counters mode from two rocprofv3 --pmc runs of this script: one
@@ -75,7 +76,8 @@ def parse():
     ap.add_argument("--only", metavar="KERNEL", default=None,
                     help="launch only this kernel of the encoder layer (a kernel-breakdown name) --kernel-reps "
                          "times at the headline shape and exit (for counter runs)")
-    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head", "variants", "configs"), default="all",
+    ap.add_argument("--part", choices=("all", "encoder", "predictor", "head", "variants", "configs", "weights8"),
+                    default="all",
                     help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
                          "head (reported in the line's `predictor` / `head` objects), or all three")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
@@ -567,6 +569,81 @@ def bench_variants(args, stream):
     return res
 
 
+def bench_weights8(args, stream):
+    """8-bit block weights against bf16 weights on the ViT-L/16 image encoder
+    (the regime the pages quantise for: small image batches, where the
+    weights are a large part of the bytes a forward moves), batch 8 and
+    batch 1: one encode call per step, and the up and down projections alone
+    at the encode shapes (weights rotated over the 24 layers, so every launch
+    reads its weights from HBM) with their algorithmic bytes per launch."""
+    import torch
+    from vision_transformer_amd import vitenc as V
+    from vision_transformer_amd import workloads as W
+    res = {}
+    for batch in (8, 1):
+        row = {}
+        encs = {}
+        for fmt, wf in (("bf16", W.WEIGHTS_PLAIN), ("mxfp8", W.WEIGHTS_MXFP8)):
+            cfg = W.CONFIGS[1].replace(batch=batch, weight_format=wf)
+            wl = W.make_workload(cfg)
+            enc = V.Encoder.from_workload(wl)
+            px = torch.from_numpy(wl.pixels).cuda()
+            ws, out, pooled = enc.alloc(cfg.batch, cfg.frames, cfg.height, cfg.width)
+            ms, _ = time_steps(lambda: enc.encode_into(px, ws, out, pooled, stream), max(10, args.steps),
+                               args.warmup, stream)
+            M, D, F = cfg.batch * cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim
+            wb = 1 + 1 / 32 if wf == W.WEIGHTS_MXFP8 else 2   # weight bytes per weight
+            Y = torch.randn((M, D), device="cuda").to(torch.bfloat16)
+            Uo = torch.randn((M, F), device="cuda").to(torch.bfloat16)
+            Z = torch.zeros((M, D), device="cuda")
+            L = len(enc.blocks)
+            reps = 3 * L
+
+            def up(i):
+                b = enc.blocks[i % L]
+                if wf == W.WEIGHTS_MXFP8:
+                    V.op_linear_mxfp8(1, Y, b["up_w"], b["up_s"], b["up_b"], Uo)
+                else:
+                    V.op_linear_gelu(W.DTYPE_BF16, Y, b["up_w"], b["up_b"], out=Uo)
+
+            def down(i):
+                b = enc.blocks[i % L]
+                if wf == W.WEIGHTS_MXFP8:
+                    V.op_linear_mxfp8(0, Uo, b["down_w"], b["down_s"], b["down_b"], Z)
+                else:
+                    V.op_linear_residual(W.DTYPE_BF16, Uo, b["down_w"], b["down_b"], Z)
+
+            gem = {}
+            for name, fn, flops, nbytes in (
+                    ("up_gemm", up, 2.0 * M * D * F, M * D * 2 + F * D * wb + M * F * 2),
+                    ("down_gemm", down, 2.0 * M * F * D, M * F * 2 + D * F * wb + 8 * M * D)):
+                for i in range(L):
+                    fn(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(reps):
+                    fn(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / reps * 1e3
+                gem[name] = {"us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                             "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                             "algorithmic_MB": round(nbytes / 1e6, 2),
+                             "hbm_GBs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                             "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            row[fmt] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.batch * cfg.n_tokens / ms * 1e3, 1),
+                        "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
+                        "weight_MB_per_forward": round(cfg.n_layer * (4 * D * D + 2 * D * F) * wb / 1e6, 1),
+                        **gem}
+            log(f"[bench] weights8 batch {batch} {fmt}: {row[fmt]}")
+            enc.close()
+            del wl, px, ws, out, pooled, Y, Uo, Z
+            torch.cuda.empty_cache()
+        row["speedup"] = round(row["bf16"]["ms_per_step"] / row["mxfp8"]["ms_per_step"], 3)
+        res[f"vit_l16_image_batch{batch}"] = row
+    return res
+
+
 def bench_configs(args, stream):
     """Every encoder workload at its own shape (the five the metric's
     configuration list names), one encode call per step: throughput and the
@@ -620,6 +697,9 @@ def main():
     if args.part == "configs":
         print(json.dumps({"configs": bench_configs(args, stream)}), flush=True)
         return
+    if args.part == "weights8":
+        print(json.dumps({"weights8": bench_weights8(args, stream)}), flush=True)
+        return
     cfg = W.HEADLINE
     log(f"[bench] workload {cfg.name}: B={cfg.batch} N={cfg.n_tokens} D={cfg.embed_dim} L={cfg.n_layer}")
     wl = W.make_workload(cfg)
@@ -664,6 +744,7 @@ def main():
     head = bench_head(args, stream) if args.part == "all" else None
     variants = bench_variants(args, stream) if args.part == "all" else None
     configs = bench_configs(args, stream) if args.part == "all" else None
+    weights8 = bench_weights8(args, stream) if args.part == "all" else None
 
     line = {
         "metric": "encoder tokens/sec + MFMA TFLOP/s fraction of peak (ViT-L video, bf16, 1 GPU)",
@@ -681,6 +762,7 @@ def main():
         "head": head,
         "variants": variants,
         "all_configs": configs,
+        "weights8": weights8,
     }
     print(json.dumps(line), flush=True)
 

@@ -554,6 +554,20 @@ constexpr bool kSwap = VITENC_GEMM_SWAP;
 // 4t + 2g + h at step 2t + h).  The scale bytes of a slab (2 per weight row,
 // contiguous over the rows in the [K/64][N][2] layout) come along with it:
 // wave 0 issues one more direct-to-LDS load per slab.
+// One 16-byte-per-lane buffer load straight into LDS at dst (wave-uniform;
+// lane l's 16 bytes land at dst + 16 l), issued from inline assembly.  The
+// 8-bit weight variant uses it for all its slab loads: with the builtin, the
+// compiler cannot tell the ring stages apart there and waits for every
+// refill (vmcnt(0)) before the next stage's fragment reads, which serialises
+// the ring; the kernel orders these loads itself (vm_wait + barrier).  M0
+// carries the LDS address; nothing else in that kernel keeps a value in M0.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void *dst, uint32_t voff, uint32_t soff) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(const lds_void_t *)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rs),
+                 "s"(soff)
+                 : "memory");
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI, bool WQ>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
                                                                      const void *__restrict__ W, int64_t ldw, int M,
@@ -612,28 +626,28 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     const int kw = ep.kwrap ? ep.kwrap : K; // W columns
     const __amdgpu_buffer_rsrc_t rss =
         __builtin_amdgcn_make_buffer_rsrc((void *)(WQ ? ep.wscale : nullptr), 0, WQ ? s_bytes : 0, 0x00020000);
+    auto load = [&](__amdgpu_buffer_rsrc_t rs, const void *dst, uint32_t voff, uint32_t soff) {
+        if constexpr (WQ) dma16(rs, dst, voff, soff);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+    };
     auto issue = [&](int stage, int k0) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int row = (wave * AI + j) * RPI;
             const uint32_t soff = (uint32_t)((k0 + (int64_t)j * RPI * lda) * ES);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_void_t *)&lA(stage, row, 0), 16,
-                                                     ((row / RPI) & 1) ? va1 : va0, soff, 0, 0);
+            load(rsa, &lA(stage, row, 0), ((row / RPI) & 1) ? va1 : va0, soff);
         }
         const int kb = k0 >= kw ? k0 - kw : k0; // W column of A column k0
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
             const int row = (wave * BI + j) * RPW;
             const uint32_t soff = (uint32_t)((kb + (int64_t)j * RPW * ldw) * WES);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_void_t *)&lW(stage, row, 0), 16,
-                                                     ((row / RPW) & 1) ? vb1 : vb0, soff, 0, 0);
+            load(rsb, &lW(stage, row, 0), ((row / RPW) & 1) ? vb1 : vb0, soff);
         }
         if constexpr (WQ) {
             // scale bytes of rows n0 .. n0 + BN for this slab: [k0/64][n][2]
             if (wave == 0)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rss, (lds_void_t *)lS(stage), 16,
-                                                         (uint32_t)(lane * 16 + 2 * n0),
-                                                         (uint32_t)((int64_t)(k0 / 64) * 2 * N), 0, 0);
+                load(rss, lS(stage), (uint32_t)(lane * 16 + 2 * n0), (uint32_t)((int64_t)(k0 / 64) * 2 * N));
         }
     };
 
@@ -661,18 +675,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
                 const int r = wm * WM + fm * MI + lr;
                 a[fm] = lA(stage, r, cc ^ swz<NCH>(r));
             }
+            // only the reads here: the codes are expanded by expand() after
+            // the current step's MFMAs are issued, so that the wave does not
+            // wait on these reads before issuing them
+            (void)b;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const int r = wn * WN + fn * MI + lr;
                 if (s == 0) wsc[fn] = lS(stage)[r];
                 if (h == 0) wraw[fn] = lW(stage, r, (2 * t + lq) ^ swz<WCH>(r));
-                // E8M0 byte -> fp32 2^(byte - 127); the conversion uses its exponent
-                const float sc = __builtin_bit_cast(float, ((wsc[fn] >> (8 * t)) & 0xFFu) << 23);
-                const uint32_t lo = wraw[fn].w[2 * h], hi = wraw[fn].w[2 * h + 1];
-                b[fn].w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
-                b[fn].w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
-                b[fn].w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
-                b[fn].w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
             }
         } else {
             const int cc = (MI == 32 ? 2 : 4) * s + lq;
@@ -685,6 +696,22 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
             for (int fn = 0; fn < FN; ++fn) {
                 const int r = wn * WN + fn * MI + lr;
                 b[fn] = lW(stage, r, cc ^ swz<NCH>(r));
+            }
+        }
+    };
+    // WQ: the bf16 weight fragment of step s from the codes read by frags()
+    auto expand = [&](Chunk *b, int s) {
+        if constexpr (WQ) {
+            const int t = s >> 1, h = s & 1;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                // E8M0 byte -> fp32 2^(byte - 127); the conversion uses its exponent
+                const float sc = __builtin_bit_cast(float, ((wsc[fn] >> (8 * t)) & 0xFFu) << 23);
+                const uint32_t lo = wraw[fn].w[2 * h], hi = wraw[fn].w[2 * h + 1];
+                b[fn].w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+                b[fn].w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+                b[fn].w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+                b[fn].w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
             }
         }
     };
@@ -702,6 +729,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     auto order_reads_first = [&]() {
         __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0); // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0); // MFMAs
+        if constexpr (WQ) __builtin_amdgcn_sched_group_barrier(0x002, 4 * FN + 2, 0); // expansion (VALU)
     };
     // Wait until this wave's loads of one slab have landed while `later`
     // slabs issued after it may still be in flight, then barrier: every
@@ -741,6 +769,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     wait_slab(min(STAGES, nk) - 1);
     Chunk a0[FM], b0[FN], a1[FM], b1[FN];
     frags(a0, b0, 0, 0);
+    expand(b0, 0);
     int stage = 0;
     for (int kt = 0; kt < nk; ++kt) {
         int nstage = stage + 1;
@@ -752,6 +781,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
             if (s + 1 < KSUB) {
                 frags(na, nb, stage, s + 1);
                 mfmas(ca, cb);
+                expand(nb, s + 1);
                 order_reads_first();
             } else {
                 if (kt + 1 < nk) {
@@ -761,7 +791,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
                     frags(na, nb, nstage, 0);
                 }
                 mfmas(ca, cb);
-                if (kt + 1 < nk) order_reads_first();
+                if (kt + 1 < nk) {
+                    expand(nb, 0);
+                    order_reads_first();
+                }
             }
         }
         stage = nstage;
