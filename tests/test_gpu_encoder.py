@@ -106,14 +106,22 @@ def test_f16_path(gpu_lib):
     _parity(SMALL["levjepa"].replace(dtype=W.DTYPE_F16, n_layer=4))
 
 
-def test_batch_equals_single_items_bitwise(gpu_lib):
+def test_batch_equals_single_items(gpu_lib):
+    """Items are independent: an item encoded alone gives what it gets inside
+    a batch.  Not bit for bit: a single item's GEMMs have fewer tiles and
+    split K over more workgroups (split-K), which groups the fp32 sums
+    differently; the difference stays at the fp32 rounding level (the bf16
+    rounding of an activation differs now and then), far below what any
+    mixing of items would give."""
     cfg = W.CONFIGS[1].replace(n_layer=2, batch=3)
     wl = W.make_workload(cfg)
     out, pooled = run_gpu(wl)
     for b in range(cfg.batch):
         one = W.Workload(cfg.replace(batch=1), wl.pixels[b:b + 1], wl.weights)
         o1, p1 = run_gpu(one)
-        assert np.array_equal(o1[0], out[b]) and np.array_equal(p1[0], pooled[b])
+        d = np.abs(o1[0] - out[b]).max()
+        say(f"  item {b}: max |single - batched| {d:.3g}")
+        assert d <= 1e-2 and np.abs(p1[0] - pooled[b]).max() <= 1e-3
 
 
 def test_repeat_calls_bitwise_identical(gpu_lib):

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -139,6 +140,8 @@ struct Plan {
     int64_t M;
     int D, F, nh, hd, K, lda, ldv;
     size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_rope, off_tok, off_pos, off_attn, total;
+    size_t off_skp;           // split-K partials (sk_floats == 0: none)
+    int64_t sk_floats;
     bool resample;
 };
 
@@ -193,6 +196,17 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     pl.off_tok = take((size_t)pl.Np * 4);
     pl.off_pos = pl.resample ? take((size_t)pl.N * pl.D * 4) : 0;
     pl.off_attn = take((size_t)attention_scratch_floats(B, pl.N, pl.nh, pl.hd, pl.p) * 4);
+    // split-K scratch for the GEMMs whose tiles leave most CUs idle (small inputs)
+    {
+        const bool wq = hp.weight_format == VITENC_WEIGHTS_MXFP8;
+        const int Kp = pl.lda == 2 * pl.K ? 2 * pl.K : pl.K, Mi = (int)pl.M;
+        pl.sk_floats = std::max<int64_t>({gemm_splitk_floats(hp.dtype, EPI_PATCH, B * pl.Np, pl.D, Kp, false),
+                                          gemm_splitk_floats(hp.dtype, EPI_QKV, Mi, 3 * pl.D, pl.D, wq),
+                                          gemm_splitk_floats(hp.dtype, EPI_RESID, Mi, pl.D, pl.D, wq),
+                                          gemm_splitk_floats(hp.dtype, EPI_GELU, Mi, pl.F, pl.D, wq),
+                                          gemm_splitk_floats(hp.dtype, EPI_RESID, Mi, pl.D, pl.F, wq)});
+    }
+    pl.off_skp = pl.sk_floats ? take((size_t)pl.sk_floats * 4) : 0;
     pl.total = off;
     return VITENC_OK;
 }
@@ -307,6 +321,12 @@ vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int
         pos = pbuf;
     }
 
+    float *sk_part = pl.sk_floats ? reinterpret_cast<float *>(ws + pl.off_skp) : nullptr;
+    auto with_splitk = [&](EpiArgs &ep) {
+        ep.sk_part = sk_part;
+        ep.sk_part_floats = pl.sk_floats;
+    };
+
     // a1-a3: tokens
     CHECK_DEV(launch_patchify(dt, pixels, B, pl.C, T, H, W, pl.tub, hp.patch_size, A, pl.lda, s), "patchify");
     const float *mod = !hp.modality_embed ? nullptr : pl.image ? m->w.mod_embed_img : m->w.mod_embed;
@@ -322,6 +342,7 @@ vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int
         ep.prefix = pl.p;
         const bool split = pl.lda == 2 * pl.K;
         ep.kwrap = split ? pl.K : 0;
+        with_splitk(ep);
         CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda, pl.image ? m->w.patch_img_w : m->w.patch_w, pl.K, B * pl.Np, D,
                               split ? 2 * pl.K : pl.K, ep, s),
                   "patch GEMM");
@@ -345,6 +366,8 @@ vitenc_status vitenc_encode_hier(const vitenc_model *m, const float *pixels, int
     BlockBufs bb;
     bb.Z = Z; bb.Y = Y; bb.Q = Q; bb.K = Kb; bb.Vt = Vt; bb.O = O; bb.U = U;
     bb.attn_scratch = reinterpret_cast<float *>(ws + pl.off_attn);
+    bb.sk_part = sk_part;
+    bb.sk_part_floats = pl.sk_floats;
     int k_hier = 0;
     for (int l = 0; l < hp.n_layer; ++l) {
         const char *what = "block";

@@ -11,6 +11,10 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
                      const char **what) {
     const int M = g.B * g.N, D = g.D, F = g.F;
     hipError_t e;
+    auto splitk = [&](EpiArgs &ep) {
+        ep.sk_part = b.sk_part;
+        ep.sk_part_floats = b.sk_part_floats;
+    };
 #define STEP(expr, name)                                                                                          \
     do {                                                                                                          \
         e = (expr);                                                                                               \
@@ -32,6 +36,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.rope_tab_pairs = (g.gt + g.gh + g.gw) * ep.d_rot;
         ep.gt = g.gt; ep.gh = g.gh;
         if (g.wq) ep.wscale = w.qkv_s;
+        splitk(ep);
         STEP(launch_gemm(g.dtype, EPI_QKV, b.Y, D, w.qkv_w, D, M, 3 * D, D, ep, s), "qkv GEMM");
     }
     STEP(launch_attention(g.dtype, b.Q, b.K, b.Vt, g.B, g.N, g.n_head, g.head_dim, g.ldv, g.attn_mode, g.prefix,
@@ -42,6 +47,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.bias = w.out_b; ep.Z = b.Z; ep.ldz = D;
         ep.ls = g.layer_scale ? w.ls1 : nullptr;
         if (g.wq) ep.wscale = w.out_s;
+        splitk(ep);
         STEP(launch_gemm(g.dtype, EPI_RESID, b.O, D, w.out_w, D, M, D, D, ep, s), "out GEMM");
     }
     STEP(launch_layernorm(g.dtype, b.Z, w.ln2_w, w.ln2_b, g.eps, M, D, b.Y, s), "ln2");
@@ -49,6 +55,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         EpiArgs ep;
         ep.bias = w.up_b; ep.out = b.U; ep.ldo = F;
         if (g.wq) ep.wscale = w.up_s;
+        splitk(ep);
         STEP(launch_gemm(g.dtype, EPI_GELU, b.Y, D, w.up_w, D, M, F, D, ep, s), "up GEMM");
     }
     {
@@ -56,6 +63,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.bias = w.down_b; ep.Z = b.Z; ep.ldz = D;
         ep.ls = g.layer_scale ? w.ls2 : nullptr;
         if (g.wq) ep.wscale = w.down_s;
+        splitk(ep);
         STEP(launch_gemm(g.dtype, EPI_RESID, b.U, F, w.down_w, F, M, D, F, ep, s), "down GEMM");
     }
 #undef STEP

@@ -21,6 +21,7 @@
 //   QKV    split [q; k; v] into heads, 3-D RoPE on q and k of patch tokens
 //          ("Architecture", "3-D RoPE"), V written transposed per head
 // where v = accumulator + bias.
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -100,7 +101,7 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
 template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, bool SWAP, typename AccT>
 __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, float *stage, float2 *lds_tab,
                                               int lds_tab_cap, int m0, int n0, int woff_m, int woff_n, int M, int N,
-                                              const EpiArgs &ep) {
+                                              const EpiArgs &ep, float *part = nullptr) {
     constexpr int NV = MI == 32 ? 16 : 4; // accumulator values per lane per block
     constexpr int LD = WN + 4;            // staging row stride (floats), 16-byte aligned
     constexpr int CPR = WN / 8;           // 8-column groups per row
@@ -240,6 +241,18 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
     auto row_path = [&](int rt, const float (&x)[8]) {
         const int row = m0 + rt;
         if (row >= M || !col_any) return;
+        if (part) {
+            // split-K: the raw partial sum of this workgroup's K range, fp32 [M, N]
+            float *dst = part + (int64_t)row * N + col0;
+            if (col_full) {
+                reinterpret_cast<float4 *>(dst)[0] = make_float4(x[0], x[1], x[2], x[3]);
+                reinterpret_cast<float4 *>(dst)[1] = make_float4(x[4], x[5], x[6], x[7]);
+            } else {
+                for (int j = 0; j < 8; ++j)
+                    if (col0 + j < N) dst[j] = x[j];
+            }
+            return;
+        }
         float v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = x[j] + bias8[j];
@@ -407,7 +420,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
     const int wm = wave >> 1, wn = wave & 1;
     const int g = lane >> 5, l32 = lane & 31;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int ntile = gridDim.x / ep.splits;
+    const int split = blockIdx.x / ntile;
+    const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
     const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int lc = tid & 7, lr = tid >> 3;
@@ -492,19 +507,23 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     // Two LDS buffers and two register staging sets: the slab of step k+2 is
     // fetched while step k is multiplied, so each load has two compute phases
     // to land before it is written to LDS.
-    const int nk = (int)cdiv(K, BK);
+    // this workgroup's K steps: [kb0, kb0 + nk) of cdiv(K, BK)
+    const int nk_all = (int)cdiv(K, BK);
+    const int kb0 = (int)((int64_t)split * nk_all / ep.splits);
+    const int nk = (int)((int64_t)(split + 1) * nk_all / ep.splits) - kb0;
+    const int kbase = kb0 * BK;
     Chunk ra0[A_PER], rb0[B_PER], ra1[A_PER], rb1[B_PER];
-    gload(ra0, rb0, 0);
-    if (nk > 1) gload(ra1, rb1, BK);
+    gload(ra0, rb0, kbase);
+    if (nk > 1) gload(ra1, rb1, kbase + BK);
     sstore(ra0, rb0, 0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt += 2) {
-        if (kt + 2 < nk) gload(ra0, rb0, (kt + 2) * BK);
+        if (kt + 2 < nk) gload(ra0, rb0, kbase + (kt + 2) * BK);
         compute(0);
         if (kt + 1 < nk) sstore(ra1, rb1, 1);
         __syncthreads();
         if (kt + 1 >= nk) break;
-        if (kt + 3 < nk) gload(ra1, rb1, (kt + 3) * BK);
+        if (kt + 3 < nk) gload(ra1, rb1, kbase + (kt + 3) * BK);
         compute(1);
         if (kt + 2 < nk) sstore(ra0, rb0, 0);
         __syncthreads();
@@ -518,8 +537,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     float *stage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * 32 * (WN + 4);
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(smem) - kRiBytes - kStageBytes) / 8;
-    gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN, false>(acc, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M,
-                                                        N, ep);
+    gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN, false>(
+        acc, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N, ep,
+        ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
 }
 
 
@@ -556,11 +576,13 @@ constexpr bool kSwap = VITENC_GEMM_SWAP;
 // wave 0 issues one more direct-to-LDS load per slab.
 // One 16-byte-per-lane buffer load straight into LDS at dst (wave-uniform;
 // lane l's 16 bytes land at dst + 16 l), issued from inline assembly.  The
-// 8-bit weight variant uses it for all its slab loads: with the builtin, the
-// compiler cannot tell the ring stages apart there and waits for every
-// refill (vmcnt(0)) before the next stage's fragment reads, which serialises
-// the ring; the kernel orders these loads itself (vm_wait + barrier).  M0
-// carries the LDS address; nothing else in that kernel keeps a value in M0.
+// direct-to-LDS kernel issues all its slab loads this way: with the builtin,
+// the compiler cannot always tell the ring stages apart and then waits for
+// every refill (vmcnt(0)) before the next stage's fragment reads, which
+// serialises the ring (whether it does depends on how its alias analysis of
+// the surrounding code comes out); the kernel orders these loads itself
+// (vm_wait + barrier).  M0 carries the LDS address; nothing else in that
+// kernel keeps a value in M0.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void *dst, uint32_t voff, uint32_t soff) {
     const uint32_t lds = (uint32_t)(uintptr_t)(const lds_void_t *)dst;
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rs),
@@ -601,7 +623,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, lives in an SGPR
     const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 5, l32 = lane & 31;
-    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int ntile = gridDim.x / ep.splits;
+    const int split = blockIdx.x / ntile;
+    const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
     const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
 
@@ -627,8 +651,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     const __amdgpu_buffer_rsrc_t rss =
         __builtin_amdgcn_make_buffer_rsrc((void *)(WQ ? ep.wscale : nullptr), 0, WQ ? s_bytes : 0, 0x00020000);
     auto load = [&](__amdgpu_buffer_rsrc_t rs, const void *dst, uint32_t voff, uint32_t soff) {
-        if constexpr (WQ) dma16(rs, dst, voff, soff);
-        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
+        dma16(rs, dst, voff, soff);
     };
     auto issue = [&](int stage, int k0) {
 #pragma unroll
@@ -762,10 +785,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     // kt+1, barrier (after which slab kt's stage is free), issue slab
     // kt+STAGES into it, and read the first fragments of slab kt+1; those
     // reads then overlap the last MFMAs of slab kt.
-    const int nk = K / BK;
+    // this workgroup's slabs: [kb0, kb0 + nk) of K / BK
+    const int nk_all = K / BK;
+    const int kb0 = (int)((int64_t)split * nk_all / ep.splits);
+    const int nk = (int)((int64_t)(split + 1) * nk_all / ep.splits) - kb0;
+    const int kbase = kb0 * BK;
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
-        if (s < nk) issue(s, s * BK);
+        if (s < nk) issue(s, kbase + s * BK);
     wait_slab(min(STAGES, nk) - 1);
     Chunk a0[FM], b0[FN], a1[FM], b1[FN];
     frags(a0, b0, 0, 0);
@@ -787,7 +814,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
                 if (kt + 1 < nk) {
                     // slabs issued so far: 0 .. min(kt + STAGES - 1, nk - 1)
                     wait_slab(min(kt + STAGES - 1, nk - 1) - (kt + 1));
-                    if (kt + STAGES < nk) issue(stage, (kt + STAGES) * BK);
+                    if (kt + STAGES < nk) issue(stage, kbase + (kt + STAGES) * BK);
                     frags(na, nb, nstage, 0);
                 }
                 mfmas(ca, cb);
@@ -817,18 +844,104 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(lds) - kRiBytes - kStageBytes) / 8;
     gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, kSwap>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
-                                                  ep);
+                                                  ep, ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
 }
 
-template <typename T, int EPI, bool FAST>
+// Split-K where the output tiles fill at most half of the per_cu workgroup
+// slots of the 256 CUs (the tiles of small inputs walk K serially, bound by the
+// latency of each step): enough splits to fill them, each split keeping at
+// least min_steps K steps, at most 16.  The partials cost 8 bytes per output
+// and split of HBM traffic, so short-K GEMMs with many outputs do not split.
+// Only the STORE, GELU and RESID epilogues split (the reduction kernel below
+// applies them); N must be a multiple of 4.
+inline int splits_for(int epi, int64_t tiles, int nk, int per_cu, int min_steps, int M, int N, int K) {
+    if (!(epi == EPI_STORE || epi == EPI_GELU || epi == EPI_RESID) || N % 4 != 0) return 1;
+    const int64_t target = 256 * (int64_t)per_cu;
+    if (2 * tiles > target) return 1; // measured: 400 tiles of 64 x 64 (target 768) run slower split
+    int S = (int)std::min<int64_t>({cdiv(target, tiles), (int64_t)nk / min_steps, 16});
+    if (S > 1 && K < 2048 && (int64_t)M * N * 4 * S > (int64_t(8) << 20)) S = 1;
+    return std::max(S, 1);
+}
+// ... and as far as the caller's scratch allows
+inline int splits_with(int epi, int64_t tiles, int nk, int per_cu, int min_steps, int M, int N, int K,
+                       const EpiArgs &ep) {
+    if (!ep.sk_part) return 1;
+    int S = splits_for(epi, tiles, nk, per_cu, min_steps, M, N, K);
+    while (S > 1 && (int64_t)S * M * N > ep.sk_part_floats) --S;
+    return S;
+}
+// workgroups per CU and minimum K steps per split of each kernel configuration
+constexpr int kRegPerCU = 2, kRegMinSteps = 2, kLdsMinSteps = 8;
+constexpr int lds_per_cu(int BM, int STAGES) { return BM == 64 ? 3 : (BM == 128 && STAGES == 2) ? 2 : 1; }
+
+// Second half of a split GEMM: v = (partial_0 + ... + partial_{S-1}) + bias,
+// added in split order (the result does not depend on the order in which
+// the splits finished), then the epilogue: STORE out = v, GELU out =
+// GELU_erf(v), RESID Z += ls * v.  Four consecutive columns per thread.
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int S, int M, int N,
+                                                            EpiArgs ep) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; // float4 index
+    const int64_t MN = (int64_t)M * N;
+    if (q * 4 >= MN) return;
+    const int64_t e = q * 4;
+    const int row = (int)(e / N), col = (int)(e - (int64_t)row * N);
+    float4 v = reinterpret_cast<const float4 *>(part)[q];
+    for (int sp = 1; sp < S; ++sp) {
+        const float4 p = reinterpret_cast<const float4 *>(part + sp * MN)[q];
+        v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    }
+    float r[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] += ep.bias ? ep.bias[col + j] : 0.0f;
+    if constexpr (EPI == EPI_RESID) {
+        float4 *z = reinterpret_cast<float4 *>(ep.Z + (int64_t)row * ep.ldz + col);
+        float4 zz = *z;
+        const float l0 = ep.ls ? ep.ls[col] : 1.0f, l1 = ep.ls ? ep.ls[col + 1] : 1.0f;
+        const float l2 = ep.ls ? ep.ls[col + 2] : 1.0f, l3 = ep.ls ? ep.ls[col + 3] : 1.0f;
+        zz.x += l0 * r[0]; zz.y += l1 * r[1]; zz.z += l2 * r[2]; zz.w += l3 * r[3];
+        *z = zz;
+    } else {
+        if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = gelu_erf(r[j]);
+        }
+        T *o = reinterpret_cast<T *>(ep.out) + (int64_t)row * ep.ldo + col;
+        if constexpr (sizeof(T) == 4) {
+            *reinterpret_cast<float4 *>(o) = make_float4(r[0], r[1], r[2], r[3]);
+        } else {
+            *reinterpret_cast<uint2 *>(o) = make_uint2(pack2<T>(r[0], r[1]), pack2<T>(r[2], r[3]));
+        }
+    }
+}
+
+template <typename T, int EPI>
+hipError_t launch_reduce(int S, int M, int N, const EpiArgs &ep, hipStream_t s) {
+    if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
+        const int64_t n4 = (int64_t)M * N / 4;
+        hipLaunchKernelGGL((splitk_reduce_kernel<T, EPI>), dim3((unsigned)cdiv(n4, 256)), dim3(256), 0, s, ep.sk_part,
+                           S, M, N, ep);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+// register-staged kernel, BM x BM tiles
+template <typename T, int EPI, int BM, bool FAST>
 hipError_t launch_t(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K,
                     const EpiArgs &ep, hipStream_t s) {
-    constexpr int BM = 128, BN = 128;
+    constexpr int BN = BM;
     const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, EPI, FAST>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0,
-                       s, reinterpret_cast<const T *>(A), lda, reinterpret_cast<const T *>(W), ldw, M, N, K, tiles_n,
-                       ep);
-    return hipGetLastError();
+    EpiArgs e = ep;
+    e.splits = splits_with(EPI, (int64_t)tiles_m * tiles_n, (int)cdiv(K, 8 * Elem<T>::kPerChunk), kRegPerCU,
+                           kRegMinSteps, M, N, K, ep);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, EPI, FAST>), dim3((unsigned)(tiles_m * tiles_n * e.splits)),
+                       dim3(kThreads), 0, s, reinterpret_cast<const T *>(A), lda, reinterpret_cast<const T *>(W),
+                       ldw, M, N, K, tiles_n, e);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || e.splits == 1) return err;
+    return launch_reduce<T, EPI>(e.splits, M, N, e, s);
 }
 
 template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, bool WQ = false>
@@ -836,12 +949,17 @@ hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, in
                       hipStream_t s) {
     const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
     const int64_t wbytes = WQ ? 1 : (int64_t)sizeof(T);
+    EpiArgs e = ep;
+    e.splits = splits_with(EPI, (int64_t)tiles_m * tiles_n, K / (NCH * Elem<T>::kPerChunk), lds_per_cu(BM, STAGES),
+                           kLdsMinSteps, M, N, K, ep);
     hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, WQ>),
-                       dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WGM * WGN), 0, s,
+                       dim3((unsigned)(tiles_m * tiles_n * e.splits)), dim3(64 * WGM * WGN), 0, s,
                        reinterpret_cast<const T *>(A), lda, W, ldw, M, N, K, tiles_n,
                        (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * wbytes),
-                       WQ ? (int)((int64_t)(K / 64) * N * 2) : 0, ep);
-    return hipGetLastError();
+                       WQ ? (int)((int64_t)(K / 64) * N * 2) : 0, e);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || e.splits == 1) return err;
+    return launch_reduce<T, EPI>(e.splits, M, N, e, s);
 }
 
 // Tile configuration (measured on the ViT-L shapes: M = 4096, N = 1024 ..
@@ -879,6 +997,8 @@ inline int pick_tile(int M, int N, bool fast, bool fp32) {
     if (cdiv(M, 128) * cdiv(N, 128) <= kCUs) return TILE_128x128_DEEP;
     return TILE_128x128;
 }
+
+inline bool reg_small_tiles(int M, int N) { return cdiv(M, 128) * cdiv(N, 128) < 128; }
 
 template <typename T, int EPI>
 hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K,
@@ -918,8 +1038,14 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
         default: break;
         }
     }
-    if (fast) return launch_t<T, EPI, true>(A, lda, W, ldw, M, N, K, ep, s);
-    return launch_t<T, EPI, false>(A, lda, W, ldw, M, N, K, ep, s);
+    // register-staged kernel: 64 x 64 tiles when 128 x 128 ones would leave
+    // more than half of the CUs idle
+    if (reg_small_tiles(M, N)) {
+        if (fast) return launch_t<T, EPI, 64, true>(A, lda, W, ldw, M, N, K, ep, s);
+        return launch_t<T, EPI, 64, false>(A, lda, W, ldw, M, N, K, ep, s);
+    }
+    if (fast) return launch_t<T, EPI, 128, true>(A, lda, W, ldw, M, N, K, ep, s);
+    return launch_t<T, EPI, 128, false>(A, lda, W, ldw, M, N, K, ep, s);
 }
 
 template <typename T>
@@ -936,6 +1062,29 @@ hipError_t launch_epi(int epi, const void *A, int64_t lda, const void *W, int64_
 }
 
 } // namespace
+
+int64_t gemm_splitk_floats(int dtype, int epi, int M, int N, int K, bool wq) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    int bm, nk, per_cu, min_steps;
+    if (dtype != DT_F32 && (K % 64 == 0 || wq)) {
+        switch (pick_tile(M, N, true, false)) {
+        case TILE_256x256: bm = 256; per_cu = lds_per_cu(256, 2); break;
+        case TILE_128x128: bm = 128; per_cu = lds_per_cu(128, 2); break;
+        case TILE_128x128_DEEP: bm = 128; per_cu = lds_per_cu(128, VITENC_DEEP_STAGES); break;
+        default: bm = 64; per_cu = lds_per_cu(64, 3); break;
+        }
+        nk = K / 64;
+        min_steps = kLdsMinSteps;
+    } else {
+        bm = reg_small_tiles(M, N) ? 64 : 128;
+        nk = (int)cdiv(K, dtype == DT_F32 ? 32 : 64);
+        per_cu = kRegPerCU;
+        min_steps = kRegMinSteps;
+    }
+    const int64_t tiles = cdiv(M, bm) * cdiv(N, bm);
+    const int S = splits_for(epi, tiles, nk, per_cu, min_steps, M, N, K);
+    return S > 1 ? (int64_t)S * M * N : 0;
+}
 
 hipError_t launch_gemm(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N,
                        int K, const EpiArgs &ep, hipStream_t s) {

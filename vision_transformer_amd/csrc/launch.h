@@ -52,7 +52,18 @@ struct EpiArgs {
     // block, laid out [K/64][N][2] (the two blocks of a 64-column slab of a
     // row side by side); needs K % 64 == 0, N % 8 == 0, no kwrap
     const uint8_t *wscale = nullptr;
+    // split-K scratch: when sk_part is set the launcher may split K over S
+    // workgroups per tile (STORE, GELU and RESID epilogues); each writes its
+    // raw fp32 partial [M, N] to sk_part + split * M * N and a second kernel
+    // adds the S partials in split order and applies the epilogue.
+    float *sk_part = nullptr;
+    int64_t sk_part_floats = 0;
+    int splits = 1; // set by the launcher
 };
+
+// Split-K scratch floats a GEMM of this shape can use (0: it does not split;
+// the launcher splits only when the tiles leave most of the CUs idle).
+int64_t gemm_splitk_floats(int dtype, int epi, int M, int N, int K, bool wq);
 
 // Patch embedding in a 16-bit type with K a multiple of 64 stores each pixel
 // as two values, hi = round(x) and lo = round(x - hi), in the two halves of a
@@ -154,6 +165,8 @@ struct BlockBufs {
     float *Z = nullptr;              // fp32 [B*N, D]
     void *Y = nullptr, *Q = nullptr, *K = nullptr, *Vt = nullptr, *O = nullptr, *U = nullptr;
     float *attn_scratch = nullptr;   // attention_scratch_floats(...) floats when prefix > 0
+    float *sk_part = nullptr;        // split-K scratch (EpiArgs::sk_part), or none
+    int64_t sk_part_floats = 0;
 };
 // *what names the failing launch
 hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_weights &w, hipStream_t s,

@@ -345,15 +345,8 @@ class Predictor:
              "norm_b": f32_to_device(w.norm_b, device), "proj_w": to_device(w.store["proj_w"], dt, device),
              "proj_b": f32_to_device(w.proj_b, device)}
         blocks = []
-        wq = hp.get("weight_format", WEIGHTS_PLAIN) == WEIGHTS_MXFP8
         for b in w.blocks:
-            d = {}
-            for n in QUANT_MATRICES:
-                if wq:
-                    # fp32 matrices quantised on the device into codes and block scales
-                    d[n], d[n[:-2] + "_s"] = quantize_mxfp8(f32_to_device(b.store[n], device))
-                else:
-                    d[n] = to_device(b.store[n], dt, device)
+            d = {n: to_device(b.store[n], dt, device) for n in QUANT_MATRICES}
             for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b"):
                 d[n] = f32_to_device(getattr(b, n), device)
             blocks.append(d)
@@ -430,15 +423,8 @@ class Head:
         for n in ("q_w", "k_w", "v_w", "up_w", "down_w", "cls_w"):
             t[n] = to_device(w.store[n], dt, device)
         blocks = []
-        wq = hp.get("weight_format", WEIGHTS_PLAIN) == WEIGHTS_MXFP8
         for b in w.blocks:
-            d = {}
-            for n in QUANT_MATRICES:
-                if wq:
-                    # fp32 matrices quantised on the device into codes and block scales
-                    d[n], d[n[:-2] + "_s"] = quantize_mxfp8(f32_to_device(b.store[n], device))
-                else:
-                    d[n] = to_device(b.store[n], dt, device)
+            d = {n: to_device(b.store[n], dt, device) for n in QUANT_MATRICES}
             for n in ("qkv_b", "out_b", "up_b", "down_b", "ln1_w", "ln1_b", "ln2_w", "ln2_b"):
                 d[n] = f32_to_device(getattr(b, n), device)
             blocks.append(d)
