@@ -49,14 +49,15 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (MFMA / packed vector)
 COPY_BYTES = 256 << 20        # plain device copy used to calibrate the HBM byte counters
 CSRC = os.path.join(ROOT, "vision_transformer_amd", "csrc")
 # kernel-breakdown name -> (pattern of its device kernel's mangled name, sources it is compiled from).
-# The GEMM epilogue is the last template argument of gemm_lds_kernel (STORE 0, GELU 1, RESID 2,
-# PATCH 3, QKV 4); the out and down projections share the RESID instantiation.
+# The GEMM epilogue is the second-to-last template argument of gemm_lds_kernel (STORE 0, GELU 1,
+# RESID 2, PATCH 3, QKV 4; the last one is the 8-bit weight flag); the out and down projections
+# share the RESID instantiation.
 KERNEL_SOURCES = {
     "attention": (r"attention_lds_kernel", ["attention.hip", "common.h", "launch.h"]),
-    "qkv_gemm": (r"gemm_lds_kernel.*Li4EEEv", ["gemm.hip", "common.h", "launch.h"]),
-    "up_gemm": (r"gemm_lds_kernel.*Li1EEEv", ["gemm.hip", "common.h", "launch.h"]),
-    "down_gemm": (r"gemm_lds_kernel.*Li2EEEv", ["gemm.hip", "common.h", "launch.h"]),
-    "out_gemm": (r"gemm_lds_kernel.*Li2EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "qkv_gemm": (r"gemm_lds_kernel.*Li4ELb0EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "up_gemm": (r"gemm_lds_kernel.*Li1ELb0EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "down_gemm": (r"gemm_lds_kernel.*Li2ELb0EEEv", ["gemm.hip", "common.h", "launch.h"]),
+    "out_gemm": (r"gemm_lds_kernel.*Li2ELb0EEEv", ["gemm.hip", "common.h", "launch.h"]),
     "layernorm": (r"layernorm", ["elementwise.hip", "common.h", "launch.h"]),
 }
 

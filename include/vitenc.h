@@ -403,16 +403,18 @@ int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32
  * vitenc_op_qkv_rope; O: T [B, N, H*hd] (heads concatenated).  attn_mode
  * FULL or BLOCK_CAUSAL with frames of `tokens_per_frame` patch tokens after
  * n_prefix prefix tokens (0 <= n_prefix < N).  scratch: fp32 device memory
- * of vitenc_attention_scratch_floats() floats for the prefix rows (their
- * partial results over runs of keys), NULL when that is 0; contents undefined
- * on entry and exit. */
+ * of vitenc_attention_scratch_floats() floats for the rows computed split
+ * over runs of keys (their partial results), NULL when that is 0; contents
+ * undefined on entry and exit. */
 vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt,
                                   int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
                                   int32_t attn_mode, int32_t n_prefix,
                                   int32_t tokens_per_frame, float *scratch, void *O, void *stream);
 
-/* Floats of scratch vitenc_op_attention needs for these sizes (0 without
- * prefix rows; -1 for invalid sizes). */
+/* Floats of scratch vitenc_op_attention needs for these sizes: for the
+ * prefix rows, and for every row when the query tiles of 128 would make fewer
+ * than 16 workgroups (then a full-attention fp32 call computes all rows split
+ * over runs of keys); 0 when neither applies, -1 for invalid sizes. */
 int64_t vitenc_attention_scratch_floats(int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
                                         int32_t n_prefix);
 

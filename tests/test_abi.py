@@ -257,9 +257,12 @@ def test_step_entry_point_refusals():
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 48, 0, 0, 0, None, FAKE, None) == 6
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 1, 0, 0, None, FAKE, None) == 2
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 0, 64, 0, None, FAKE, None) == 2
-    # prefix rows need the scratch
-    assert L.vitenc_attention_scratch_floats(1, 257, 2, 64, 1) == 2 * 2 * 66
-    assert L.vitenc_attention_scratch_floats(1, 256, 2, 64, 0) == 0
+    # prefix rows need the scratch (8 heads, 9 runs of 256 keys, 64 + 2 floats each)
+    assert L.vitenc_attention_scratch_floats(1, 2049, 8, 64, 1) == 8 * 9 * 66
+    assert L.vitenc_attention_scratch_floats(1, 2048, 8, 64, 0) == 0
+    # and every row when the query tiles make fewer than 16 workgroups (3 heads x 2 tiles)
+    assert L.vitenc_attention_scratch_floats(1, 257, 3, 64, 1) == 3 * 257 * 2 * 66
+    assert L.vitenc_attention_scratch_floats(1, 256, 3, 64, 0) == 3 * 256 * 1 * 66
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 257, 2, 64, 0, 1, 0, None, FAKE, None) == 3
     assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 2, 2, 2, 0,
                                 FAKE, FAKE, FAKE, FAKE, None) == 2          # 8 patches + 0 prefix != 17

@@ -724,6 +724,13 @@ __global__ __launch_bounds__(64) void prefix_merge_kernel(const float *__restric
 // prefix_attention_kernel (all of them: a model has at most a few)
 inline int query_begin(int N, int p) { return p < N ? p : 0; }
 
+// When the query tiles make fewer than kRowSplitTiles workgroups (a single
+// small image: 257 tokens and 3 heads make 6), most CUs would idle while each
+// tile walks every key; with full attention all rows then take the row
+// kernels above instead (a workgroup per row and run of keys, then the merge).
+constexpr int kRowSplitTiles = 16;
+inline bool row_split(int B, int N, int H, int qb) { return (int64_t)B * H * cdiv(N - qb, BQ) < kRowSplitTiles; }
+
 template <typename T, int HD>
 hipError_t launch_prefix(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int qb,
                          float scale_log2, float *scratch, void *O, hipStream_t s) {
@@ -762,6 +769,8 @@ hipError_t launch_t<float, 64>(const void *Q, const void *K, const void *Vt, int
                                int p, int S, float *scratch, void *O, hipStream_t s) {
     const int qb = query_begin(N, p);
     const float scale_log2 = 1.4426950408889634f / 8.0f;
+    if (!causal && row_split(B, N, H, qb))
+        return launch_prefix<float, 64>(Q, K, Vt, B, N, H, ldv, N, scale_log2, scratch, O, s);
     dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, BQ));
     hipLaunchKernelGGL((attention_kernel<float, 64>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
                        reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
@@ -774,6 +783,8 @@ hipError_t launch_t<float, 32>(const void *Q, const void *K, const void *Vt, int
                                int p, int S, float *scratch, void *O, hipStream_t s) {
     const int qb = query_begin(N, p);
     const float scale_log2 = 1.4426950408889634f / sqrtf(32.0f);
+    if (!causal && row_split(B, N, H, qb))
+        return launch_prefix<float, 32>(Q, K, Vt, B, N, H, ldv, N, scale_log2, scratch, O, s);
     dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, BQ));
     hipLaunchKernelGGL((attention_kernel<float, 32>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
                        reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
@@ -793,7 +804,8 @@ hipError_t launch_hd(int head_dim, const void *Q, const void *K, const void *Vt,
 
 int64_t attention_scratch_floats(int B, int N, int H, int head_dim, int n_prefix) {
     const int qb = query_begin(N, n_prefix);
-    return (int64_t)B * H * qb * cdiv(N, kPrefixKeys) * (head_dim + 2);
+    const int64_t rows = (int64_t)B * H * (row_split(B, N, H, qb) ? N : qb);
+    return rows * cdiv(N, kPrefixKeys) * (head_dim + 2);
 }
 
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N, int H,

@@ -52,7 +52,7 @@ vitenc_status validate(const vitenc_head_hparams *hp) {
 struct HeadPlan {
     int B, N, M, D, F, H, hd, ldv, NC, C;
     size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U;
-    size_t off_q, off_u, off_ub, off_s, off_stats, off_P, off_ybar, off_y, off_h, off_f, total;
+    size_t off_q, off_u, off_ub, off_s, off_stats, off_P, off_ybar, off_y, off_h, off_f, off_attn, total;
 };
 
 vitenc_status make_plan(const vitenc_head *hd, int B, int N, HeadPlan &pl) {
@@ -83,6 +83,8 @@ vitenc_status make_plan(const vitenc_head *hd, int B, int N, HeadPlan &pl) {
         pl.off_O = take(M * D * es);
         pl.off_U = take(M * (size_t)pl.F * es);
     }
+    // the pooler blocks' attention has no prefix rows, but a small grid splits every row over runs of keys
+    pl.off_attn = hp.n_pool_layers > 0 ? take((size_t)attention_scratch_floats(B, N, H, pl.hd, 0) * 4) : 0;
     pl.off_q = take(D * 4);
     pl.off_u = take(H * D * 4);
     pl.off_ub = take(H * 4);
@@ -185,6 +187,7 @@ vitenc_status vitenc_head_forward(const vitenc_head *h, const float *tokens, int
         BlockBufs bb;
         bb.Z = Z; bb.Y = ws + pl.off_Y; bb.Q = ws + pl.off_Q; bb.K = ws + pl.off_K; bb.Vt = ws + pl.off_V;
         bb.O = ws + pl.off_O; bb.U = ws + pl.off_U;
+        bb.attn_scratch = reinterpret_cast<float *>(ws + pl.off_attn);
         for (int l = 0; l < hp.n_pool_layers; ++l) {
             const char *what = "pooler block";
             const hipError_t e = run_block(g, bb, h->blocks[l], s, &what);

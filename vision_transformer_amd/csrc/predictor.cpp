@@ -60,7 +60,7 @@ struct PredPlan {
     int B, nc, nt, N, M, D, De, F, nh, hd, ldv, lda_e;
     bool split;
     size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_Zt, off_rctx, off_rtgt, off_tok, off_rope,
-        total;
+        off_attn, total;
 };
 
 vitenc_status make_plan(const vitenc_predictor *p, int B, int nc, int nt, PredPlan &pl) {
@@ -100,6 +100,8 @@ vitenc_status make_plan(const vitenc_predictor *p, int B, int nc, int nt, PredPl
     pl.off_tok = take(M * 4);
     const int d = 2 * ((pl.hd / 3) / 2);
     pl.off_rope = take((size_t)(hp.grid_t + hp.grid_h + hp.grid_w) * d * 2 * 4);
+    // attention keeps no prefix rows here, but a small grid splits every row over runs of keys
+    pl.off_attn = take((size_t)attention_scratch_floats(B, pl.N, pl.nh, pl.hd, 0) * 4);
     pl.total = off;
     return VITENC_OK;
 }
@@ -219,6 +221,7 @@ vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens,
     BlockBufs bb;
     bb.Z = Z; bb.Y = Y; bb.Q = ws + pl.off_Q; bb.K = ws + pl.off_K; bb.Vt = ws + pl.off_V; bb.O = ws + pl.off_O;
     bb.U = ws + pl.off_U;
+    bb.attn_scratch = reinterpret_cast<float *>(ws + pl.off_attn);
     for (int l = 0; l < hp.n_layer; ++l) {
         const char *what = "block";
         const hipError_t e = run_block(g, bb, p->blocks[l], s, &what);
