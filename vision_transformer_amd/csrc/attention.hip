@@ -628,7 +628,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
 constexpr int kPrefixThreads = 256;
 constexpr int kPrefixKeys = 256;
 
-template <typename T, int HD>
+// QR query rows of one (item, head) per workgroup (the rows of a row-split
+// call share their K and V^T reads; a prefix call has QR = 1): thread k of the
+// run scores key k against each row, the weights go through LDS, and thread
+// (group, d) accumulates output dim d over its key group for each row.
+template <typename T, int HD, int QR>
 __global__ __launch_bounds__(kPrefixThreads) void prefix_partial_kernel(const T *__restrict__ Q,
                                                                         const T *__restrict__ K,
                                                                         const T *__restrict__ Vt, int N, int ldv,
@@ -639,64 +643,97 @@ __global__ __launch_bounds__(kPrefixThreads) void prefix_partial_kernel(const T 
     constexpr int G = kPrefixThreads / HD;   // key groups of the PV step
     constexpr int VE = 16 / (int)sizeof(T);  // keys per 16-byte V^T load
     static_assert(kPrefixKeys <= kPrefixThreads, "one key per thread");
-    __shared__ float ss[kPrefixKeys];
-    __shared__ float sq[HD];
-    __shared__ float red[NW];
-    __shared__ float so[G][HD];
-    const int row = blockIdx.x, bh = row / p, pq = row - bh * p;
+    static_assert(QR * HD <= kPrefixThreads, "one query element per thread");
+    __shared__ float ss[QR][kPrefixKeys];
+    __shared__ float sq[QR][HD];
+    __shared__ float red[2][QR][NW];
+    __shared__ float so[QR][G][HD];
+    const int gpb = (p + QR - 1) / QR;       // row groups per (item, head)
+    const int bh = blockIdx.x / gpb, pq0 = (blockIdx.x - bh * gpb) * QR, nq = min(QR, p - pq0);
     const int run = blockIdx.y, c0 = run * kPrefixKeys, n = min(kPrefixKeys, N - c0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int d = tid % HD, grp = tid / HD;
-    if (tid < HD) sq[tid] = to_f32(Q[((int64_t)bh * N + pq) * HD + tid]) * scale_log2;
+    if (tid < QR * HD) {
+        const int q = tid / HD;
+        sq[q][d] = q < nq ? to_f32(Q[((int64_t)bh * N + pq0 + q) * HD + d]) * scale_log2 : 0.0f;
+    }
     __syncthreads();
-    float sc = -INFINITY;
+    float sc[QR];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) sc[q] = -INFINITY;
     if (tid < n) {
-        sc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < QR; ++q) sc[q] = 0.0f;
         const T *kr = K + ((int64_t)bh * N + c0 + tid) * HD;
 #pragma unroll
         for (int c = 0; c < HD / KPC; ++c) {
             const Chunk ch = load_chunk(kr + c * KPC);
             const T *e = reinterpret_cast<const T *>(&ch);
 #pragma unroll
-            for (int u = 0; u < KPC; ++u) sc = fmaf(sq[c * KPC + u], to_f32(e[u]), sc);
+            for (int u = 0; u < KPC; ++u) {
+                const float kv = to_f32(e[u]);
+#pragma unroll
+                for (int q = 0; q < QR; ++q) sc[q] = fmaf(sq[q][c * KPC + u], kv, sc[q]);
+            }
         }
     }
-    const float mw = wave_max(sc);
-    if (lane == 0) red[wave] = mw;
-    __syncthreads();
-    float m = red[0];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w]);
-    const float wgt = tid < n ? __builtin_amdgcn_exp2f(sc - m) : 0.0f;
-    ss[tid] = wgt;
-    const float lw = wave_sum(wgt);
+    for (int q = 0; q < QR; ++q) {
+        const float mw = wave_max(sc[q]);
+        if (lane == 0) red[0][q][wave] = mw;
+    }
     __syncthreads();
-    if (lane == 0) red[wave] = lw;
+    float m[QR];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) {
+        m[q] = red[0][q][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m[q] = fmaxf(m[q], red[0][q][w]);
+        const float wgt = tid < n ? __builtin_amdgcn_exp2f(sc[q] - m[q]) : 0.0f;
+        ss[q][tid] = wgt;
+        const float lw = wave_sum(wgt);
+        if (lane == 0) red[1][q][wave] = lw;
+    }
+    __syncthreads();
     const T *vrow = Vt + ((int64_t)bh * HD + d) * ldv + c0;
-    float acc = 0.0f;
+    float acc[QR];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) acc[q] = 0.0f;
     const int full = n / VE * VE;
     for (int k = grp * VE; k < full; k += G * VE) {
         const Chunk ch = load_chunk(vrow + k);
         const T *e = reinterpret_cast<const T *>(&ch);
 #pragma unroll
-        for (int u = 0; u < VE; ++u) acc = fmaf(ss[k + u], to_f32(e[u]), acc);
+        for (int u = 0; u < VE; ++u) {
+            const float vv = to_f32(e[u]);
+#pragma unroll
+            for (int q = 0; q < QR; ++q) acc[q] = fmaf(ss[q][k + u], vv, acc[q]);
+        }
     }
-    for (int k = full + grp; k < n; k += G) acc = fmaf(ss[k], to_f32(vrow[k]), acc);
-    so[grp][d] = acc;
+    for (int k = full + grp; k < n; k += G) {
+        const float vv = to_f32(vrow[k]);
+#pragma unroll
+        for (int q = 0; q < QR; ++q) acc[q] = fmaf(ss[q][k], vv, acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < QR; ++q) so[q][grp][d] = acc[q];
     __syncthreads();
-    float *out = part + ((int64_t)row * gridDim.y + run) * (HD + 2);
-    if (tid < HD) {
-        float t = 0.0f;
+    if (tid < QR * HD) {
+        const int q = tid / HD;
+        if (q < nq) {
+            float t = 0.0f;
 #pragma unroll
-        for (int g2 = 0; g2 < G; ++g2) t += so[g2][tid];
-        out[2 + tid] = t;
-    }
-    if (tid == 0) {
-        float l = 0.0f;
+            for (int g2 = 0; g2 < G; ++g2) t += so[q][g2][d];
+            float *out = part + (((int64_t)bh * p + pq0 + q) * gridDim.y + run) * (HD + 2);
+            out[2 + d] = t;
+            if (d == 0) {
+                float l = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) l += red[w];
-        out[0] = m;
-        out[1] = l;
+                for (int w = 0; w < NW; ++w) l += red[1][q][w];
+                out[0] = m[q];
+                out[1] = l;
+            }
+        }
     }
 }
 
@@ -731,15 +768,16 @@ inline int query_begin(int N, int p) { return p < N ? p : 0; }
 constexpr int kRowSplitTiles = 16;
 inline bool row_split(int B, int N, int H, int qb) { return (int64_t)B * H * cdiv(N - qb, BQ) < kRowSplitTiles; }
 
-template <typename T, int HD>
+template <typename T, int HD, int QR = 1>
 hipError_t launch_prefix(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int qb,
                          float scale_log2, float *scratch, void *O, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || qb == 0) return e;
     if (!scratch) return hipErrorInvalidValue;
     const int runs = (int)cdiv(N, kPrefixKeys), rows = B * H * qb;
-    hipLaunchKernelGGL((prefix_partial_kernel<T, HD>), dim3((unsigned)rows, (unsigned)runs), dim3(kPrefixThreads), 0,
-                       s, reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
+    const int groups = B * H * (int)cdiv(qb, QR);
+    hipLaunchKernelGGL((prefix_partial_kernel<T, HD, QR>), dim3((unsigned)groups, (unsigned)runs),
+                       dim3(kPrefixThreads), 0, s, reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
                        reinterpret_cast<const T *>(Vt), N, ldv, qb, scale_log2, scratch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -770,7 +808,7 @@ hipError_t launch_t<float, 64>(const void *Q, const void *K, const void *Vt, int
     const int qb = query_begin(N, p);
     const float scale_log2 = 1.4426950408889634f / 8.0f;
     if (!causal && row_split(B, N, H, qb))
-        return launch_prefix<float, 64>(Q, K, Vt, B, N, H, ldv, N, scale_log2, scratch, O, s);
+        return launch_prefix<float, 64, 4>(Q, K, Vt, B, N, H, ldv, N, scale_log2, scratch, O, s);
     dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, BQ));
     hipLaunchKernelGGL((attention_kernel<float, 64>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
                        reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,
@@ -784,7 +822,7 @@ hipError_t launch_t<float, 32>(const void *Q, const void *K, const void *Vt, int
     const int qb = query_begin(N, p);
     const float scale_log2 = 1.4426950408889634f / sqrtf(32.0f);
     if (!causal && row_split(B, N, H, qb))
-        return launch_prefix<float, 32>(Q, K, Vt, B, N, H, ldv, N, scale_log2, scratch, O, s);
+        return launch_prefix<float, 32, 4>(Q, K, Vt, B, N, H, ldv, N, scale_log2, scratch, O, s);
     dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, BQ));
     hipLaunchKernelGGL((attention_kernel<float, 32>), grid, dim3(kThreads), 0, s, reinterpret_cast<const float *>(Q),
                        reinterpret_cast<const float *>(K), reinterpret_cast<const float *>(Vt), N, H, ldv, causal, p,

@@ -857,7 +857,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
 inline int splits_for(int epi, int64_t tiles, int nk, int per_cu, int min_steps, int M, int N, int K) {
     if (!(epi == EPI_STORE || epi == EPI_GELU || epi == EPI_RESID) || N % 4 != 0) return 1;
     const int64_t target = 256 * (int64_t)per_cu;
-    if (2 * tiles > target) return 1; // measured: 400 tiles of 64 x 64 (target 768) run slower split
+    // measured: 400 tiles of 64 x 64 (target 768) run slower split, and so do
+    // GEMMs with fewer than four splits' worth of K steps (the reduction's
+    // launch costs more than the split saves)
+    if (2 * tiles > target || nk < 4 * min_steps) return 1;
     int S = (int)std::min<int64_t>({cdiv(target, tiles), (int64_t)nk / min_steps, 16});
     if (S > 1 && K < 2048 && (int64_t)M * N * 4 * S > (int64_t(8) << 20)) S = 1;
     return std::max(S, 1);
