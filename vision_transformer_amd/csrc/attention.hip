@@ -737,23 +737,52 @@ __global__ __launch_bounds__(kPrefixThreads) void prefix_partial_kernel(const T 
     }
 }
 
+// Merge of the runs of one row: 256 threads, a group of HD threads per share
+// of the runs (each thread one output dim), the shares added in a fixed order
+// at the end; loads of different runs are independent, so a thread keeps
+// several in flight.
+constexpr int kMergeThreads = 256;
+
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void prefix_merge_kernel(const float *__restrict__ part, int runs, int N, int H,
-                                                          int p, T *__restrict__ O) {
+__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(const float *__restrict__ part, int runs, int N,
+                                                                      int H, int p, T *__restrict__ O) {
+    constexpr int RG = kMergeThreads / HD;  // run groups
+    constexpr int NW = kMergeThreads / 64;
+    __shared__ float sacc[RG][HD];
+    __shared__ float sl[RG];
+    __shared__ float smax[NW];
     const int row = blockIdx.x, bh = row / p, pq = row - bh * p;
     const int b = bh / H, head = bh - b * H;
     const float *pr = part + (int64_t)row * runs * (HD + 2);
-    float M = -INFINITY;
-    for (int r = 0; r < runs; ++r) M = fmaxf(M, pr[(int64_t)r * (HD + 2)]);
-    for (int dd = threadIdx.x; dd < HD; dd += blockDim.x) {
-        float L = 0.0f, acc = 0.0f;
-        for (int r = 0; r < runs; ++r) {
-            const float *q = pr + (int64_t)r * (HD + 2);
-            const float f = __builtin_amdgcn_exp2f(q[0] - M);
-            L = fmaf(q[1], f, L);
-            acc = fmaf(q[2 + dd], f, acc);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float mx = -INFINITY;
+    for (int r = tid; r < runs; r += kMergeThreads) mx = fmaxf(mx, pr[(int64_t)r * (HD + 2)]);
+    mx = wave_max(mx);
+    if (lane == 0) smax[wave] = mx;
+    __syncthreads();
+    float M = smax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, smax[w]);
+    const int dd = tid % HD, rg = tid / HD;
+    float L = 0.0f, acc = 0.0f;
+#pragma unroll 4
+    for (int r = rg; r < runs; r += RG) {
+        const float *q = pr + (int64_t)r * (HD + 2);
+        const float f = __builtin_amdgcn_exp2f(q[0] - M);
+        L = fmaf(q[1], f, L);
+        acc = fmaf(q[2 + dd], f, acc);
+    }
+    sacc[rg][dd] = acc;
+    if (dd == 0) sl[rg] = L;
+    __syncthreads();
+    if (rg == 0) {
+        float a = 0.0f, l = 0.0f;
+#pragma unroll
+        for (int g2 = 0; g2 < RG; ++g2) {
+            a += sacc[g2][dd];
+            l += sl[g2];
         }
-        O[((int64_t)b * N + pq) * H * HD + head * HD + dd] = from_f32<T>(L > 0.0f ? acc / L : 0.0f);
+        O[((int64_t)b * N + pq) * H * HD + head * HD + dd] = from_f32<T>(l > 0.0f ? a / l : 0.0f);
     }
 }
 
@@ -781,8 +810,8 @@ hipError_t launch_prefix(const void *Q, const void *K, const void *Vt, int B, in
                        reinterpret_cast<const T *>(Vt), N, ldv, qb, scale_log2, scratch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefix_merge_kernel<T, HD>), dim3((unsigned)rows), dim3(64), 0, s, scratch, runs, N, H, qb,
-                       reinterpret_cast<T *>(O));
+    hipLaunchKernelGGL((prefix_merge_kernel<T, HD>), dim3((unsigned)rows), dim3(kMergeThreads), 0, s, scratch, runs,
+                       N, H, qb, reinterpret_cast<T *>(O));
     return hipGetLastError();
 }
 
