@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VITENC_ABI_VERSION 3
+#define VITENC_ABI_VERSION 4
 
 typedef enum {
     VITENC_OK = 0,
@@ -402,21 +402,28 @@ int64_t vitenc_rope_table_floats(int32_t head_dim, int32_t gt, int32_t gh, int32
  * O = softmax(Q K^T / sqrt(hd) + mask) V with Q, K, Vt in the layouts of
  * vitenc_op_qkv_rope; O: T [B, N, H*hd] (heads concatenated).  attn_mode
  * FULL or BLOCK_CAUSAL with frames of `tokens_per_frame` patch tokens after
- * n_prefix prefix tokens (0 <= n_prefix < N).  scratch: fp32 device memory
- * of vitenc_attention_scratch_floats() floats for the rows computed split
- * over runs of keys (their partial results), NULL when that is 0; contents
- * undefined on entry and exit. */
+ * n_prefix prefix tokens (0 <= n_prefix < N).  scratch: fp32 device memory,
+ * 16-byte aligned, of vitenc_attention_scratch_floats() floats for the
+ * partial results of rows or query tiles computed split over their keys, NULL
+ * when that is 0; contents undefined on entry and exit.  Errors: EINVAL for
+ * an unknown dtype or attn_mode or a misaligned scratch, ENULL for a missing
+ * pointer (scratch included when it is needed), ESHAPE for inconsistent
+ * sizes, EUNSUPPORTED for a head width other than 32 or 64. */
 vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt,
                                   int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
                                   int32_t attn_mode, int32_t n_prefix,
                                   int32_t tokens_per_frame, float *scratch, void *O, void *stream);
 
-/* Floats of scratch vitenc_op_attention needs for these sizes: for the
- * prefix rows, and for every row when the query tiles of 128 would make fewer
- * than 16 workgroups (then a full-attention fp32 call computes all rows split
- * over runs of keys); 0 when neither applies, -1 for invalid sizes. */
-int64_t vitenc_attention_scratch_floats(int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
-                                        int32_t n_prefix);
+/* Floats of scratch vitenc_op_attention needs for the same arguments: for
+ * the prefix rows (split over runs of 256 keys); in fp32, for every row when
+ * the query tiles of 128 would make fewer than 16 workgroups (a full-attention
+ * call then computes all rows that way); in 16-bit types with the block-causal
+ * mask, for the late query tiles computed as two halves of their keys when
+ * the grid is small (at most 1024 workgroups).  0 when none applies, -1 for
+ * invalid arguments. */
+int64_t vitenc_attention_scratch_floats(int32_t dtype, int32_t B, int32_t N, int32_t n_head,
+                                        int32_t head_dim, int32_t attn_mode, int32_t n_prefix,
+                                        int32_t tokens_per_frame);
 
 /* a8/a10 projection with bias, layer scale and residual: Z[M, Nout] (fp32)
  * += ls * (A[M, K] W[Nout, K]^T + b); ls may be NULL (= 1). */

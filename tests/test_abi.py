@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(V.SIGNATURES), "binding and header disagree"
-    assert L.vitenc_abi_version() == 3
+    assert L.vitenc_abi_version() == 4
 
 
 FAKE = 0x1000  # a non-NULL pointer that is never dereferenced: creation only validates
@@ -257,12 +257,33 @@ def test_step_entry_point_refusals():
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 48, 0, 0, 0, None, FAKE, None) == 6
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 1, 0, 0, None, FAKE, None) == 2
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 0, 64, 0, None, FAKE, None) == 2
+    S = L.vitenc_attention_scratch_floats
+    # (dtype, B, N, heads, hd, attn_mode, n_prefix, tokens_per_frame)
     # prefix rows need the scratch (8 heads, 9 runs of 256 keys, 64 + 2 floats each)
-    assert L.vitenc_attention_scratch_floats(1, 2049, 8, 64, 1) == 8 * 9 * 66
-    assert L.vitenc_attention_scratch_floats(1, 2048, 8, 64, 0) == 0
-    # and every row when the query tiles make fewer than 16 workgroups (3 heads x 2 tiles)
-    assert L.vitenc_attention_scratch_floats(1, 257, 3, 64, 1) == 3 * 257 * 2 * 66
-    assert L.vitenc_attention_scratch_floats(1, 256, 3, 64, 0) == 3 * 256 * 1 * 66
+    assert S(1, 1, 2049, 8, 64, 0, 1, 0) == 8 * 9 * 66
+    assert S(1, 1, 2048, 8, 64, 0, 0, 0) == 0
+    # in fp32 every row when the query tiles make fewer than 16 workgroups (3 heads x 2 tiles)
+    assert S(0, 1, 257, 3, 64, 0, 1, 0) == 3 * 257 * 2 * 66
+    assert S(0, 1, 256, 3, 64, 0, 0, 0) == 3 * 256 * 1 * 66
+    assert S(1, 1, 257, 3, 64, 0, 1, 0) == 3 * 1 * 2 * 66          # 16-bit: the prefix row only
+    assert S(0, 1, 257, 3, 64, 1, 1, 64) == 3 * 1 * 2 * 66          # fp32 block-causal: no row split
+    # block-causal 16-bit calls with a small grid split the late query tiles:
+    # 16 frames of 256 tokens after a CLS, 16 heads -> 32 query tiles of 128;
+    # tile qt walks 4 (qt // 2 + 1) + 1 key tiles of 64 (the CLS shifts the
+    # frames by one key), largest 65; those above 65 / 3 (25 and up: qt >= 10)
+    # are split: 22 tiles x 128 rows x 2 halves x (64 + 4) floats per head,
+    # after the prefix row's 17 runs x 66 floats (a multiple of 4 already)
+    pre = 16 * 17 * 66
+    assert S(1, 1, 4097, 16, 64, 1, 1, 256) == pre + 16 * 22 * 128 * 2 * 68
+    assert S(2, 1, 4097, 16, 64, 1, 1, 256) == pre + 16 * 22 * 128 * 2 * 68   # fp16 alike
+    assert S(1, 1, 4097, 16, 64, 0, 1, 256) == pre                  # full attention: none
+    assert S(1, 2, 4097, 16, 64, 1, 1, 256) == 2 * (pre + 16 * 22 * 128 * 2 * 68)  # 1024 workgroups
+    assert S(1, 3, 4097, 16, 64, 1, 1, 256) == 3 * pre              # 1536 workgroups: not split
+    # 3 heads: the prefix area (3 x 17 x 66 = 3366 floats) is padded to 3368
+    assert S(1, 1, 4097, 3, 64, 1, 1, 256) == 3368 + 3 * 22 * 128 * 2 * 68
+    assert S(1, 1, 4097, 16, 64, 1, 1, 4096) == pre                 # one frame: nothing to balance
+    assert S(7, 1, 64, 1, 64, 0, 0, 0) == -1 and S(1, 1, 64, 1, 64, 2, 0, 0) == -1
+    assert S(1, 1, 64, 1, 64, 1, 0, 0) == -1
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 257, 2, 64, 0, 1, 0, None, FAKE, None) == 3
     assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 2, 2, 2, 0,
                                 FAKE, FAKE, FAKE, FAKE, None) == 2          # 8 patches + 0 prefix != 17

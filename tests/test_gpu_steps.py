@@ -163,6 +163,10 @@ def test_qkv_rope(gpu_lib, dtype, case):
     dict(B=1, H=2, N=257, hd=64, mode=0, p=1, S=0),
     dict(B=1, H=2, N=1 + 4 * 256, hd=64, mode=1, p=1, S=256),
     dict(B=2, H=1, N=1 + 33, hd=32, mode=0, p=1, S=0),
+    # 16-bit calls split their late query tiles over two halves of the keys:
+    # frames that straddle query tiles, a ragged last query tile and key tile
+    dict(B=2, H=3, N=1 + 6 * 200, hd=64, mode=1, p=1, S=200),
+    dict(B=1, H=2, N=8 * 128, hd=32, mode=1, p=0, S=128),
 ])
 def test_attention(gpu_lib, dtype, case):
     from vision_transformer_amd import vitenc as V
@@ -202,11 +206,12 @@ def test_pool(gpu_lib, cls, p):
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
-def test_linear_wide_tiles(gpu_lib, dtype):
+@pytest.mark.parametrize("M,N,K", [(4133, 4096, 256), (4000, 3072, 256)])
+def test_linear_wide_tiles(gpu_lib, dtype, M, N, K):
     """Shapes with enough tiles for the 256 x 256 direct-to-LDS kernel, with a
-    ragged last row block (M = 4133)."""
+    ragged last row block (M = 4133), and for 1.5 rounds of its 128 x 128
+    tiles (width 3072, the last row block ragged)."""
     from vision_transformer_amd import vitenc as V
-    M, N, K = 4133, 4096, 256
     say(f"linear wide dtype={dtype} M={M} N={N} K={K}")
     rng = np.random.default_rng(11)
     A = rng.standard_normal((M, K)).astype(np.float32)

@@ -195,7 +195,8 @@ vitenc_status make_plan(const vitenc_model *m, int32_t B, int32_t T, int32_t H, 
     pl.off_rope = take((size_t)(pl.gt + pl.gh + pl.gw) * d * 2 * 4);
     pl.off_tok = take((size_t)pl.Np * 4);
     pl.off_pos = pl.resample ? take((size_t)pl.N * pl.D * 4) : 0;
-    pl.off_attn = take((size_t)attention_scratch_floats(B, pl.N, pl.nh, pl.hd, pl.p) * 4);
+    pl.off_attn = take(
+        (size_t)attention_scratch_floats(hp.dtype, B, pl.N, pl.nh, pl.hd, hp.attn_mode, pl.p, pl.gh * pl.gw) * 4);
     // split-K scratch for the GEMMs whose tiles leave most CUs idle (small inputs)
     {
         const bool wq = hp.weight_format == VITENC_WEIGHTS_MXFP8;

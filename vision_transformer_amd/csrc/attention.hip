@@ -77,13 +77,14 @@ __device__ __forceinline__ int wave_max_i(int v) {
     return v;
 }
 
-__device__ __forceinline__ void key_interval(int q, int N, int causal, int p, int S, int &lo, int &hi) {
+__host__ __device__ __forceinline__ void key_interval(int q, int N, int causal, int p, int S, int &lo, int &hi) {
     if (!causal || q < p) {
         lo = 0;
         hi = N;
     } else {
         lo = p;
-        hi = min(N, p + ((q - p) / S + 1) * S);
+        const int end = p + ((q - p) / S + 1) * S;
+        hi = end < N ? end : N;
     }
 }
 
@@ -417,11 +418,32 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, Chunk *dst
 }
 __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Order in which the workgroups of the direct-to-LDS kernel take the query
+// tiles, and which tiles are computed as two workgroups over halves of their
+// keys.  With the block-causal mask a late frame's query tile sees up to
+// (frames) times the keys of frame 0's; when the grid is one or two rounds of
+// workgroups over the CUs, the late tiles alone then set the kernel's time.
+// When the largest key count is at least twice the smallest, a tile is split
+// in two when its key tiles exceed a third of the largest count: each half writes its unnormalised partial (o, running max,
+// running sum) to scratch and split_merge_kernel combines the two.  Jobs run
+// largest first.  n = 0: no split, tiles in reverse order (the heaviest last
+// tiles first), one workgroup each.
+constexpr int kMaxJobs = 480;
+constexpr int kSplitMaxWorkgroups = 1024; // above this the dispatcher balances the tiles by itself
+constexpr int kSplitMinKeyTiles = 8;
+struct TileOrder {
+    int n;      // jobs (the grid's y extent), 0 when nothing is split
+    int qs;     // the query tiles qs .. T-1 are split
+    int nslots; // T - qs
+    uint16_t job[kMaxJobs]; // bits 0-13 query tile; bits 14-15: 0 all keys, 1 first half, 2 second half
+};
+
 template <typename T, int HD, int STAGES, int NWV>
 __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                     const T *__restrict__ Vt, int N, int H, int ldv,
                                                                     int causal, int p, int S, int q_begin,
-                                                                    float scale_log2, T *__restrict__ O) {
+                                                                    float scale_log2, const TileOrder order,
+                                                                    float *__restrict__ part, T *__restrict__ O) {
     static_assert(sizeof(T) == 2, "16-bit types");
     constexpr int KPC = 8;
     constexpr int QCH = HD / KPC;              // chunks per K row (8 or 4)
@@ -445,7 +467,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     const int g = lane >> 5, l32 = lane & 31;
     const int bh = blockIdx.x;
     const int b = bh / H, head = bh - b * H;
-    const int qt = gridDim.y - 1 - blockIdx.y; // heavy (late-frame) tiles first
+    int qt = gridDim.y - 1 - blockIdx.y, piece = 0; // heavy (late-frame) tiles first
+    if (order.n > 0) {
+        const int j = order.job[blockIdx.y];
+        qt = j & 0x3FFF;
+        piece = j >> 14;
+    }
     const int q0 = q_begin + qt * BQL;
     const int D = H * HD;
 
@@ -470,7 +497,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     key_interval(q0, N, causal, p, S, wg_lo, tmp);
     key_interval(min(q0 + BQL - 1, N - 1), N, causal, p, S, tmp, wg_hi);
     if (q0 < p) wg_hi = N;
-    const int kt_begin = wg_lo / BKV, kt_end = (int)cdiv(wg_hi, BKV);
+    int kt_begin = wg_lo / BKV, kt_end = (int)cdiv(wg_hi, BKV);
+    if (piece) {
+        const int mid = kt_begin + (kt_end - kt_begin) / 2;
+        if (piece == 1) kt_end = mid;
+        else kt_begin = mid;
+    }
     const int ntiles = kt_end - kt_begin;
 
     Chunk qf[QCH / 2];
@@ -601,6 +633,21 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (piece) {
+        // half of the keys: the unnormalised partial, [HD] o then (max, sum)
+        if (qrow < N) {
+            const int64_t prow = ((int64_t)bh * order.nslots + (qt - order.qs)) * BQL + (qrow - q0);
+            float *dst = part + (prow * 2 + piece - 1) * (HD + 4);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    *reinterpret_cast<float4 *>(dst + db * 32 + acc_row(4 * u, g)) =
+                        make_float4(o[db][4 * u], o[db][4 * u + 1], o[db][4 * u + 2], o[db][4 * u + 3]);
+            if (g == 0) *reinterpret_cast<float2 *>(dst + HD) = make_float2(m_run, l_tot);
+        }
+        return;
+    }
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (qrow < N) {
         T *orow = O + ((int64_t)b * N + qrow) * D + head * HD;
@@ -786,6 +833,38 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(const float
     }
 }
 
+// Combines the two halves of a split query tile (TileOrder): with the running
+// maxima m0, m1 (log2 units) and M = max(m0, m1), o = (o0 2^(m0-M) + o1
+// 2^(m1-M)) / (l0 2^(m0-M) + l1 2^(m1-M)).  One thread per 4 output dims of
+// a row.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void split_merge_kernel(const float *__restrict__ part, int64_t n, int N, int H,
+                                                          int q_begin, int qs, int nslots, int bq,
+                                                          T *__restrict__ O) {
+    constexpr int G = HD / 4, PS = HD + 4;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n) return;
+    const int64_t row = idx / G;
+    const int d = (int)(idx - row * G) * 4;
+    const int local = (int)(row % bq);
+    const int64_t rest = row / bq;
+    const int slot = (int)(rest % nslots), bh = (int)(rest / nslots);
+    const int q = q_begin + (qs + slot) * bq + local;
+    if (q >= N) return;
+    const float *p0 = part + row * 2 * PS, *p1 = p0 + PS;
+    const float2 ml0 = *reinterpret_cast<const float2 *>(p0 + HD), ml1 = *reinterpret_cast<const float2 *>(p1 + HD);
+    const float M = fmaxf(ml0.x, ml1.x);
+    const float f0 = ml0.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml0.x - M);
+    const float f1 = ml1.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml1.x - M);
+    const float L = fmaf(ml0.y, f0, ml1.y * f1);
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float4 a = *reinterpret_cast<const float4 *>(p0 + d), c = *reinterpret_cast<const float4 *>(p1 + d);
+    const int b = bh / H, head = bh - b * H;
+    T *dst = O + ((int64_t)b * N + q) * H * HD + head * HD + d;
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(fmaf(a.x, f0, c.x * f1) * inv, fmaf(a.y, f0, c.y * f1) * inv),
+                                                 pack2<T>(fmaf(a.z, f0, c.z * f1) * inv, fmaf(a.w, f0, c.w * f1) * inv));
+}
+
 // the first query row the tiled kernels cover: the prefix rows go to
 // prefix_attention_kernel (all of them: a model has at most a few)
 inline int query_begin(int N, int p) { return p < N ? p : 0; }
@@ -796,6 +875,74 @@ inline int query_begin(int N, int p) { return p < N ? p : 0; }
 // kernels above instead (a workgroup per row and run of keys, then the merge).
 constexpr int kRowSplitTiles = 16;
 inline bool row_split(int B, int N, int H, int qb) { return (int64_t)B * H * cdiv(N - qb, BQ) < kRowSplitTiles; }
+
+// Key tiles (of BKV) a query tile of bq rows starting at q0 walks.
+inline int tile_key_tiles(int q0, int bq, int N, int causal, int p, int S) {
+    int lo, hi, tmp;
+    key_interval(q0, N, causal, p, S, lo, tmp);
+    key_interval(q0 + bq - 1 < N - 1 ? q0 + bq - 1 : N - 1, N, causal, p, S, tmp, hi);
+    if (q0 < p) hi = N;
+    return (int)(cdiv(hi, BKV) - lo / BKV);
+}
+
+// The TileOrder of a 16-bit attention call (bq queries per tile); returns
+// false (ord.n = 0) when no tile is split.
+inline bool plan_tile_order(int B, int N, int H, int causal, int p, int S, int bq, TileOrder &ord) {
+    ord.n = 0;
+    ord.qs = ord.nslots = 0;
+    const int qb = query_begin(N, p), T = (int)cdiv(N - qb, bq);
+    if (!causal || T < 4 || (int64_t)B * H * T > kSplitMaxWorkgroups) return false;
+    int cnt[kMaxJobs];
+    if (T > kMaxJobs) return false;
+    int maxn = 0, minn = 1 << 30;
+    for (int qt = 0; qt < T; ++qt) {
+        cnt[qt] = tile_key_tiles(qb + qt * bq, bq, N, causal, p, S);
+        maxn = cnt[qt] > maxn ? cnt[qt] : maxn;
+        minn = cnt[qt] < minn ? cnt[qt] : minn;
+    }
+    if (maxn < 2 * minn) return false; // tiles of alike cost (a single frame): nothing to balance
+    int qs = T; // split: the run of last tiles above the threshold (block-causal counts never fall)
+    while (qs > 0 && cnt[qs - 1] >= kSplitMinKeyTiles && 3 * cnt[qs - 1] > maxn) --qs;
+    if (qs == T || T + (T - qs) > kMaxJobs) return false;
+    // jobs with their key-tile counts, sorted largest first (ties: later tile first)
+    int njob = 0, size[kMaxJobs];
+    for (int qt = T - 1; qt >= 0; --qt) {
+        if (qt >= qs) {
+            size[njob] = cnt[qt] / 2;
+            ord.job[njob++] = (uint16_t)(qt | (1 << 14));
+            size[njob] = cnt[qt] - cnt[qt] / 2;
+            ord.job[njob++] = (uint16_t)(qt | (2 << 14));
+        } else {
+            size[njob] = cnt[qt];
+            ord.job[njob++] = (uint16_t)qt;
+        }
+    }
+    for (int i = 1; i < njob; ++i) { // insertion sort, stable
+        const int sz = size[i];
+        const uint16_t jb = ord.job[i];
+        int k = i - 1;
+        while (k >= 0 && size[k] < sz) {
+            size[k + 1] = size[k];
+            ord.job[k + 1] = ord.job[k];
+            --k;
+        }
+        size[k + 1] = sz;
+        ord.job[k + 1] = jb;
+    }
+    ord.n = njob;
+    ord.qs = qs;
+    ord.nslots = T - qs;
+    return true;
+}
+
+// fp32 scratch layout of a 16-bit attention call: the prefix rows' partials,
+// then (16-byte aligned) the split tiles' halves
+inline int64_t prefix_scratch_floats(int B, int N, int H, int hd, int rows_per_bh) {
+    return (int64_t)B * H * rows_per_bh * cdiv(N, kPrefixKeys) * (hd + 2);
+}
+inline int64_t split_scratch_floats(int B, int H, int hd, int bq, const TileOrder &ord) {
+    return ord.n > 0 ? (int64_t)B * H * ord.nslots * bq * 2 * (hd + 4) : 0;
+}
 
 template <typename T, int HD, int QR = 1>
 hipError_t launch_prefix(const void *Q, const void *K, const void *Vt, int B, int N, int H, int ldv, int qb,
@@ -822,12 +969,26 @@ hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, 
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
     // hd 32 tiles are too small to split their loads over more than 4 waves
     constexpr int NWV = HD == 64 ? kLdsWaves : 4;
+    constexpr int BQL = 32 * NWV;
     const int qb = query_begin(N, p);
-    dim3 grid((unsigned)(B * H), (unsigned)cdiv(N - qb, 32 * NWV));
+    const int ntq = (int)cdiv(N - qb, BQL);
+    TileOrder ord;
+    plan_tile_order(B, N, H, causal, p, S, BQL, ord);
+    float *part = nullptr;
+    if (ord.n > 0) {
+        if (!scratch) return hipErrorInvalidValue;
+        part = scratch + cdiv(prefix_scratch_floats(B, N, H, HD, qb), 4) * 4;
+    }
+    dim3 grid((unsigned)(B * H), (unsigned)(ord.n > 0 ? ord.n : ntq));
     hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV>), grid, dim3(64 * NWV), 0, s,
                        reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
-                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2,
+                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part,
                        reinterpret_cast<T *>(O));
+    if (ord.n > 0) {
+        const int64_t n = (int64_t)B * H * ord.nslots * BQL * (HD / 4);
+        hipLaunchKernelGGL((split_merge_kernel<T, HD>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, n, N, H,
+                           qb, ord.qs, ord.nslots, BQL, reinterpret_cast<T *>(O));
+    }
     return launch_prefix<T, HD>(Q, K, Vt, B, N, H, ldv, qb, scale_log2, scratch, O, s);
 }
 
@@ -869,10 +1030,19 @@ hipError_t launch_hd(int head_dim, const void *Q, const void *K, const void *Vt,
 
 } // namespace
 
-int64_t attention_scratch_floats(int B, int N, int H, int head_dim, int n_prefix) {
+int64_t attention_scratch_floats(int dtype, int B, int N, int H, int head_dim, int attn_mode, int n_prefix,
+                                 int tokens_per_frame) {
+    if (B <= 0 || N <= 0) return 0;
+    const int causal = attn_mode == 1;
+    const int S = tokens_per_frame > 0 ? tokens_per_frame : 1;
     const int qb = query_begin(N, n_prefix);
-    const int64_t rows = (int64_t)B * H * (row_split(B, N, H, qb) ? N : qb);
-    return rows * cdiv(N, kPrefixKeys) * (head_dim + 2);
+    if (dtype == DT_F32)
+        return prefix_scratch_floats(B, N, H, head_dim, !causal && row_split(B, N, H, qb) ? N : qb);
+    TileOrder ord;
+    plan_tile_order(B, N, H, causal, n_prefix, S, 32 * (head_dim == 64 ? kLdsWaves : 4), ord);
+    const int64_t pre = prefix_scratch_floats(B, N, H, head_dim, qb);
+    return ord.n > 0 ? cdiv(pre, 4) * 4 + split_scratch_floats(B, H, head_dim, 32 * (head_dim == 64 ? kLdsWaves : 4), ord)
+                     : pre;
 }
 
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N, int H,

@@ -84,7 +84,9 @@ vitenc_status make_plan(const vitenc_head *hd, int B, int N, HeadPlan &pl) {
         pl.off_U = take(M * (size_t)pl.F * es);
     }
     // the pooler blocks' attention has no prefix rows, but a small grid splits every row over runs of keys
-    pl.off_attn = hp.n_pool_layers > 0 ? take((size_t)attention_scratch_floats(B, N, H, pl.hd, 0) * 4) : 0;
+    pl.off_attn = hp.n_pool_layers > 0
+                      ? take((size_t)attention_scratch_floats(hp.dtype, B, N, H, pl.hd, VITENC_ATTN_FULL, 0, 0) * 4)
+                      : 0;
     pl.off_q = take(D * 4);
     pl.off_u = take(H * D * 4);
     pl.off_ub = take(H * 4);

@@ -138,9 +138,11 @@ int xattn_chunks(int N);
 hipError_t launch_xattn_pool(const float *Z, const float2 *stats, const float *w, int B, int N, int D, int H,
                              const float *ln_w, const float *ln_b, float *P, float *ybar, hipStream_t st);
 
-// scratch: fp32, attention_scratch_floats(...) floats (the prefix rows' partial
-// results); may be NULL when n_prefix is 0
-int64_t attention_scratch_floats(int B, int N, int H, int head_dim, int n_prefix);
+// scratch: fp32, 16-byte aligned, attention_scratch_floats(...) floats (partial
+// results of the prefix rows, of rows split over runs of keys and of query
+// tiles split over halves of their keys); may be NULL when that is 0
+int64_t attention_scratch_floats(int dtype, int B, int N, int H, int head_dim, int attn_mode, int n_prefix,
+                                 int tokens_per_frame);
 hipError_t launch_attention(int dtype, const void *Q, const void *K, const void *Vt, int B, int N,
                             int H, int head_dim, int ldv, int attn_mode, int n_prefix,
                             int tokens_per_frame, float *scratch, void *O, hipStream_t s);

@@ -135,9 +135,12 @@ vitenc_status vitenc_op_qkv_rope(int32_t dtype, const void *Y, const void *qkv_w
     return op_dev(launch_gemm(dtype, EPI_QKV, Y, D, qkv_w, D, B * N, 3 * D, D, ep, s), "qkv GEMM");
 }
 
-int64_t vitenc_attention_scratch_floats(int32_t B, int32_t N, int32_t n_head, int32_t head_dim, int32_t n_prefix) {
-    if (B <= 0 || N <= 0 || n_head <= 0 || head_dim <= 0 || n_prefix < 0 || n_prefix > N) return -1;
-    return attention_scratch_floats(B, N, n_head, head_dim, n_prefix);
+int64_t vitenc_attention_scratch_floats(int32_t dtype, int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
+                                        int32_t attn_mode, int32_t n_prefix, int32_t tokens_per_frame) {
+    if (!dtype_ok(dtype) || B <= 0 || N <= 0 || n_head <= 0 || head_dim <= 0 || n_prefix < 0 || n_prefix > N ||
+        (attn_mode != 0 && attn_mode != 1) || (attn_mode == 1 && tokens_per_frame <= 0))
+        return -1;
+    return attention_scratch_floats(dtype, B, N, n_head, head_dim, attn_mode, n_prefix, tokens_per_frame);
 }
 
 vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, const void *Vt, int32_t B, int32_t N,
@@ -150,8 +153,11 @@ vitenc_status vitenc_op_attention(int32_t dtype, const void *Q, const void *K, c
     if (head_dim != 64 && head_dim != 32) return op_fail(VITENC_EUNSUPPORTED, "head_dim %d", head_dim);
     if (n_prefix < 0 || n_prefix >= N) return op_fail(VITENC_ESHAPE, "n_prefix %d outside [0, N)", n_prefix);
     if (attn_mode == 1 && tokens_per_frame <= 0) return op_fail(VITENC_ESHAPE, "block-causal geometry");
-    if (attention_scratch_floats(B, N, n_head, head_dim, n_prefix) > 0 && !scratch)
-        return op_fail(VITENC_ENULL, "scratch is NULL but the prefix rows need it");
+    if (attn_mode != 0 && attn_mode != 1) return op_fail(VITENC_EINVAL, "unknown attn_mode %d", attn_mode);
+    if (attention_scratch_floats(dtype, B, N, n_head, head_dim, attn_mode, n_prefix, tokens_per_frame) > 0) {
+        if (!scratch) return op_fail(VITENC_ENULL, "scratch is NULL but this call needs it");
+        if (reinterpret_cast<uintptr_t>(scratch) % 16 != 0) return op_fail(VITENC_EINVAL, "scratch must be 16-byte aligned");
+    }
     return op_dev(launch_attention(dtype, Q, K, Vt, B, N, n_head, head_dim, (N + 63) / 64 * 64, attn_mode, n_prefix,
                                    tokens_per_frame, scratch, O, reinterpret_cast<hipStream_t>(stream)),
                   "attention");

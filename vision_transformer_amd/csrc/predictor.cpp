@@ -101,7 +101,8 @@ vitenc_status make_plan(const vitenc_predictor *p, int B, int nc, int nt, PredPl
     const int d = 2 * ((pl.hd / 3) / 2);
     pl.off_rope = take((size_t)(hp.grid_t + hp.grid_h + hp.grid_w) * d * 2 * 4);
     // attention keeps no prefix rows here, but a small grid splits every row over runs of keys
-    pl.off_attn = take((size_t)attention_scratch_floats(B, pl.N, pl.nh, pl.hd, 0) * 4);
+    pl.off_attn =
+        take((size_t)attention_scratch_floats(hp.dtype, B, pl.N, pl.nh, pl.hd, VITENC_ATTN_FULL, 0, 0) * 4);
     pl.total = off;
     return VITENC_OK;
 }
