@@ -81,6 +81,8 @@ def parse():
                     default="all",
                     help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
                          "head (reported in the line's `predictor` / `head` objects), or all three")
+    ap.add_argument("--workload", default=None,
+                    help="with --part configs: time only the encoder workload of this name")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
                     help="summarise two rocprofv3 --pmc counter_collection.csv files of this script "
                          "for KERNEL (a kernel-breakdown name)")
@@ -653,7 +655,12 @@ def bench_configs(args, stream):
     from vision_transformer_amd import vitenc as V
     from vision_transformer_amd import workloads as W
     res = {}
+    names = [c.name for c in W.CONFIGS]
+    if args.workload is not None and args.workload not in names:
+        raise SystemExit(f"unknown workload {args.workload!r}; one of {names}")
     for cfg in W.CONFIGS:
+        if args.workload is not None and cfg.name != args.workload:
+            continue
         wl = W.make_workload(cfg)
         enc = V.Encoder.from_workload(wl)
         px = torch.from_numpy(wl.pixels).cuda()
