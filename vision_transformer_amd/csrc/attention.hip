@@ -424,10 +424,11 @@ __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 
 // (frames) times the keys of frame 0's; when the grid is one or two rounds of
 // workgroups over the CUs, the late tiles alone then set the kernel's time.
 // When the largest key count is at least twice the smallest, a tile is split
-// in two when its key tiles exceed a third of the largest count: each half writes its unnormalised partial (o, running max,
-// running sum) to scratch and split_merge_kernel combines the two.  Jobs run
-// largest first.  n = 0: no split, tiles in reverse order (the heaviest last
-// tiles first), one workgroup each.
+// in two when its key tiles exceed a third of the largest count: each half
+// writes its unnormalised partial (o, running max, running sum) to scratch and
+// split_merge_kernel combines the two.  Jobs run largest first.  n = 0: no
+// split, tiles in reverse order (the heaviest last tiles first), one
+// workgroup each.
 constexpr int kMaxJobs = 480;
 constexpr int kSplitMaxWorkgroups = 1024; // above this the dispatcher balances the tiles by itself
 constexpr int kSplitMinKeyTiles = 8;
