@@ -81,6 +81,9 @@ def parse():
                     default="all",
                     help="what to time: the encoder (the headline line), the predictor or the attentive-pool "
                          "head (reported in the line's `predictor` / `head` objects), or all three")
+    ap.add_argument("--sq-summary", metavar="COUNTER_CSV", default=None,
+                    help="print per-kernel MFMA / VALU / LDS utilisation from a rocprofv3 --pmc pass over the "
+                         "SQ counters of this script")
     ap.add_argument("--workload", default=None,
                     help="with --part configs: time only the encoder workload of this name")
     ap.add_argument("--write-counters", nargs=4, metavar=("KERNEL", "FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
@@ -118,6 +121,45 @@ def counter_means(path, counter, share=None):
         if vals:
             out[k] = (sum(v for _, v in vals) / len(vals), len(vals))
     return out
+
+
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU",
+               "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES")
+
+
+def sq_summary(csv_path, clock_ghz=2.4, cus=256, simds=1024):
+    """Per-kernel utilisation from one rocprofv3 --pmc pass over SQ_COUNTERS
+    (+ GRBM_GUI_ACTIVE) of this script: means per dispatch of the MFMA-busy
+    cycles over all SIMDs, the VALU- and LDS-active cycles summed over waves
+    (quad-cycles, scaled by 4) per CU, and the instruction counts, each
+    against the dispatch's duration at the quoted clock."""
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            k = r["Kernel_Name"]
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[k][r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lines = ["kernel           dispatches  us    mfma_busy  valu_active  lds_active   valu_insts  mfma_insts"
+             "  trans_insts  lds_bank_conflicts"]
+    for name, (pattern, _) in KERNEL_SOURCES.items():
+        if name == "out_gemm":
+            continue
+        ks = [k for k in vals if re.search(pattern, k.split("(")[0])]
+        if not ks:
+            continue
+        c, d = vals[ks[0]], dur[ks[0]]
+        mean = lambda n: sum(c[n]) / len(c[n])
+        ns = sum(d.values()) / len(d)
+        cyc = ns * clock_ghz
+        label = "out+down_gemm" if name == "down_gemm" else name
+        lines.append(f"{label:16s} {len(d):10d} {ns / 1000:5.1f} {mean('SQ_VALU_MFMA_BUSY_CYCLES') / (simds * cyc):10.3f}"
+                     f" {4 * mean('SQ_ACTIVE_INST_VALU') / (cus * cyc):12.3f}"
+                     f" {4 * mean('SQ_ACTIVE_INST_LDS') / (cus * cyc):11.3f}"
+                     f" {mean('SQ_INSTS_VALU'):12.4g} {mean('SQ_INSTS_MFMA'):11.4g}"
+                     f" {mean('SQ_INSTS_VALU_TRANS_F32'):12.4g} {mean('SQ_LDS_BANK_CONFLICT'):19.4g}")
+    print("\n".join(lines))
 
 
 def write_counters(dominant, fetch_csv, write_csv, out_txt):
@@ -681,6 +723,9 @@ def bench_configs(args, stream):
 
 def main():
     args = parse()
+    if args.sq_summary:
+        sq_summary(args.sq_summary)
+        return
     if args.write_counters:
         write_counters(*args.write_counters)
         return
