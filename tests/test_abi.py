@@ -285,6 +285,9 @@ def test_step_entry_point_refusals():
     assert S(7, 1, 64, 1, 64, 0, 0, 0) == -1 and S(1, 1, 64, 1, 64, 2, 0, 0) == -1
     assert S(1, 1, 64, 1, 64, 1, 0, 0) == -1
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 257, 2, 64, 0, 1, 0, None, FAKE, None) == 3
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 64, 2, 64, 2, 0, 0, None, FAKE, None) == 1   # attn_mode
+    # the scratch must be 16-byte aligned when the call needs one (the split tiles' float4 partials)
+    assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 257, 2, 64, 0, 1, 0, FAKE + 4, FAKE, None) == 1
     assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 17, 64, 1, 1, 2, 2, 2, 0,
                                 FAKE, FAKE, FAKE, FAKE, None) == 2          # 8 patches + 0 prefix != 17
     assert L.vitenc_op_qkv_rope(1, FAKE, FAKE, FAKE, 1, 8, 64, 1, 1, 2, 2, 2, 0,
