@@ -167,6 +167,10 @@ def test_qkv_rope(gpu_lib, dtype, case):
     # frames that straddle query tiles, a ragged last query tile and key tile
     dict(B=2, H=3, N=1 + 6 * 200, hd=64, mode=1, p=1, S=200),
     dict(B=1, H=2, N=8 * 128, hd=32, mode=1, p=0, S=128),
+    # a split query tile whose earliest rows see no key in the second half of
+    # its keys while later rows of the same wave do (frames of 300 tokens)
+    dict(B=1, H=2, N=1 + 4 * 300, hd=64, mode=1, p=1, S=300),
+    dict(B=1, H=2, N=1 + 4 * 300, hd=32, mode=1, p=1, S=300),
 ])
 def test_attention(gpu_lib, dtype, case):
     from vision_transformer_amd import vitenc as V

@@ -38,21 +38,8 @@ constexpr int kThreads = 256;
 constexpr int BQ = 128;   // queries per workgroup
 constexpr int BKV = 64;   // keys per tile
 constexpr float kRescale = 8.0f; // log2 headroom before the running max moves
-#ifndef VITENC_ATTN_PIPE
-#define VITENC_ATTN_PIPE 0
-#endif
-constexpr bool kPipe = VITENC_ATTN_PIPE; // scores of the next tile overlap this tile's softmax
-#ifndef VITENC_ATTN_STAGES
-#define VITENC_ATTN_STAGES 4
-#endif
-constexpr int kStages = VITENC_ATTN_STAGES; // LDS ring depth of the direct-to-LDS kernel
-#ifndef VITENC_ATTN_WAVES
-#define VITENC_ATTN_WAVES 4
-#endif
-constexpr int kLdsWaves = VITENC_ATTN_WAVES; // waves (32 queries each) per workgroup, hd 64
-#ifndef VITENC_ATTN_DOT
-#define VITENC_ATTN_DOT 1
-#endif
+constexpr int kStages = 4;  // LDS ring depth of the direct-to-LDS kernel
+constexpr int kLdsWaves = 4; // waves (32 queries each) per workgroup, hd 64
 
 // acc + lo + hi of a dword holding two 16-bit values (one packed dot product
 // with (1, 1), fp32 accumulation)
@@ -235,51 +222,24 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
         for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    // Software pipeline over key tiles.  At the start of iteration t the
-    // scores S(t) are in registers, LDS holds V(t) and K(t+1); the iteration
-    // fetches K(t+2) and V(t+1) into registers, issues the MFMAs of S(t+1)
-    // (they run while the softmax of tile t occupies the vector ALUs), does
-    // P(t) and O += V(t)^T P(t)^T, then stores K(t+2) over K(t) and V(t+1)
-    // over V(t-1), both last read before the previous barrier.
-    f32x16 sc[2], sn[2];
-    if constexpr (kPipe) {
-        if (kt_begin < kt_end) {
-            gload_k(kt_begin);
-            gload_v(kt_begin);
-            sstore_k(0);
-            sstore_v(0);
-            if (kt_begin + 1 < kt_end) {
-                gload_k(kt_begin + 1);
-                sstore_k(1);
-            }
-        }
-        __syncthreads();
-        if (kt_begin < kt_end && tile_active(kt_begin)) scores(sc, 0);
-    } else {
-        if (kt_begin < kt_end) {
-            gload_k(kt_begin);
-            gload_v(kt_begin);
-            sstore_k(0);
-            sstore_v(0);
-        }
-        __syncthreads();
+    // Register-staged double buffer: tile t+1 is fetched into registers
+    // while tile t is computed out of LDS, then stored into the other buffer.
+    f32x16 sc[2];
+    if (kt_begin < kt_end) {
+        gload_k(kt_begin);
+        gload_v(kt_begin);
+        sstore_k(0);
+        sstore_v(0);
     }
+    __syncthreads();
     for (int kt = kt_begin; kt < kt_end; ++kt) {
         const int cur = (kt - kt_begin) & 1;
         const int kb = kt * BKV;
-        bool next_active = false;
-        if constexpr (kPipe) {
-            if (kt + 2 < kt_end) gload_k(kt + 2);
-            if (kt + 1 < kt_end) gload_v(kt + 1);
-            next_active = kt + 1 < kt_end && tile_active(kt + 1);
-            if (next_active) scores(sn, cur ^ 1);
-        } else {
-            if (kt + 1 < kt_end) {
-                gload_k(kt + 1);
-                gload_v(kt + 1);
-            }
-            if (tile_active(kt)) scores(sc, cur);
+        if (kt + 1 < kt_end) {
+            gload_k(kt + 1);
+            gload_v(kt + 1);
         }
+        if (tile_active(kt)) scores(sc, cur);
 
         if (tile_active(kt)) {
             const bool need_mask = !(kb >= w_full_lo && kb + BKV <= w_full_hi);
@@ -305,8 +265,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
             // for any m_run.
             const bool grow = mx > m_run + kRescale;
             if (__ballot(grow)) {
+                // lanes that do not grow keep their state (alpha 1): their
+                // m_run may still be -inf, and exp2(-inf - -inf) is NaN
                 const float m_new = grow ? mx : m_run;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new); // 0 on the first tile
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f; // 0 on the first tile
                 m_run = m_new;
                 l_run *= alpha;
 #pragma unroll
@@ -331,8 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                         for (int e = 0; e < 4; ++e) {
                             pb.w[e] = pack2<T>(pv[8 * st + 2 * e], pv[8 * st + 2 * e + 1]);
                             // the row sum adds the rounded weights the MFMA uses
-                            if constexpr (VITENC_ATTN_DOT) l_run = sum2<T>(pb.w[e], l_run);
-                            else l_run += pv[8 * st + 2 * e] + pv[8 * st + 2 * e + 1];
+                            l_run = sum2<T>(pb.w[e], l_run);
                         }
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
@@ -362,24 +323,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
                 }
             }
         }
-        if constexpr (kPipe) {
-            // every wave has read K(t0) (the scores before the loop) before the
-            // first store overwrites it; later K(t) were read before the last barrier
-            if (kt == kt_begin) __syncthreads();
-            if (kt + 2 < kt_end) sstore_k(cur);
-            if (kt + 1 < kt_end) sstore_v(cur ^ 1);
-            __syncthreads();
-            if (next_active) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) sc[j] = sn[j];
-            }
-        } else {
-            if (kt + 1 < kt_end) {
-                sstore_k(cur ^ 1);
-                sstore_v(cur ^ 1);
-            }
-            __syncthreads();
+        if (kt + 1 < kt_end) {
+            sstore_k(cur ^ 1);
+            sstore_v(cur ^ 1);
         }
+        __syncthreads();
     }
 
     // ---- normalise and store O[b, q, head*HD + d]
@@ -600,8 +548,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
         const bool grow = mx > m_run + kRescale;
         if (__ballot(grow)) {
+            // lanes that do not grow keep their state: a lane whose keys in
+            // this half of a split tile are all masked still has m_run = -inf,
+            // and exp2(-inf - -inf) would be NaN
             const float m_new = grow ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
@@ -855,11 +806,16 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float *__restric
     const float *p0 = part + row * 2 * PS, *p1 = p0 + PS;
     const float2 ml0 = *reinterpret_cast<const float2 *>(p0 + HD), ml1 = *reinterpret_cast<const float2 *>(p1 + HD);
     const float M = fmaxf(ml0.x, ml1.x);
-    const float f0 = ml0.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml0.x - M);
-    const float f1 = ml1.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml1.x - M);
-    const float L = fmaf(ml0.y, f0, ml1.y * f1);
+    // a half in which this row sees no key (max -inf) is dropped by a select,
+    // never multiplied by 0 (its partial is not read at all)
+    const bool h0 = ml0.x != -INFINITY, h1 = ml1.x != -INFINITY;
+    const float f0 = h0 ? __builtin_amdgcn_exp2f(ml0.x - M) : 0.0f;
+    const float f1 = h1 ? __builtin_amdgcn_exp2f(ml1.x - M) : 0.0f;
+    const float L = (h0 ? ml0.y * f0 : 0.0f) + (h1 ? ml1.y * f1 : 0.0f);
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const float4 a = *reinterpret_cast<const float4 *>(p0 + d), c = *reinterpret_cast<const float4 *>(p1 + d);
+    const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const float4 a = h0 ? *reinterpret_cast<const float4 *>(p0 + d) : z4;
+    const float4 c = h1 ? *reinterpret_cast<const float4 *>(p1 + d) : z4;
     const int b = bh / H, head = bh - b * H;
     T *dst = O + ((int64_t)b * N + q) * H * HD + head * HD + d;
     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(fmaf(a.x, f0, c.x * f1) * inv, fmaf(a.y, f0, c.y * f1) * inv),

@@ -555,13 +555,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
 // choosing which chunk each lane fetches.  A ring of STAGES LDS stages keeps
 // STAGES - 1 slabs in flight while one is multiplied.  Requires the FAST
 // conditions (K a multiple of the slab width, 16-byte aligned rows).
-#ifndef VITENC_GEMM_SWAP
-#define VITENC_GEMM_SWAP 1
-#endif
 // The direct-to-LDS kernel computes each 32x32 block transposed (weight
 // fragment as MFMA operand A), so that every lane holds runs of 4 consecutive
 // output columns and stages them into LDS with 16-byte writes.
-constexpr bool kSwap = VITENC_GEMM_SWAP;
 
 //
 // WQ (8-bit weights, bf16 activations): W holds one E4M3 byte per weight and
@@ -743,8 +739,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                if constexpr (MI == 32 && kSwap) mfma_chunk<T>(acc[fm][fn], b[fn], a[fm]); // D^T
-                else if constexpr (MI == 32) mfma_chunk<T>(acc[fm][fn], a[fm], b[fn]);
+                if constexpr (MI == 32) mfma_chunk<T>(acc[fm][fn], b[fn], a[fm]); // D^T
                 else mfma16_chunk<T>(acc[fm][fn], a[fm], b[fn]);
             }
     };
@@ -843,7 +838,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     float *estage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * MI * (WN + 4);
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(lds) - kRiBytes - kStageBytes) / 8;
-    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, kSwap>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
+    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, MI == 32>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
                                                   ep, ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
 }
 
@@ -972,12 +967,7 @@ hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, in
 // FAST conditions use the register-staged kernel.
 enum TileCfg { TILE_REG = 0, TILE_256x256 = 1, TILE_128x128 = 2, TILE_128x128_DEEP = 3, TILE_64x64 = 4 };
 
-#ifndef VITENC_DEEP_STAGES
-#define VITENC_DEEP_STAGES 3
-#endif
-#ifndef VITENC_SMALL_TILES
-#define VITENC_SMALL_TILES 1
-#endif
+constexpr int kDeepStages = 3; // LDS ring of the one-tile-per-CU 128 x 128 configuration
 
 // With at most one 128 x 128 tile per CU (the N = D projections of one clip)
 // occupancy cannot hide the first touch of the weights in HBM: those tiles
@@ -996,7 +986,7 @@ inline int pick_tile(int M, int N, bool fast, bool fp32) {
         if (t256 >= kCUs && !(t256 % kCUs != 0 && t256 % kCUs < kCUs / 4)) return TILE_256x256;
         if (t256 >= kCUs && cdiv(M, 128) * cdiv(N, 128) > kCUs) return TILE_128x128;
     }
-    if (VITENC_SMALL_TILES && cdiv(M, 128) * cdiv(N, 128) < kCUs / 2) return TILE_64x64;
+    if (cdiv(M, 128) * cdiv(N, 128) < kCUs / 2) return TILE_64x64;
     if (cdiv(M, 128) * cdiv(N, 128) <= kCUs) return TILE_128x128_DEEP;
     return TILE_128x128;
 }
@@ -1022,7 +1012,7 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
             case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32, true>(A, lda, W, ldw, M, N, K, ep, s);
             case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 4, 8, 2, 32, true>(A, lda, W, ldw, M, N, K, ep, s);
             case TILE_128x128_DEEP:
-                return launch_lds<T, EPI, 128, 128, 2, 4, 8, VITENC_DEEP_STAGES, 32, true>(A, lda, W, ldw, M, N, K,
+                return launch_lds<T, EPI, 128, 128, 2, 4, 8, kDeepStages, 32, true>(A, lda, W, ldw, M, N, K,
                                                                                           ep, s);
             case TILE_64x64: return launch_lds<T, EPI, 64, 64, 2, 2, 8, 3, 32, true>(A, lda, W, ldw, M, N, K, ep, s);
             default: return hipErrorInvalidValue;
@@ -1036,7 +1026,7 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
         case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_128x128_DEEP:
-            return launch_lds<T, EPI, 128, 128, 2, 4, 8, VITENC_DEEP_STAGES, 32>(A, lda, W, ldw, M, N, K, ep, s);
+            return launch_lds<T, EPI, 128, 128, 2, 4, 8, kDeepStages, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_64x64: return launch_lds<T, EPI, 64, 64, 2, 2, 8, 3, 32>(A, lda, W, ldw, M, N, K, ep, s);
         default: break;
         }
@@ -1073,7 +1063,7 @@ int64_t gemm_splitk_floats(int dtype, int epi, int M, int N, int K, bool wq) {
         switch (pick_tile(M, N, true, false)) {
         case TILE_256x256: bm = 256; per_cu = lds_per_cu(256, 2); break;
         case TILE_128x128: bm = 128; per_cu = lds_per_cu(128, 2); break;
-        case TILE_128x128_DEEP: bm = 128; per_cu = lds_per_cu(128, VITENC_DEEP_STAGES); break;
+        case TILE_128x128_DEEP: bm = 128; per_cu = lds_per_cu(128, kDeepStages); break;
         default: bm = 64; per_cu = lds_per_cu(64, 3); break;
         }
         nk = K / 64;
