@@ -425,6 +425,29 @@ int64_t vitenc_attention_scratch_floats(int32_t dtype, int32_t B, int32_t N, int
                                         int32_t head_dim, int32_t attn_mode, int32_t n_prefix,
                                         int32_t tokens_per_frame);
 
+/* vitenc_op_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and kernels without the scratch argument.
+ * The partial results vitenc_op_attention keeps in the caller's scratch go
+ * to a fixed device array of the library instead (the one exception to the
+ * rule above that the library holds no device memory), of
+ * VITENC_NOALLOC_SCRATCH_FLOATS floats (64 MiB) per device, held until the
+ * process ends.  That covers every shape of the five encoder workloads (the
+ * largest need is 47 MiB, two 4097-token block-causal clips at 16 heads); a
+ * call that needs more (vitenc_attention_scratch_floats of the same
+ * arguments above the limit, e.g. prefix rows over millions of keys) is
+ * refused with EUNSUPPORTED before any device work.  Every call on one
+ * device shares that device's array and each call writes every partial it
+ * reads (nothing needs to start at zero), so calls whose executions overlap
+ * on one device (different streams or threads) race on it: order them (one
+ * stream, or events).  The first call on a device looks the array's address
+ * up with that device current.  Other errors as vitenc_op_attention. */
+#define VITENC_NOALLOC_SCRATCH_FLOATS (16 << 20)
+vitenc_status vitenc_op_attention_noalloc(int32_t dtype, const void *Q, const void *K, const void *Vt,
+                                          int32_t B, int32_t N, int32_t n_head, int32_t head_dim,
+                                          int32_t attn_mode, int32_t n_prefix,
+                                          int32_t tokens_per_frame, void *O, void *stream);
+
 /* a8/a10 projection with bias, layer scale and residual: Z[M, Nout] (fp32)
  * += ls * (A[M, K] W[Nout, K]^T + b); ls may be NULL (= 1). */
 vitenc_status vitenc_op_linear_residual(int32_t dtype, const void *A, const void *W,

@@ -100,6 +100,7 @@ SIGNATURES = {
     "vitenc_rope_table_floats": (ctypes.c_int64, [c_i32] * 4),
     "vitenc_op_pos_resample": (c_i32, [c_vp] + [c_i32] * 9 + [c_vp, c_vp]),
     "vitenc_op_attention": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp, c_vp]),
+    "vitenc_op_attention_noalloc": (c_i32, [c_i32, c_vp, c_vp, c_vp] + [c_i32] * 7 + [c_vp, c_vp]),
     "vitenc_attention_scratch_floats": (ctypes.c_int64, [c_i32] * 8),
     "vitenc_op_linear_residual": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "vitenc_op_linear_gelu": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]),
@@ -553,6 +554,16 @@ def op_attention(dtype, Q, K, Vt, attn_mode=0, n_prefix=0, tokens_per_frame=0, s
         scratch = torch.empty(nf, dtype=torch.float32, device=Q.device)
     check(lib().vitenc_op_attention(dtype, Q.data_ptr(), K.data_ptr(), Vt.data_ptr(), B, N, H, hd, attn_mode,
                                     n_prefix, tokens_per_frame, _ptr(scratch), O.data_ptr(), _stream(stream)))
+    return O
+
+
+def op_attention_noalloc(dtype, Q, K, Vt, attn_mode=0, n_prefix=0, tokens_per_frame=0, stream=None, out=None):
+    """vitenc_op_attention_noalloc: the partials in the library's fixed array."""
+    import torch
+    B, H, N, hd = Q.shape
+    O = torch.empty((B, N, H * hd), dtype=torch_dtype(dtype), device=Q.device) if out is None else out
+    check(lib().vitenc_op_attention_noalloc(dtype, Q.data_ptr(), K.data_ptr(), Vt.data_ptr(), B, N, H, hd, attn_mode,
+                                            n_prefix, tokens_per_frame, O.data_ptr(), _stream(stream)))
     return O
 
 
