@@ -43,9 +43,51 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
+# Peaks, recomputed from the device's reported CU count and peak clock by
+# device_peaks(): dense bf16 MFMA 4096 flop per clock per CU (256 CU x 2.4 GHz
+# x 4096 = 2516.6 TFLOP/s on MI355X), fp32 256 flop per clock per CU
+# (157.3 TFLOP/s); HBM3E 8 TB/s as published (not derivable from attributes).
+BF16_FLOP_PER_CLK_CU = 4096
+FP32_FLOP_PER_CLK_CU = 256
+PEAK_BF16_TFLOPS = 2516.6
 PEAK_HBM_GBS = 8000.0
-PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 (MFMA / packed vector)
+PEAK_FP32_TFLOPS = 157.3
+PEAK_SOURCE = {"cus": 256, "clock_ghz": 2.4, "from": "published MI355X figures"}
+# hipDeviceAttribute_t values of the HIP runtime API (hip_runtime_api.h)
+_HIP_ATTR_CLOCK_RATE_KHZ = 5
+_HIP_ATTR_CU_COUNT = 63
+
+
+def device_peaks():
+    """Set the MFMA peaks from the device's CU count and peak clock (HIP
+    device attributes) and return the figures used."""
+    global PEAK_BF16_TFLOPS, PEAK_FP32_TFLOPS, PEAK_SOURCE
+    import ctypes
+    import torch
+    torch.cuda.init()
+    hip = ctypes.CDLL("libamdhip64.so")
+    dev = torch.cuda.current_device()
+    clk, cus = ctypes.c_int(0), ctypes.c_int(0)
+    if (hip.hipDeviceGetAttribute(ctypes.byref(clk), _HIP_ATTR_CLOCK_RATE_KHZ, dev) != 0 or
+            hip.hipDeviceGetAttribute(ctypes.byref(cus), _HIP_ATTR_CU_COUNT, dev) != 0 or clk.value <= 0):
+        return PEAK_SOURCE
+    ghz = clk.value / 1e6
+    PEAK_BF16_TFLOPS = round(cus.value * BF16_FLOP_PER_CLK_CU * ghz / 1e3, 1)
+    PEAK_FP32_TFLOPS = round(cus.value * FP32_FLOP_PER_CLK_CU * ghz / 1e3, 1)
+    PEAK_SOURCE = {"cus": cus.value, "clock_ghz": ghz, "bf16_flop_per_clk_per_cu": BF16_FLOP_PER_CLK_CU,
+                   "fp32_flop_per_clk_per_cu": FP32_FLOP_PER_CLK_CU, "from": "hipDeviceGetAttribute (peak clock)"}
+    return PEAK_SOURCE
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 COPY_BYTES = 256 << 20        # plain device copy used to calibrate the HBM byte counters
 CSRC = os.path.join(ROOT, "vision_transformer_amd", "csrc")
 # kernel-breakdown name -> (pattern of its device kernel's mangled name, sources it is compiled from).
@@ -323,6 +365,7 @@ def cpu_baseline(cfg, wl, layers=None):
     t3 = time.perf_counter()
     per_clip = (t1 - t0) + (t2 - t1) * cfg.n_layer / layers + (t3 - t2)
     return {"value": round(one.n_tokens / per_clip, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"1 of {cfg.batch} clips ({one.n_tokens} tokens), patch embed + {layers} of {cfg.n_layer} "
                       f"layers + final norm, {t3 - t0:.1f} s"}
 
@@ -352,6 +395,7 @@ def cpu_baseline_predictor(cfg, wl):
     oracle.predictor_forward(cfg.hparams(), wl.weights, wl.enc_tokens, wl.ctx_ids, wl.tgt_ids, cfg.mask_index)
     dt = time.perf_counter() - t0
     return {"value": round(cfg.batch * cfg.n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "cpu_model": cpu_model(),
             "kind": "oracle", "sample": f"the whole workload ({cfg.batch} items x {cfg.n_tokens} tokens, "
                                         f"{cfg.n_layer} blocks), {dt:.1f} s"}
 
@@ -385,20 +429,32 @@ def roofline_of(bd, workload):
     return roof
 
 
-def time_steps(step, steps, warmup, stream):
+def time_steps(step, steps, warmup, stream, per_call=None):
+    """Mean ms per step over `steps` back-to-back steps bracketed by one
+    event pair (and the host wall time).  With per_call a list, an event pair
+    also brackets every call on the same stream and the list receives each
+    call's ms (their median and minimum are reported beside the mean)."""
     import torch
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)] \
+        if per_call is not None else None
     t_wall = time.perf_counter()
     start.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        if evs:
+            evs[i][0].record(stream)
         step()
+        if evs:
+            evs[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    if evs:
+        per_call.extend(e0.elapsed_time(e1) for e0, e1 in evs)
     return start.elapsed_time(end) / steps, t_wall * 1e3 / steps
 
 
@@ -482,6 +538,7 @@ def cpu_baseline_head(cfg, wl):
     oracle.attentive_pool_forward(cfg.hparams(), wl.weights, wl.tokens)
     dt = time.perf_counter() - t0
     return {"value": round(cfg.batch * cfg.n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "cpu_model": cpu_model(),
             "kind": "oracle", "sample": f"the whole workload ({cfg.batch} items x {cfg.n_tokens} tokens, "
                                         f"{cfg.n_pool_layers} pooler blocks + cross-attention + classifier), "
                                         f"{dt:.1f} s"}
@@ -737,6 +794,8 @@ def main():
     from vision_transformer_amd import vitenc as V
     from vision_transformer_amd import workloads as W
 
+    peak_source = device_peaks()
+    log(f"[bench] peaks: bf16 {PEAK_BF16_TFLOPS} TFLOP/s, fp32 {PEAK_FP32_TFLOPS} TFLOP/s from {peak_source}")
     stream = torch.cuda.current_stream()
     if args.part == "predictor":
         print(json.dumps({"predictor": bench_predictor(args, stream)}), flush=True)
@@ -772,11 +831,13 @@ def main():
         with torch.cuda.graph(graph):
             enc.encode_into(px, ws, out, pooled)
         step = graph.replay
-    ms, wall = time_steps(step, args.steps, args.warmup, stream)
+    calls = []
+    ms, wall = time_steps(step, args.steps, args.warmup, stream, per_call=calls)
     tokens = cfg.batch * cfg.n_tokens
     tflops = cfg.flops() / (ms * 1e-3) / 1e12
+    med, mn = float(np.median(calls)), float(np.min(calls))
     log(f"[bench] {ms:.3f} ms/step, {tokens / ms * 1e3:.0f} tokens/s, {tflops:.1f} TFLOP/s "
-        f"(wall {wall:.3f} ms/step)")
+        f"(wall {wall:.3f} ms/step; per call median {med:.3f} min {mn:.3f} ms)")
 
     def busy():
         for _ in range(4):
@@ -805,6 +866,12 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) pixels, N(0,0.02) weights)",
         "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "per_call": {"median_ms": round(med, 4), "min_ms": round(mn, 4), "max_ms": round(float(np.max(calls)), 4),
+                     "calls": len(calls), "tokens_per_s_median": round(tokens / med * 1e3, 1),
+                     "tflops_median": round(cfg.flops() / (med * 1e-3) / 1e12, 2),
+                     "mfma_frac_median": round(cfg.flops() / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "peak": {"bf16_tflops": PEAK_BF16_TFLOPS, "fp32_tflops": PEAK_FP32_TFLOPS, "hbm_gbs": PEAK_HBM_GBS,
+                 **peak_source},
         "config": {"workload": cfg.name, "global_batch": cfg.batch, "tokens_per_item": cfg.n_tokens,
                    "embed_dim": cfg.embed_dim, "layers": cfg.n_layer, "heads": cfg.n_head,
                    "graph": bool(args.graph)},

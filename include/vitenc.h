@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define VITENC_ABI_VERSION 4
+#define VITENC_ABI_VERSION 5
 
 typedef enum {
     VITENC_OK = 0,
@@ -189,69 +189,104 @@ vitenc_status vitenc_encode(const vitenc_model *m, const float *pixels, int32_t 
  * "masked-latent predictor"; hyperparameters and tensors of jepa.cpp "GGUF
  * schema (v1)", section "Predictor (jepa.pred.*)"):
  *
- *   x_ctx = enc_tokens[ctx_ids] embed_w^T + embed_b        (enc_dim -> embed_dim)
+ *   x_ctx = embed(enc_tokens[ctx_ids])                    (enc_dim -> embed_dim)
  *   x_tgt = mask_tokens[mask_index] at every target id
- *   x     = [x_ctx; x_tgt] put in increasing token-id order
+ *   x     = [x_ctx; x_tgt] (+ modality vector) put in increasing token-id order
  *   per block (the encoder's block, full attention, no prefix token, 3-D RoPE
  *   at each token's (t, h, w) on the grid, no interpolation):
  *         x += attn(ln1(x));  x += ffn(ln2(x))
- *   out   = norm(x) at the target ids, in the order of tgt_ids, proj_w^T + proj_b
+ *   y     = norm(x)
+ *   out   = y at the target ids, in the order of tgt_ids, proj_w^T + proj_b
+ *   out_ctx = y at the context ids, in the order of ctx_ids, proj_ctx_w^T + proj_ctx_b
+ *
+ * embed is one linear map (V-JEPA 2; 2.1 after a ViT-B/L encoder) or, with
+ * n_hier_in > 1 (V-JEPA 2.1 after a ViT-g/G encoder: pred.embed.0 / .2), the
+ * 2-layer MLP embed2(GELU_erf(embed(f))) over the concatenation f of the
+ * token's n_hier_in hierarchical encoder features, in level order.  The
+ * V-JEPA 2.1 modality vector (pred.mod_embed_img for a one-frame grid,
+ * pred.mod_embed_video otherwise) is added to every token, context and mask
+ * tokens alike.  proj and proj_context (2.1) map to out_dim, the teacher's
+ * width in 2.1 (enc_dim in V-JEPA 2).
  * ------------------------------------------------------------------------- */
 
 /* embed_dim D (1..4096), enc_dim De (1..65536), n_layer, n_head (head_dim
  * D/n_head must be 32 or 64), ffn_dim F, n_mask_tokens (>= 1), ln_eps,
  * rope_theta (> 0), rope_layout TILED or INTERLEAVED, the token grid
  * grid_t x grid_h x grid_w (1..1023 each) on which ids are numbered in the
- * encoder's token order (id = (t*grid_h + h)*grid_w + w), dtype as the encoder. */
+ * encoder's token order (id = (t*grid_h + h)*grid_w + w), dtype as the encoder.
+ * V-JEPA 2.1 options (all 0 = V-JEPA 2): out_dim (0: enc_dim; else 1..65536),
+ * n_hier_in (0 or 1: one level; up to VITENC_MAX_HIER), embed_hidden (the
+ * embed MLP's hidden width, 1..65536, when n_hier_in > 1), modality_embed and
+ * context_proj (0 / 1: the modality vectors / the context projection are
+ * present). */
 typedef struct {
     int32_t embed_dim, enc_dim, n_layer, n_head, ffn_dim, n_mask_tokens;
     float ln_eps, rope_theta;
     int32_t rope_layout, grid_t, grid_h, grid_w;
     int32_t dtype;
+    int32_t out_dim, n_hier_in, embed_hidden, modality_embed, context_proj;
 } vitenc_pred_hparams;
 
-/* embed_w [D, De] and proj_w [De, D] in the model dtype; embed_b [D],
- * mask_tokens [n_mask_tokens, D], norm_w/norm_b [D], proj_b [De] fp32;
+/* embed_w [D, De] (with n_hier_in > 1: embed.0 [embed_hidden, n_hier_in*De])
+ * and proj_w [out_dim, D] in the model dtype; embed_b [D] (embed_hidden),
+ * mask_tokens [n_mask_tokens, D], norm_w/norm_b [D], proj_b [out_dim] fp32;
  * blocks: HOST array of n_layer vitenc_block_weights with the predictor's
- * widths (D, F; layer scales ignored), copied at creation. */
+ * widths (D, F; layer scales ignored), copied at creation.  V-JEPA 2.1
+ * (NULL when the option is off): embed2_w [D, embed_hidden] (model dtype)
+ * and embed2_b [D] when n_hier_in > 1; mod_embed_img / mod_embed_video [D]
+ * with modality_embed; proj_ctx_w [out_dim, D] (model dtype) and proj_ctx_b
+ * [out_dim] with context_proj. */
 typedef struct {
     const void *embed_w;  const float *embed_b;
     const float *mask_tokens;
     const vitenc_block_weights *blocks;
     const float *norm_w, *norm_b;
     const void *proj_w;   const float *proj_b;
+    const void *embed2_w; const float *embed2_b;
+    const float *mod_embed_img, *mod_embed_video;
+    const void *proj_ctx_w; const float *proj_ctx_b;
 } vitenc_pred_weights;
 
 typedef struct vitenc_predictor vitenc_predictor;
 
 /* Refusals as vitenc_model_create: EINVAL for ranges and enum values, ENULL
- * for a missing weight, EUNSUPPORTED for head_dim other than 32 or 64 or
- * embed_dim above 4096. */
+ * for a missing weight (an option's tensors included), EUNSUPPORTED for
+ * head_dim other than 32 or 64 or embed_dim above 4096. */
 vitenc_status vitenc_predictor_create(const vitenc_pred_hparams *hp, const vitenc_pred_weights *w,
                                       vitenc_predictor **out);
 void vitenc_predictor_destroy(vitenc_predictor *p);
 
-/* Bytes of device workspace vitenc_predict needs for B items of n_ctx context
- * and n_tgt target ids.  Refusals: ESHAPE (B, n_ctx or n_tgt below 1,
- * n_ctx + n_tgt above the grid's token count). */
+/* Bytes of device workspace vitenc_predict / vitenc_predict_all need for B
+ * items of n_ctx context and n_tgt target ids.  Refusals: ESHAPE (B, n_ctx or
+ * n_tgt below 1, n_ctx + n_tgt above the grid's token count). */
 vitenc_status vitenc_predict_workspace_size(const vitenc_predictor *p, int32_t B, int32_t n_ctx,
                                             int32_t n_tgt, size_t *bytes);
 
-/* Predicts the encoder features of the target tokens of B items.
- * enc_tokens: fp32 [B, n_enc, De], the encoder's patch-token features in
- * token order (n_enc must equal grid_t*grid_h*grid_w); ctx_ids int32
- * [B, n_ctx] and tgt_ids int32 [B, n_tgt]: per item, each list strictly
- * increasing, both within [0, n_enc) and disjoint.  The ids are device data
- * and are NOT checked here (the check would need a synchronisation): ids
- * that break the contract give unspecified values in out, but every access
- * stays within the buffers.  mask_index: the mask token that fills the
- * targets, in [0, n_mask_tokens).  out: fp32 [B, n_tgt, De].  workspace as
- * vitenc_encode's, of vitenc_predict_workspace_size() bytes.  Refusals: those
- * of the workspace size, ENULL, ESHAPE (n_enc), EINVAL (mask_index),
- * EWORKSPACE. */
+/* Predicts the teacher features of the target tokens of B items.
+ * enc_tokens: fp32 [n_hier_in, B, n_enc, De] (one level: [B, n_enc, De]),
+ * the encoder's patch-token features in token order (n_enc must equal
+ * grid_t*grid_h*grid_w); ctx_ids int32 [B, n_ctx] and tgt_ids int32
+ * [B, n_tgt]: per item, each list strictly increasing, both within
+ * [0, n_enc) and disjoint.  The ids are device data and are NOT checked here
+ * (the check would need a synchronisation): ids that break the contract give
+ * unspecified values in out, but every access stays within the buffers.
+ * mask_index: the mask token that fills the targets, in [0, n_mask_tokens).
+ * out: fp32 [B, n_tgt, out_dim].  workspace as vitenc_encode's, of
+ * vitenc_predict_workspace_size() bytes.  Refusals: those of the workspace
+ * size, ENULL, ESHAPE (n_enc), EINVAL (mask_index), EWORKSPACE. */
 vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens, int32_t B, int32_t n_enc,
                              const int32_t *ctx_ids, int32_t n_ctx, const int32_t *tgt_ids, int32_t n_tgt,
                              int32_t mask_index, void *workspace, size_t ws_bytes, float *out, void *stream);
+
+/* vitenc_predict that also returns the context rows (V-JEPA 2.1 "return all
+ * tokens"): out_ctx fp32 [B, n_ctx, out_dim] = the final norm's output at the
+ * context ids, in the order of ctx_ids, through proj_context.  out_ctx may be
+ * NULL (then this is vitenc_predict); a non-NULL out_ctx on a predictor
+ * without context_proj is refused with EINVAL. */
+vitenc_status vitenc_predict_all(const vitenc_predictor *p, const float *enc_tokens, int32_t B, int32_t n_enc,
+                                 const int32_t *ctx_ids, int32_t n_ctx, const int32_t *tgt_ids, int32_t n_tgt,
+                                 int32_t mask_index, void *workspace, size_t ws_bytes, float *out,
+                                 float *out_ctx, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Attentive-pool head and classifier (jepa.cpp "GGUF schema (v1)", "Head

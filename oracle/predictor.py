@@ -24,6 +24,22 @@ Readings:
     (mask_index): the pages note that the reference always uses index 1;
   * ids are distinct within an item (context and targets are disjoint), so the
     position order is unique.
+
+V-JEPA 2.1 options ("GGUF schema (v1)", "Predictor (jepa.pred.*)": n_hier_in,
+modality_embed, context_proj, out_dim; tensors pred.embed.0 / .2,
+pred.mod_embed_img / _video, pred.proj_context), with these readings:
+  * n_hier_in > 1: a context token's input is the concatenation, in level
+    order, of its n_hier_in hierarchical encoder features, and pred.embed is
+    the 2-layer MLP embed.0 -> GELU (erf) -> embed.2 (the .0 / .2 names are
+    the layers around the activation of a sequential MLP; the pages name no
+    activation there, GELU-erf is the one every MLP of the family uses);
+  * the modality vector (image for a one-frame grid, video otherwise, as the
+    encoder picks its tokenizer) is added to every predictor token, context
+    and mask tokens alike, before the blocks;
+  * pred.proj maps to out_dim (the teacher's width in 2.1, the encoder's in
+    V-JEPA 2), and pred.proj_context maps the context rows of the final norm's
+    output to the same width (the context half of "return all tokens"),
+    returned in the order of ctx_ids.
 """
 from __future__ import annotations
 
@@ -47,17 +63,35 @@ def _block_hp(hp):
                 rope_theta=hp["rope_theta"])
 
 
-def predictor_forward(hp, w, enc_tokens, ctx_ids, tgt_ids, mask_index=1, n_layers=None):
-    """enc_tokens [B, N_grid, enc_dim]; ctx_ids [B, n_ctx]; tgt_ids [B, n_tgt]
-    -> predicted target features [B, n_tgt, enc_dim] (float64)."""
-    B = enc_tokens.shape[0]
+def predictor_forward(hp, w, enc_tokens, ctx_ids, tgt_ids, mask_index=1, n_layers=None, return_context=False):
+    """enc_tokens [B, N_grid, enc_dim] (with n_hier_in > 1: [n_hier_in, B,
+    N_grid, enc_dim]); ctx_ids [B, n_ctx]; tgt_ids [B, n_tgt] -> predicted
+    target features [B, n_tgt, out_dim] (float64); with return_context also
+    the projected context rows [B, n_ctx, out_dim] (needs context_proj)."""
+    n_hier = int(hp.get("n_hier_in", 1) or 1)
+    enc = np.asarray(enc_tokens)
+    if n_hier == 1 and enc.ndim == 4:
+        enc = enc[0]
+    B = enc.shape[-3]
     n_ctx, n_tgt = ctx_ids.shape[1], tgt_ids.shape[1]
     bhp = _block_hp(hp)
     L = len(w.blocks) if n_layers is None else n_layers
-    out = np.empty((B, n_tgt, hp["enc_dim"]))
+    out_dim = int(hp.get("out_dim", 0) or hp["enc_dim"])
+    mod = None
+    if hp.get("modality_embed", 0):
+        mod = E._f64(w.mod_img if hp["grid"][0] == 1 else w.mod_video)
+    out = np.empty((B, n_tgt, out_dim))
+    out_ctx = np.empty((B, n_ctx, out_dim)) if return_context else None
     for b in range(B):
-        x_ctx = E.linear(enc_tokens[b, ctx_ids[b]], w.embed_w, w.embed_b)
+        if n_hier > 1:
+            feats = np.concatenate([enc[lv, b, ctx_ids[b]] for lv in range(n_hier)], axis=1)
+            x_ctx = E.linear(E.gelu_erf(E.linear(feats, w.embed_w, w.embed_b)), w.embed2_w, w.embed2_b)
+        else:
+            x_ctx = E.linear(enc[b, ctx_ids[b]], w.embed_w, w.embed_b)
         x_tgt = np.repeat(E._f64(w.mask_tokens[mask_index])[None, :], n_tgt, axis=0)
+        if mod is not None:
+            x_ctx = x_ctx + mod
+            x_tgt = x_tgt + mod
         ids = np.concatenate([ctx_ids[b], tgt_ids[b]]).astype(np.int64)
         x = np.concatenate([x_ctx, x_tgt], axis=0)
         assert len(np.unique(ids)) == len(ids), "token ids must be distinct"
@@ -69,5 +103,8 @@ def predictor_forward(hp, w, enc_tokens, ctx_ids, tgt_ids, mask_index=1, n_layer
         x = E.layer_norm(x[0], w.norm_w, w.norm_b, hp["ln_eps"])
         back = np.empty_like(order)
         back[order] = np.arange(len(order))
-        out[b] = E.linear(x[back][n_ctx:], w.proj_w, w.proj_b)
-    return out
+        x = x[back]
+        out[b] = E.linear(x[n_ctx:], w.proj_w, w.proj_b)
+        if return_context:
+            out_ctx[b] = E.linear(x[:n_ctx], w.proj_ctx_w, w.proj_ctx_b)
+    return (out, out_ctx) if return_context else out

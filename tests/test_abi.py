@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(V.SIGNATURES), "binding and header disagree"
-    assert L.vitenc_abi_version() == 4
+    assert L.vitenc_abi_version() == 5
 
 
 FAKE = 0x1000  # a non-NULL pointer that is never dereferenced: creation only validates

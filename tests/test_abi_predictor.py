@@ -149,3 +149,41 @@ def test_host_id_check():
         V.check_pred_ids(ctx, np.array([[1, 2, 10]], np.int32), 10)
     with pytest.raises(ValueError, match="outside"):
         V.check_pred_ids(np.array([[-1, 3, 5]], np.int32), np.array([[1, 2, 9]], np.int32), 10)
+
+
+def test_predictor21_option_tensors_are_required():
+    """Each V-JEPA 2.1 option needs its tensors; out_dim, n_hier_in and
+    embed_hidden are range-checked; out_ctx needs the context projection."""
+    import ctypes
+    from vision_transformer_amd import vitenc as V
+    L = V.lib()
+    base = dict(embed_dim=64, enc_dim=32, n_layer=1, n_head=2, ffn_dim=128, n_mask_tokens=2, ln_eps=1e-6,
+                rope_theta=1e4, rope_layout=1, grid_t=2, grid_h=3, grid_w=4, dtype=0)
+    fake = 0x1000
+
+    def create(extra_hp=None, extra_w=None):
+        hp = V.PredHparams(**dict(base, **(extra_hp or {})))
+        bw = (V.BlockWeights * 1)()
+        for n in V.BLOCK_FIELDS:
+            if n not in ("ls1", "ls2"):
+                setattr(bw[0], n, fake)
+        w = V.PredWeights(fake, fake, fake, ctypes.cast(bw, ctypes.POINTER(V.BlockWeights)), fake, fake, fake, fake)
+        for k, v in (extra_w or {}).items():
+            setattr(w, k, v)
+        h = ctypes.c_void_p()
+        st = L.vitenc_predictor_create(ctypes.byref(hp), ctypes.byref(w), ctypes.byref(h))
+        if st == 0:
+            L.vitenc_predictor_destroy(h)
+        return st
+
+    assert create() == 0
+    assert create({"n_hier_in": 4, "embed_hidden": 96}) == 3                     # ENULL: embed2
+    assert create({"n_hier_in": 4, "embed_hidden": 96}, {"embed2_w": fake, "embed2_b": fake}) == 0
+    assert create({"n_hier_in": 4, "embed_hidden": 0}, {"embed2_w": fake, "embed2_b": fake}) == 1
+    assert create({"n_hier_in": 99}) == 1
+    assert create({"modality_embed": 1}) == 3
+    assert create({"modality_embed": 1}, {"mod_embed_img": fake, "mod_embed_video": fake}) == 0
+    assert create({"context_proj": 1}) == 3
+    assert create({"context_proj": 1}, {"proj_ctx_w": fake, "proj_ctx_b": fake}) == 0
+    assert create({"out_dim": -3}) == 1
+    assert create({"out_dim": 1664}) == 0

@@ -121,7 +121,7 @@ def test_batch_equals_single_items(gpu_lib):
         o1, p1 = run_gpu(one)
         st = oracle.compare(o1[0], out[b])
         say(f"  item {b}: single vs batched {st}")
-        assert st["min_cos"] >= 1 - 1e-6 and st["maxabs"] <= 4e-3, st
+        assert st["min_cos"] >= 1 - 1e-6 and st["maxabs"] <= 5e-3, st
         assert np.abs(p1[0] - pooled[b]).max() <= 1e-3
 
 

@@ -116,3 +116,63 @@ def test_predictor_items_are_independent(gpu_lib):
     wl1.tgt_ids = np.ascontiguousarray(wl.tgt_ids[1:2])
     one = run_pred(wl1, 1)
     np.testing.assert_allclose(one[0], both[1], rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# V-JEPA 2.1 (jepa.cpp "GGUF schema (v1)", "Predictor (jepa.pred.*)"): the
+# hierarchical embed MLP, the modality vectors, the context projection and an
+# output width other than the encoder's
+# ---------------------------------------------------------------------------
+def _parity21(cfg, wl=None, rows=None):
+    from vision_transformer_amd.vitenc import Predictor
+    wl = wl or W.make_predictor_workload(cfg)
+    say(f"predict 2.1 {cfg.name} L={cfg.n_layer} B={cfg.batch} ctx={cfg.n_ctx} tgt={cfg.n_tgt} "
+        f"levels={cfg.n_hier_in} out={cfg.out_width}")
+    pred = Predictor.from_workload(wl)
+    enc = torch.from_numpy(wl.enc_tokens).cuda()
+    ctx = torch.from_numpy(wl.ctx_ids).cuda()
+    tgt = torch.from_numpy(wl.tgt_ids).cuda()
+    out, out_ctx = pred.predict(enc, ctx, tgt, mask_index=cfg.mask_index, return_context=True)
+    torch.cuda.synchronize()
+    g, gc = to_np(out), to_np(out_ctx)
+    pred.close()
+    ref, ref_ctx = oracle.predictor_forward(cfg.hparams(), wl.weights, wl.enc_tokens, wl.ctx_ids, wl.tgt_ids,
+                                            cfg.mask_index, return_context=True)
+    for name, a, b in (("targets", g, ref), ("context", gc, ref_ctx)):
+        st = oracle.compare(a, b)
+        say(f"  {name}: {st}")
+        assert gates_ok(cfg, st), (name, st)
+    return g, gc
+
+
+def test_predictor21_vit_l_full_shape_full_depth(gpu_lib):
+    """The 2.1 predictor after a ViT-L encoder: 12 blocks of width 384 over
+    2 x (1024 + 1024) tokens of the 8 x 16 x 16 grid, interleaved RoPE, video
+    modality vector, 8 mask tokens, targets and context rows projected to a
+    1664-wide teacher space, bf16."""
+    _parity21(W.PREDICTOR_21_L)
+
+
+def test_predictor21_vit_g_four_levels(gpu_lib):
+    """After a ViT-g encoder: four hierarchical levels of width 1408
+    concatenated into the 2-layer embed MLP (5632 -> 1536 -> 384), 12 blocks
+    over 1152 + 1152 tokens of the 8 x 24 x 24 grid, bf16."""
+    _parity21(W.PREDICTOR_21_G)
+
+
+def test_predictor21_small_fp32_image_grid(gpu_lib):
+    """fp32 at small ragged sizes: three levels, a one-frame grid (the image
+    modality vector), widths that are not multiples of the tiles."""
+    cfg = SMALL_F32.replace(name="pred21_small_f32", grid=(1, 6, 7), n_ctx=23, n_tgt=14, n_hier_in=3,
+                            embed_hidden=72, out_dim=52, modality_embed=1, context_proj=1, n_mask_tokens=8,
+                            rope_layout=W.LAYOUT_INTERLEAVED, mask_index=0)
+    _parity21(cfg)
+
+
+def test_predictor21_small_bf16_split_pixels_path(gpu_lib):
+    """bf16 with the levels' total width a multiple of 64, so that the
+    encoder features enter the embed GEMM as hi + lo bf16 halves."""
+    cfg = SMALL_F32.replace(name="pred21_small_bf16", dtype=W.DTYPE_BF16, enc_dim=64, n_hier_in=2,
+                            embed_hidden=128, out_dim=80, modality_embed=1, context_proj=1,
+                            rope_layout=W.LAYOUT_INTERLEAVED)
+    _parity21(cfg)

@@ -121,6 +121,32 @@ template <int NCH> __device__ __forceinline__ int swz(int row) {
 // LDS destination of the direct global -> LDS buffer loads
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Range-checked loads through a buffer resource: bytes at or past `bytes`
+// from the base (and everything, when the base is NULL) read as zero, with no
+// branch.  Used for loads issued early and consumed much later: a load under a
+// branch whose result lands in different registers on the two paths makes the
+// compiler wait for it where the paths join.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, base ? bytes : 0u, 0x00020000);
+}
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ int buf_i32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+// (the loaded vector is reinterpreted whole: taking the bits of one element
+// expression of a vector with __builtin_bit_cast reads element 0 with this
+// compiler)
+__device__ __forceinline__ float2 buf_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const f32x2_t f = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return make_float2(f.x, f.y);
+}
+__device__ __forceinline__ float4 buf_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const f32x4 f = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    return make_float4(f.x, f.y, f.z, f.w);
+}
+
 // Wait until at most N of this wave's vector memory operations are still in
 // flight (the direct-to-LDS loads retire in issue order).
 template <int N> __device__ __forceinline__ void vm_wait() {
@@ -147,33 +173,54 @@ __device__ __forceinline__ int acc_row(int i, int g) { return 8 * (i >> 2) + 4 *
 // ----------------------------------------------------------------------------
 // wave-level reductions (64 lanes)
 // ----------------------------------------------------------------------------
+// Butterfly reductions: at every step each lane combines its value with one
+// partner whose own partner it is, so all 64 lanes end with the same result
+// (the two operands of each step are the same pair).  Within a row of 16
+// lanes the partners come from DPP (quad xor 1 and xor 2, then the 8- and
+// 16-lane mirrors), across rows of a half from a swizzle (xor 16), and across
+// the two halves from one permute (xor 32).  `id` fills inactive sources.
+template <int CTRL> __device__ __forceinline__ float dpp_f32(float v, float id) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id), __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swizzle_xor16(float v) {
+    // bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10 (within 32 lanes)
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRowMirror = 0x140, kDppHalfMirror = 0x141;
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v += dpp_f32<kDppXor1>(v, 0.0f);
+    v += dpp_f32<kDppXor2>(v, 0.0f);
+    v += dpp_f32<kDppHalfMirror>(v, 0.0f);
+    v += dpp_f32<kDppRowMirror>(v, 0.0f);
+    v += swizzle_xor16(v);
+    return v + __shfl_xor(v, 32, 64);
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, dpp_f32<kDppXor1>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v, -INFINITY));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v, -INFINITY));
+    v = fmaxf(v, swizzle_xor16(v));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
 }
 
-// GELU(x) = x/2 (1 + erf(x / sqrt 2)), with erf from the rational
-// approximation 7.1.26 of Abramowitz & Stegun (Handbook of Mathematical
-// Functions): erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) e^{-z^2},
-// t = 1 / (1 + p z), z >= 0, |error| <= 1.5e-7, and erf(-z) = -erf(z).
+// GELU(x) = x Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2, with erfc from the
+// rational approximation 7.1.26 of Abramowitz & Stegun (Handbook of
+// Mathematical Functions): erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
+// e^{-z^2}, t = 1 / (1 + p z), z >= 0, |error| <= 1.5e-7.  With z = |x| / sqrt 2
+// and q = (x / 2) erfc(z): GELU(x) = x - q for x >= 0 and q for x < 0 (the
+// factor 1/2 is folded into the coefficients).
 __device__ __forceinline__ float gelu_erf(float x) {
-    const float z = fabsf(x) * 0.70710678118654752440f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float poly = fmaf(1.061405429f, t, -1.453152027f);
-    poly = fmaf(poly, t, 1.421413741f);
-    poly = fmaf(poly, t, -0.284496736f);
-    poly = fmaf(poly, t, 0.254829592f);
-    poly *= t;
-    const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
-    const float erf_abs = fmaf(-poly, e, 1.0f);
-    const float erf = x < 0.0f ? -erf_abs : erf_abs;
-    return 0.5f * x * (1.0f + erf);
+    const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(x), 0.3275911f * 0.70710678118654752440f, 1.0f));
+    float h = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+    h = fmaf(h, t, 0.5f * 1.421413741f);
+    h = fmaf(h, t, 0.5f * -0.284496736f);
+    h = fmaf(h, t, 0.5f * 0.254829592f);
+    // e^{-x^2 / 2} = 2^{-x^2 log2(e) / 2}
+    const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170368f) * x);
+    const float q = (x * t) * h * e;
+    return x >= 0.0f ? x - q : q;
 }
 
 __host__ __device__ __forceinline__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }

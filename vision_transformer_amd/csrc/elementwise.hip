@@ -140,37 +140,46 @@ __global__ __launch_bounds__(256) void layernorm_vec4_kernel(const float *__rest
                                                              const float *__restrict__ b, float eps, int M, int D,
                                                              TO *__restrict__ y) {
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // wave-uniform (scalar) row, so that the buffer resources below are scalar
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (row >= M) return;
     const int D4 = D >> 2;
-    const float4 *xr = reinterpret_cast<const float4 *>(x + (int64_t)row * D);
-    float4 v[NE];
-    float s = 0.0f;
+    // the row, the scale and the shift are all requested before the first
+    // reduction, so the three loads overlap; columns past D read as zero
+    const uint32_t rb = (uint32_t)D * 4u;
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x + (int64_t)row * D, rb);
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(w, rb), rbb = buf_rsrc(b, rb);
+    float4 v[NE], ww[NE], bb[NE];
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-        const int c4 = lane + 64 * i;
-        v[i] = c4 < D4 ? xr[c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+        const uint32_t off = (uint32_t)(lane + 64 * i) * 16u;
+        v[i] = buf_f32x4(rx, off);
+        ww[i] = buf_f32x4(rw, off);
+        bb[i] = buf_f32x4(rbb, off);
     }
+    // keep the scale and shift loads here, ahead of the reductions (the
+    // scheduler would otherwise sink them to their use, a second round trip)
+    __builtin_amdgcn_sched_barrier(0);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     const float mean = wave_sum(s) / (float)D;
     float q = 0.0f;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-        const float a = v[i].x - mean, bb = v[i].y - mean, c = v[i].z - mean, d = v[i].w - mean;
-        const float t = (a * a + bb * bb) + (c * c + d * d);
+        const float a = v[i].x - mean, c = v[i].y - mean, d = v[i].z - mean, e = v[i].w - mean;
+        const float t = (a * a + c * c) + (d * d + e * e);
         q += lane + 64 * i < D4 ? t : 0.0f;
     }
     const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)D + eps);
-    const float4 *w4 = reinterpret_cast<const float4 *>(w);
-    const float4 *b4 = reinterpret_cast<const float4 *>(b);
     TO *yr = y + (int64_t)row * D;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
         const int c4 = lane + 64 * i;
-        if (c4 >= D4) break;
-        const float4 ww = w4[c4], bb = b4[c4];
-        store4<TO>(yr + 4 * c4, (v[i].x - mean) * rstd * ww.x + bb.x, (v[i].y - mean) * rstd * ww.y + bb.y,
-                   (v[i].z - mean) * rstd * ww.z + bb.z, (v[i].w - mean) * rstd * ww.w + bb.w);
+        if (c4 < D4)
+            store4<TO>(yr + 4 * c4, (v[i].x - mean) * rstd * ww[i].x + bb[i].x,
+                       (v[i].y - mean) * rstd * ww[i].y + bb[i].y, (v[i].z - mean) * rstd * ww[i].z + bb[i].z,
+                       (v[i].w - mean) * rstd * ww[i].w + bb[i].w);
     }
 }
 

@@ -89,6 +89,93 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
     return x * q + min(x, r) + b / kXcd;
 }
 
+// Row path of the epilogue: after staging, lane l of a wave owns the 8
+// consecutive columns (l % CPR) * 8 .. + 7 of the wave's WN columns and, in
+// each MI-row block, the rows p * RPP + l / CPR for p < NPASS.
+template <int MI, int WN> struct RowPath {
+    static constexpr int CPR = WN / 8;                  // 8-column groups per row
+    static constexpr int RPP = 64 / CPR;                // rows per pass
+    static constexpr int NPASS = (MI + RPP - 1) / RPP;  // passes per MI-row block
+};
+
+// What the epilogue of a lane reads besides the accumulators, requested at
+// kernel start so that its latency hides under the main loop: the bias and
+// layer scale of the lane's 8 columns; for the residual epilogue the fp32
+// residual values the lane will update (NZ rows of 8 columns, when they fit
+// in registers; wider tiles request each row block's values one block
+// ahead instead); for QKV the packed (t, h, w) of tile row m0 + tid and this
+// thread's share (NTAB pairs) of the RoPE cos / sin table.
+template <int NZ, int NTAB> struct EpiPre {
+    float bias8[8], ls8[8]; // 0 past N (ls8 is used only when there is a layer scale)
+    float4 z[NZ > 0 ? NZ : 1][2];
+    int pk;
+    float2 tab[NTAB > 0 ? NTAB : 1];
+    float vbias; // QKV: bias of the lane's column of the transposed V path
+};
+
+// the fast (vector) residual access of one lane-row: the 8 columns exist
+// and the rows are 16-byte aligned
+__device__ __forceinline__ bool z_vec(const EpiArgs &ep, int row, int M, bool col_full) {
+    return row < M && col_full && (ep.ldz % 4) == 0;
+}
+
+// All loads here are range-checked buffer loads with no branch around them
+// (see buf_rsrc): their results are consumed only in the epilogue.
+template <int EPI, int NZ, int NTAB, int BM, int FM, int NT, int MI, int WN>
+__device__ __forceinline__ EpiPre<NZ, NTAB> epi_prefetch(int m0, int n0, int woff_m, int woff_n, int M, int N,
+                                                         const EpiArgs &ep) {
+    using RP = RowPath<MI, WN>;
+    EpiPre<NZ, NTAB> pre;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int col0 = n0 + woff_n + (lane % RP::CPR) * 8;
+    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(ep.bias, (uint32_t)N * 4u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pre.bias8[j] = buf_f32(rb, (uint32_t)(col0 + j) * 4u);
+    if constexpr (EPI == EPI_RESID) {
+        const __amdgpu_buffer_rsrc_t rl = buf_rsrc(ep.ls, (uint32_t)N * 4u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pre.ls8[j] = buf_f32(rl, (uint32_t)(col0 + j) * 4u);
+        if constexpr (NZ > 0) {
+            // rows of this wave's part of the tile, from its first row on
+            const int64_t r0 = m0 + woff_m;
+            const int64_t bytes = r0 < M && ep.splits == 1 ? (int64_t)(M - r0) * ep.ldz * 4 : 0;
+            const __amdgpu_buffer_rsrc_t rz =
+                buf_rsrc(ep.Z + r0 * ep.ldz, (uint32_t)(bytes < 0xFFFFFFF0ll ? bytes : 0xFFFFFFF0ll));
+#pragma unroll
+            for (int i = 0; i < NZ; ++i) {
+                const int fm = i / RP::NPASS, p = i % RP::NPASS;
+                const int r = fm * MI + p * RP::RPP + lane / RP::CPR;
+                const uint32_t off = (uint32_t)(((int64_t)r * ep.ldz + col0) * 4);
+                pre.z[i][0] = buf_f32x4(rz, off);
+                pre.z[i][1] = buf_f32x4(rz, off + 16u);
+            }
+        }
+    }
+    if constexpr (EPI == EPI_QKV) {
+        // the transposed V path: lane -> column woff_n + lane % WN
+        pre.vbias = buf_f32(rb, (uint32_t)(n0 + woff_n + lane % WN) * 4u);
+        // packed position of row m0 + tid (read only for rows that have one)
+        const int row = m0 + tid;
+        const int b = row / ep.Ntok, tok = row - b * ep.Ntok;
+        const bool has = tid < BM && row < M && ep.rope && tok >= ep.prefix;
+        const __amdgpu_buffer_rsrc_t rp = buf_rsrc(ep.rope ? ep.tok_pos : nullptr, 0xFFFFFFF0u);
+        pre.pk = buf_i32(rp, has ? (uint32_t)(((int64_t)b * ep.tok_pos_stride + tok - ep.prefix) * 4) : 0u);
+        if constexpr (NTAB > 0) {
+            const bool fits = ep.rope && ep.rope_tab_pairs <= NTAB * NT;
+            const __amdgpu_buffer_rsrc_t rt = buf_rsrc(ep.rope_tab, fits ? (uint32_t)ep.rope_tab_pairs * 8u : 0u);
+#pragma unroll
+            for (int i = 0; i < NTAB; ++i) pre.tab[i] = buf_f32x2(rt, (uint32_t)(tid + i * NT) * 8u);
+        }
+    }
+    return pre;
+}
+
+// GELU of the epilogue
+template <int EPI> __device__ __forceinline__ float epi_act(float v) {
+    if constexpr (EPI == EPI_GELU) return gelu_erf(v);
+    else return v;
+}
+
 // Epilogue of one workgroup tile: v = accumulator + bias, then the EPI
 // operation.  Each wave stages one MI-row block of its accumulators at a time
 // through a private LDS area (MI x (WN + 4) fp32) and reads it back so that
@@ -96,15 +183,22 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
 // outputs are then 16-byte, row-contiguous vectors instead of per-element
 // accesses.  The V part of the QKV projection is read back transposed (8
 // consecutive rows of one column) because V is stored transposed per head.
+// Everything the epilogue reads from global memory besides the accumulators
+// was requested at kernel start (epi_prefetch), except for the residual rows
+// of tiles too wide to hold them in registers: those are requested one row
+// block ahead.
 // ri: LDS scratch for BM row descriptors, stage: this wave's staging area.
 // Every thread of the workgroup must call this (it contains a barrier).
-template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, bool SWAP, typename AccT>
-__device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, float *stage, float2 *lds_tab,
-                                              int lds_tab_cap, int m0, int n0, int woff_m, int woff_n, int M, int N,
-                                              const EpiArgs &ep, float *part = nullptr) {
+template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, bool SWAP, int NZ, int NTAB,
+          typename AccT>
+__device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], const EpiPre<NZ, NTAB> &pre, RowInfo *ri,
+                                              float *stage, float2 *lds_tab, int lds_tab_cap, int m0, int n0,
+                                              int woff_m, int woff_n, int M, int N, const EpiArgs &ep,
+                                              float *part = nullptr) {
+    using RP = RowPath<MI, WN>;
     constexpr int NV = MI == 32 ? 16 : 4; // accumulator values per lane per block
     constexpr int LD = WN + 4;            // staging row stride (floats), 16-byte aligned
-    constexpr int CPR = WN / 8;           // 8-column groups per row
+    constexpr int CPR = RP::CPR, RPP = RP::RPP, NPASS = RP::NPASS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int lcol = lane & (MI - 1);
     auto vrow = [&](int i) { return MI == 32 ? acc_row(i, lane >> 5) : 4 * (lane >> 4) + i; };
@@ -167,7 +261,7 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
                     info.pos = 0;
                     info.qk_off = ((int64_t)b * (ep.D / ep.head_dim) * ep.Ntok + tok) * ep.head_dim;
                     if (ep.rope && tok >= ep.prefix) {
-                        const int pk = ep.tok_pos[(int64_t)b * ep.tok_pos_stride + tok - ep.prefix];
+                        const int pk = pre.pk; // t < BM <= NT: this thread's own prefetched row
                         info.pos = 1;
                         info.base[0] = (pk & 1023) * ep.d_rot;
                         info.base[1] = (ep.gt + ((pk >> 10) & 1023)) * ep.d_rot;
@@ -178,16 +272,22 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
             ri[t] = info;
         }
     }
-    // The RoPE table goes to LDS when it fits, followed by one identity pair
+    // The RoPE table goes to LDS when it fits, followed by two identity pairs
     // (cos 1, sin 0) that the unrotated dims read, so that the rotation needs
     // no per-element branch.  Otherwise it is read from global memory.
     const float2 *tab = reinterpret_cast<const float2 *>(ep.rope_tab);
     const int id_pair = ep.rope_tab_pairs;
-    const bool tab_lds = EPI == EPI_QKV && ep.rope && ep.rope_tab_pairs + 1 <= lds_tab_cap;
+    const bool tab_lds = EPI == EPI_QKV && ep.rope && ep.rope_tab_pairs + 2 <= lds_tab_cap;
     if constexpr (EPI == EPI_QKV) {
         if (tab_lds) {
-            for (int t = tid; t < ep.rope_tab_pairs; t += NT) lds_tab[t] = tab[t];
-            if (tid == 0) lds_tab[id_pair] = make_float2(1.0f, 0.0f);
+            if (NTAB > 0 && ep.rope_tab_pairs <= NTAB * NT) {
+#pragma unroll
+                for (int i = 0; i < (NTAB > 0 ? NTAB : 1); ++i)
+                    if (tid + i * NT < ep.rope_tab_pairs) lds_tab[tid + i * NT] = pre.tab[i];
+            } else {
+                for (int t = tid; t < ep.rope_tab_pairs; t += NT) lds_tab[t] = tab[t];
+            }
+            if (tid < 2) lds_tab[id_pair + tid] = make_float2(1.0f, 0.0f);
         }
     }
     __syncthreads();
@@ -200,19 +300,15 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
     const int col0 = n0 + woff_n + c0;
     const bool col_any = col0 < N;
     const bool col_full = col0 + 8 <= N;
-    float bias8[8], ls8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const bool ok = col0 + j < N;
-        bias8[j] = (ok && ep.bias) ? ep.bias[col0 + j] : 0.0f;
-        ls8[j] = (ok && ep.ls) ? ep.ls[col0 + j] : 1.0f;
-    }
     int which = 0, head = 0, dd0 = 0;
     int axis8[8], jr8[8];
     // LDS-table RoPE: a lane's 8 dims meet at most two axis segments (every
     // segment is at least 10 dims wide): selectors s_lo / s_hi of the row's
-    // table base (0..2 = t, h, w; 3 = the identity pair), dims j < jsplit use
-    // s_lo, and off8[j] is the entry within the segment (0 for the identity)
+    // table base (0..2 = t, h, w; 3 = the identity pairs), dims j < jsplit use
+    // s_lo, and off8[j] is the entry within the segment (0 for the identity).
+    // Segments and 8-column groups start at even dims, so every aligned pair
+    // (2u, 2u + 1) of a lane's dims reads two adjacent table entries with one
+    // 16-byte LDS read.
     int s_lo = 3, s_hi = 3, jsplit = 8, off8[8];
     int64_t qk_col = 0;
     if constexpr (EPI == EPI_QKV) {
@@ -238,7 +334,33 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
     }
     const bool qk_cols = EPI == EPI_QKV && which < 2;
 
-    auto row_path = [&](int rt, const float (&x)[8]) {
+    // residual rows (when not prefetched at kernel start): the values of row
+    // blocks fm and fm + 1 are requested before block fm is processed, so one
+    // round trip to memory serves two blocks
+    constexpr bool kZBlock = EPI == EPI_RESID && NZ == 0;
+    constexpr int NZB = kZBlock ? NPASS : 1;
+    constexpr int ZD = FM < 2 ? FM : 2; // blocks in flight
+    float4 zq[ZD][NZB][2];
+    // branch-free range-checked loads (see buf_rsrc) from the wave's first row
+    const int64_t zr0 = m0 + woff_m;
+    const int64_t zbytes = kZBlock && !part && zr0 < M ? (int64_t)(M - zr0) * ep.ldz * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rzb =
+        buf_rsrc(kZBlock ? ep.Z + zr0 * ep.ldz : nullptr, (uint32_t)(zbytes < 0xFFFFFFF0ll ? zbytes : 0xFFFFFFF0ll));
+    auto load_zblock = [&](float4 (&dst)[NZB][2], int fm) {
+        if constexpr (kZBlock) {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p) {
+                const int r = fm * MI + p * RPP + lane / CPR;
+                const uint32_t off = (uint32_t)(((int64_t)r * ep.ldz + col0) * 4);
+                dst[p][0] = buf_f32x4(rzb, off);
+                dst[p][1] = buf_f32x4(rzb, off + 16u);
+            }
+        }
+    };
+#pragma unroll
+    for (int f = 0; f < ZD; ++f) load_zblock(zq[f], f);
+
+    auto row_path = [&](int rt, int zi, int p, int zslot, const float (&x)[8]) {
         const int row = m0 + rt;
         if (row >= M || !col_any) return;
         if (part) {
@@ -255,12 +377,10 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
         }
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = x[j] + bias8[j];
+        for (int j = 0; j < 8; ++j) v[j] = x[j] + pre.bias8[j];
         if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
-            if constexpr (EPI == EPI_GELU) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = gelu_erf(v[j]);
-            }
+            for (int j = 0; j < 8; ++j) v[j] = epi_act<EPI>(v[j]);
             T *dst = reinterpret_cast<T *>(ep.out) + (int64_t)row * ep.ldo + col0;
             if (col_full && (ep.ldo % 8) == 0) {
                 store_vec8<T>(dst, v);
@@ -270,15 +390,26 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
             }
         } else if constexpr (EPI == EPI_RESID) {
             float *z = ep.Z + (int64_t)row * ep.ldz + col0;
-            if (col_full && (ep.ldz % 4) == 0) {
-                float4 z0 = reinterpret_cast<const float4 *>(z)[0], z1 = reinterpret_cast<const float4 *>(z)[1];
-                z0.x += ls8[0] * v[0]; z0.y += ls8[1] * v[1]; z0.z += ls8[2] * v[2]; z0.w += ls8[3] * v[3];
-                z1.x += ls8[4] * v[4]; z1.y += ls8[5] * v[5]; z1.z += ls8[6] * v[6]; z1.w += ls8[7] * v[7];
+            if (z_vec(ep, row, M, col_full)) {
+                float4 z0, z1;
+                if constexpr (NZ > 0) {
+                    z0 = pre.z[zi][0];
+                    z1 = pre.z[zi][1];
+                } else {
+                    z0 = zq[zslot][p][0];
+                    z1 = zq[zslot][p][1];
+                }
+                if (ep.ls) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] *= pre.ls8[j];
+                }
+                z0.x += v[0]; z0.y += v[1]; z0.z += v[2]; z0.w += v[3];
+                z1.x += v[4]; z1.y += v[5]; z1.z += v[6]; z1.w += v[7];
                 reinterpret_cast<float4 *>(z)[0] = z0;
                 reinterpret_cast<float4 *>(z)[1] = z1;
             } else {
                 for (int j = 0; j < 8; ++j)
-                    if (col0 + j < N) z[j] += ls8[j] * v[j];
+                    if (col0 + j < N) z[j] += (ep.ls ? pre.ls8[j] : 1.0f) * v[j];
             }
         } else if constexpr (EPI == EPI_PATCH) {
             const RowInfo info = ri[rt];
@@ -300,10 +431,13 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
                         return sx == 0 ? info.base[0] : sx == 1 ? info.base[1] : sx == 2 ? info.base[2] : id_pair;
                     };
                     const int b_lo = sel(s_lo), b_hi = sel(s_hi);
+                    const float4 *tab4 = reinterpret_cast<const float4 *>(lds_tab);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float2 cs = lds_tab[(j < jsplit ? b_lo : b_hi) + off8[j]];
-                        y[j] = v[j] * cs.x + v[j ^ 1] * cs.y;
+                    for (int u = 0; u < 4; ++u) {
+                        // entries (2u, 2u + 1): (cos, signed sin) of dim 2u, then of dim 2u + 1
+                        const float4 cs = tab4[((2 * u < jsplit ? b_lo : b_hi) + off8[2 * u]) >> 1];
+                        y[2 * u] = v[2 * u] * cs.x + v[2 * u + 1] * cs.y;
+                        y[2 * u + 1] = v[2 * u + 1] * cs.z + v[2 * u] * cs.w;
                     }
                 } else {
 #pragma unroll
@@ -348,18 +482,21 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // row path: lane -> (row, 8-column group)
-        constexpr int RPP = 64 / CPR; // rows per pass
-        for (int r0 = 0; r0 < MI; r0 += RPP) {
-            const int r = r0 + lane / CPR;
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int r = p * RPP + lane / CPR;
             if (r < MI && lane < RPP * CPR) {
                 const float4 x0 = *reinterpret_cast<const float4 *>(&stage[r * LD + c0]);
                 const float4 x1 = *reinterpret_cast<const float4 *>(&stage[r * LD + c0 + 4]);
                 const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                row_path(woff_m + fm * MI + r, x);
+                row_path(woff_m + fm * MI + r, fm * NPASS + p, p, fm % ZD, x);
             }
         }
+        // the slot of block fm is free: request block fm + ZD into it
+        if (fm + ZD < FM) load_zblock(zq[fm % ZD], fm + ZD);
         if constexpr (EPI == EPI_QKV) {
             // V columns: lane -> (column, 8 consecutive rows), stored along tokens
+            static_assert(64 % WN == 0, "one V column per lane");
             const int cbase = n0 + woff_n;
             if (cbase + WN > 2 * ep.D) {
                 const int H = ep.D / ep.head_dim;
@@ -367,7 +504,7 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], RowInfo *ri, 
                     const int c = cc % WN, rg = cc / WN;
                     const int col = cbase + c;
                     if (col < 2 * ep.D || col >= N) continue;
-                    const float bias = ep.bias ? ep.bias[col] : 0.0f;
+                    const float bias = pre.vbias;
                     const int within = col - 2 * ep.D;
                     const int head = within / ep.head_dim, dd = within - head * ep.head_dim;
                     float v[8];
@@ -426,6 +563,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
     const int lc = tid & 7, lr = tid >> 3;
+    using RP = RowPath<32, WN>;
+    constexpr int kNZ = 0;
+    // the 128 x 128 tiles of this kernel use nearly every register already:
+    // their QKV epilogue copies the RoPE table from global memory instead
+    constexpr int kNTab = (EPI == EPI_QKV && BM < 128) ? 4 : 0;
+    const auto pre = epi_prefetch<EPI, kNZ, kNTab, BM, FM, kThreads, 32, WN>(m0, n0, wm * WM, wn * WN, M, N, ep);
 
     // per-thread row pointers of the chunks this thread stages
     const T *pa[A_PER];
@@ -538,7 +681,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(smem) - kRiBytes - kStageBytes) / 8;
     gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN, false>(
-        acc, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N, ep,
+        acc, pre, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N, ep,
         ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
 }
 
@@ -624,6 +767,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     const int tile = xcd_tile(blockIdx.x - split * ntile, ntile);
     const int tm = tile / tiles_n, tn = tile - tm * tiles_n;
     const int m0 = tm * BM, n0 = tn * BN;
+    using RP = RowPath<MI, WN>;
+    // (the residual rows are requested at the start of the epilogue: requested
+    // here they would be returned, in order, ahead of the first slabs)
+    constexpr int kNZ = 0;
+    constexpr int kNTab = EPI == EPI_QKV ? 4 : 0;
+    const auto pre = epi_prefetch<EPI, kNZ, kNTab, BM, FM, NT, MI, WN>(m0, n0, wm * WM, wn * WN, M, N, ep);
 
     // Buffer loads: one resource per operand, a per-lane byte offset and a
     // scalar offset for the slab and the instruction's row block.  Lane l of
@@ -838,7 +987,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     float *estage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * MI * (WN + 4);
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(lds) - kRiBytes - kStageBytes) / 8;
-    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, MI == 32>(acc, ri, estage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N,
+    gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, MI == 32>(acc, pre, ri, estage, ltab, kTabCap, m0, n0, wm * WM,
+                                                            wn * WN, M, N,
                                                   ep, ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
 }
 

@@ -30,7 +30,7 @@ struct EpiArgs {
     int64_t ldz = 0;
     const float *ls = nullptr;
     // PATCH: GEMM row m = b*Np + n -> token row b*Ntok + prefix + n, or
-    // row_map[m] when row_map is set (then pos and mod must be null)
+    // row_map[m] when row_map is set (then pos must be null; mod is added)
     const float *pos = nullptr;      // fp32 [Ntok, ldz] or null
     const float *mod = nullptr;      // fp32 [ldz] or null
     int Np = 0, Ntok = 0, prefix = 0;
@@ -111,12 +111,14 @@ hipError_t launch_pred_order(const int *ctx_ids, int nc, const int *tgt_ids, int
                              int *row_ctx, int *row_tgt, int *tok_pos, hipStream_t s);
 // out row r (dtype out_dtype, stride ldo) = fp32 src row rows[r] when rows is
 // set, else row ids[r] of item r / per_item (src_rows rows per item), D
-// columns; split (16-bit out only): rounded value in [0, D), remainder in [D, 2D)
+// columns; split (16-bit out only): rounded value in [0, D), remainder in
+// [lo_off, lo_off + D) of the out row (lo_off < 0: D)
 hipError_t launch_gather_rows(int out_dtype, const float *src, int64_t lds, const int *rows, const int *ids,
                               int per_item, int src_rows, int R, int D, bool split, void *out, int64_t ldo,
-                              hipStream_t s);
-// Z row rows[r] = vec (D fp32) for r in [0, R)
-hipError_t launch_fill_rows(const float *vec, const int *rows, int R, int D, float *Z, hipStream_t s);
+                              hipStream_t s, int64_t lo_off = -1);
+// Z row rows[r] = vec (+ add when set, D fp32 each) for r in [0, R)
+hipError_t launch_fill_rows(const float *vec, const float *add, const int *rows, int R, int D, float *Z,
+                            hipStream_t s);
 hipError_t launch_zero(float *x, int64_t n, hipStream_t s);
 
 // attentive-pool head: matrix-vector products for nb <= any items

@@ -4,6 +4,7 @@
 // "Predictor (jepa.pred.*)").  Every refusal happens before device work.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -47,6 +48,18 @@ vitenc_status validate(const vitenc_pred_hparams *hp) {
         return fail(VITENC_EINVAL, "token grid of more than 2^22 tokens");
     if (hp->dtype != VITENC_F32 && hp->dtype != VITENC_BF16 && hp->dtype != VITENC_F16)
         return fail(VITENC_EINVAL, "unknown dtype %d", hp->dtype);
+    if (hp->out_dim != 0 && !in_range(hp->out_dim, 1, 65536))
+        return fail(VITENC_EINVAL, "out_dim %d outside 1..65536 (0: enc_dim)", hp->out_dim);
+    if (!in_range(hp->n_hier_in, 0, VITENC_MAX_HIER))
+        return fail(VITENC_EINVAL, "n_hier_in %d outside 0..%d", hp->n_hier_in, VITENC_MAX_HIER);
+    if (hp->n_hier_in > 1 && !in_range(hp->embed_hidden, 1, 65536))
+        return fail(VITENC_EINVAL, "embed_hidden %d outside 1..65536 (needed with n_hier_in > 1)", hp->embed_hidden);
+    if ((int64_t)(hp->n_hier_in > 1 ? hp->n_hier_in : 1) * hp->enc_dim > 65536)
+        return fail(VITENC_EINVAL, "n_hier_in x enc_dim above 65536");
+    if (hp->modality_embed != 0 && hp->modality_embed != 1)
+        return fail(VITENC_EINVAL, "modality_embed %d is not 0 or 1", hp->modality_embed);
+    if (hp->context_proj != 0 && hp->context_proj != 1)
+        return fail(VITENC_EINVAL, "context_proj %d is not 0 or 1", hp->context_proj);
     if (hp->embed_dim % hp->n_head)
         return fail(VITENC_EINVAL, "embed_dim %d not divisible by n_head %d", hp->embed_dim, hp->n_head);
     const int hd = hp->embed_dim / hp->n_head;
@@ -58,9 +71,10 @@ vitenc_status validate(const vitenc_pred_hparams *hp) {
 
 struct PredPlan {
     int B, nc, nt, N, M, D, De, F, nh, hd, ldv, lda_e;
+    int nh_in, Ke, Do, Hd; // hierarchical levels, embed input width, output width, embed MLP hidden width
     bool split;
     size_t off_Z, off_Y, off_Q, off_K, off_V, off_O, off_U, off_A, off_Zt, off_rctx, off_rtgt, off_tok, off_rope,
-        off_attn, total;
+        off_attn, off_Ue, total;
 };
 
 vitenc_status make_plan(const vitenc_predictor *p, int B, int nc, int nt, PredPlan &pl) {
@@ -76,8 +90,12 @@ vitenc_status make_plan(const vitenc_predictor *p, int B, int nc, int nt, PredPl
     pl.B = B; pl.nc = nc; pl.nt = nt; pl.N = nc + nt; pl.M = B * pl.N;
     pl.D = hp.embed_dim; pl.De = hp.enc_dim; pl.F = hp.ffn_dim; pl.nh = hp.n_head; pl.hd = pl.D / pl.nh;
     pl.ldv = (int)rup(pl.N, 64);
-    pl.lda_e = embed_lda(hp.dtype, pl.De);
-    pl.split = pl.lda_e == 2 * pl.De;
+    pl.nh_in = hp.n_hier_in > 1 ? hp.n_hier_in : 1;
+    pl.Ke = pl.nh_in * pl.De;
+    pl.Do = hp.out_dim ? hp.out_dim : pl.De;
+    pl.Hd = pl.nh_in > 1 ? hp.embed_hidden : 0;
+    pl.lda_e = embed_lda(hp.dtype, pl.Ke);
+    pl.split = pl.lda_e == 2 * pl.Ke;
     const size_t es = (size_t)dtype_size(hp.dtype);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -94,7 +112,9 @@ vitenc_status make_plan(const vitenc_predictor *p, int B, int nc, int nt, PredPl
     pl.off_O = take(M * D * es);
     pl.off_U = take(M * (size_t)pl.F * es);
     pl.off_A = take((size_t)B * nc * pl.lda_e * es);
-    pl.off_Zt = take((size_t)B * nt * D * 4);
+    // target rows, then (context projection) the context rows, of the norm
+    pl.off_Zt = take((size_t)B * std::max(nc, nt) * D * 4);
+    pl.off_Ue = pl.Hd ? take((size_t)B * nc * pl.Hd * es) : 0;
     pl.off_rctx = take((size_t)B * nc * 4);
     pl.off_rtgt = take((size_t)B * nt * 4);
     pl.off_tok = take(M * 4);
@@ -128,6 +148,12 @@ vitenc_status vitenc_predictor_create(const vitenc_pred_hparams *hp, const viten
     if (!w->embed_w || !w->embed_b || !w->mask_tokens || !w->norm_w || !w->norm_b || !w->proj_w || !w->proj_b)
         return fail(VITENC_ENULL, "a required predictor tensor is NULL");
     if (!w->blocks) return fail(VITENC_ENULL, "blocks is NULL");
+    if (hp->n_hier_in > 1 && (!w->embed2_w || !w->embed2_b))
+        return fail(VITENC_ENULL, "n_hier_in > 1 needs embed2_w / embed2_b");
+    if (hp->modality_embed && (!w->mod_embed_img || !w->mod_embed_video))
+        return fail(VITENC_ENULL, "modality_embed needs mod_embed_img / mod_embed_video");
+    if (hp->context_proj && (!w->proj_ctx_w || !w->proj_ctx_b))
+        return fail(VITENC_ENULL, "context_proj needs proj_ctx_w / proj_ctx_b");
     for (int i = 0; i < hp->n_layer; ++i) {
         const vitenc_block_weights &b = w->blocks[i];
         const void *req[] = {b.ln1_w, b.ln1_b, b.qkv_w, b.qkv_b, b.out_w, b.out_b,
@@ -160,6 +186,14 @@ vitenc_status vitenc_predict_workspace_size(const vitenc_predictor *p, int32_t B
 vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens, int32_t B, int32_t n_enc,
                              const int32_t *ctx_ids, int32_t n_ctx, const int32_t *tgt_ids, int32_t n_tgt,
                              int32_t mask_index, void *workspace, size_t ws_bytes, float *out, void *stream) {
+    return vitenc_predict_all(p, enc_tokens, B, n_enc, ctx_ids, n_ctx, tgt_ids, n_tgt, mask_index, workspace,
+                              ws_bytes, out, nullptr, stream);
+}
+
+vitenc_status vitenc_predict_all(const vitenc_predictor *p, const float *enc_tokens, int32_t B, int32_t n_enc,
+                                 const int32_t *ctx_ids, int32_t n_ctx, const int32_t *tgt_ids, int32_t n_tgt,
+                                 int32_t mask_index, void *workspace, size_t ws_bytes, float *out, float *out_ctx,
+                                 void *stream) {
     clear_error();
     if (!p) return fail(VITENC_ENULL, "predictor is NULL");
     if (!enc_tokens || !ctx_ids || !tgt_ids || !out) return fail(VITENC_ENULL, "enc_tokens / ids / out is NULL");
@@ -172,6 +206,8 @@ vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens,
         return fail(VITENC_ESHAPE, "n_enc %d differs from the grid's %d tokens", n_enc, n_grid);
     if (mask_index < 0 || mask_index >= hp.n_mask_tokens)
         return fail(VITENC_EINVAL, "mask_index %d outside [0, %d)", mask_index, hp.n_mask_tokens);
+    if (out_ctx && !hp.context_proj)
+        return fail(VITENC_EINVAL, "out_ctx given to a predictor without a context projection");
     if (!workspace) return fail(VITENC_ENULL, "workspace is NULL");
     if ((uintptr_t)workspace % 256) return fail(VITENC_EWORKSPACE, "workspace not 256-byte aligned");
     if (ws_bytes < pl.total) return fail(VITENC_EWORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, pl.total);
@@ -186,29 +222,61 @@ vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens,
     int *row_tgt = reinterpret_cast<int *>(ws + pl.off_rtgt);
     int *tok_pos = reinterpret_cast<int *>(ws + pl.off_tok);
     float *rope_tab = reinterpret_cast<float *>(ws + pl.off_rope);
-    const int D = pl.D, De = pl.De;
+    const int D = pl.D, De = pl.De, Ke = pl.Ke, Do = pl.Do;
+    // the modality vector: image for a one-frame grid, video otherwise
+    const float *mod = !hp.modality_embed ? nullptr : hp.grid_t == 1 ? p->w.mod_embed_img : p->w.mod_embed_video;
 
     // token order: the Z row of every context and target token, and the
     // position of every Z row
     CHECK_DEV(launch_pred_order(ctx_ids, n_ctx, tgt_ids, n_tgt, B, hp.grid_t, hp.grid_h, hp.grid_w, row_ctx, row_tgt,
                                 tok_pos, s),
               "token order");
-    // context rows: embed the encoder features of the context ids
-    CHECK_DEV(launch_gather_rows(dt, enc_tokens, De, nullptr, ctx_ids, n_ctx, n_enc, B * n_ctx, De, pl.split, A,
-                                 pl.lda_e, s),
-              "context gather");
+    // context rows: the encoder features of the context ids, the levels of a
+    // hierarchical input side by side (level l in columns [l De, (l+1) De) of
+    // each half of a split row)
+    for (int l = 0; l < pl.nh_in; ++l) {
+        const float *src = enc_tokens + (int64_t)l * B * n_enc * De;
+        void *dst = static_cast<char *>(A) + (size_t)l * De * dtype_size(dt);
+        CHECK_DEV(launch_gather_rows(dt, src, De, nullptr, ctx_ids, n_ctx, n_enc, B * n_ctx, De, pl.split, dst,
+                                     pl.lda_e, s, Ke),
+                  "context gather");
+    }
     {
+        const bool mlp = pl.nh_in > 1;
         EpiArgs ep;
         ep.bias = p->w.embed_b;
-        ep.Z = Z;
-        ep.ldz = D;
-        ep.row_map = row_ctx;
-        ep.kwrap = pl.split ? De : 0;
-        CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda_e, p->w.embed_w, De, B * n_ctx, D, pl.split ? 2 * De : De, ep, s),
-                  "embed GEMM");
+        ep.kwrap = pl.split ? Ke : 0;
+        if (mlp) {
+            // embed.0 + GELU into the hidden rows, then embed.2 below
+            ep.out = ws + pl.off_Ue;
+            ep.ldo = pl.Hd;
+            CHECK_DEV(launch_gemm(dt, EPI_GELU, A, pl.lda_e, p->w.embed_w, Ke, B * n_ctx, pl.Hd,
+                                  pl.split ? 2 * Ke : Ke, ep, s),
+                      "embed MLP GEMM");
+        } else {
+            ep.Z = Z;
+            ep.ldz = D;
+            ep.row_map = row_ctx;
+            ep.mod = mod;
+            CHECK_DEV(launch_gemm(dt, EPI_PATCH, A, pl.lda_e, p->w.embed_w, Ke, B * n_ctx, D, pl.split ? 2 * Ke : Ke,
+                                  ep, s),
+                      "embed GEMM");
+        }
+        if (mlp) {
+            EpiArgs e2;
+            e2.bias = p->w.embed2_b;
+            e2.Z = Z;
+            e2.ldz = D;
+            e2.row_map = row_ctx;
+            e2.mod = mod;
+            CHECK_DEV(launch_gemm(dt, EPI_PATCH, ws + pl.off_Ue, pl.Hd, p->w.embed2_w, pl.Hd, B * n_ctx, D, pl.Hd, e2,
+                                  s),
+                      "embed MLP output GEMM");
+        }
     }
-    // target rows: the mask token
-    CHECK_DEV(launch_fill_rows(p->w.mask_tokens + (int64_t)mask_index * D, row_tgt, B * n_tgt, D, Z, s), "mask rows");
+    // target rows: the mask token (+ the modality vector)
+    CHECK_DEV(launch_fill_rows(p->w.mask_tokens + (int64_t)mask_index * D, mod, row_tgt, B * n_tgt, D, Z, s),
+              "mask rows");
     CHECK_DEV(launch_rope_table(pl.hd, hp.rope_layout, 0, 0, hp.rope_theta, hp.grid_t, hp.grid_h, hp.grid_w, rope_tab,
                                 nullptr, s),
               "rope table");
@@ -228,16 +296,24 @@ vitenc_status vitenc_predict(const vitenc_predictor *p, const float *enc_tokens,
         const hipError_t e = run_block(g, bb, p->blocks[l], s, &what);
         CHECK_DEV(e, what);
     }
-    // target rows in the order of tgt_ids -> norm -> proj (out = 0 + proj)
-    CHECK_DEV(launch_gather_rows(DT_F32, Z, D, row_tgt, nullptr, 1, 1, B * n_tgt, D, false, Zt, D, s), "target gather");
-    CHECK_DEV(launch_layernorm(dt, Zt, p->w.norm_w, p->w.norm_b, hp.ln_eps, B * n_tgt, D, Y, s), "final norm");
-    CHECK_DEV(launch_zero(out, (int64_t)B * n_tgt * De, s), "output clear");
-    {
+    // rows in the order of an id list -> norm -> projection (out = 0 + proj)
+    auto project = [&](const int *rows, int n, const void *pw, const float *pb, float *dst,
+                       const char *what) -> vitenc_status {
+        CHECK_DEV(launch_gather_rows(DT_F32, Z, D, rows, nullptr, 1, 1, B * n, D, false, Zt, D, s), what);
+        CHECK_DEV(launch_layernorm(dt, Zt, p->w.norm_w, p->w.norm_b, hp.ln_eps, B * n, D, Y, s), what);
+        CHECK_DEV(launch_zero(dst, (int64_t)B * n * Do, s), what);
         EpiArgs ep;
-        ep.bias = p->w.proj_b;
-        ep.Z = out;
-        ep.ldz = De;
-        CHECK_DEV(launch_gemm(dt, EPI_RESID, Y, D, p->w.proj_w, D, B * n_tgt, De, D, ep, s), "proj GEMM");
+        ep.bias = pb;
+        ep.Z = dst;
+        ep.ldz = Do;
+        CHECK_DEV(launch_gemm(dt, EPI_RESID, Y, D, pw, D, B * n, Do, D, ep, s), what);
+        return VITENC_OK;
+    };
+    st = project(row_tgt, n_tgt, p->w.proj_w, p->w.proj_b, out, "target projection");
+    if (st != VITENC_OK) return st;
+    if (out_ctx) {
+        st = project(row_ctx, n_ctx, p->w.proj_ctx_w, p->w.proj_ctx_b, out_ctx, "context projection");
+        if (st != VITENC_OK) return st;
     }
     return VITENC_OK;
 }

@@ -54,14 +54,15 @@ __global__ __launch_bounds__(256) void pred_order_kernel(const int *__restrict__
 
 // out[r, :] = src row of r, converted to T.  The source row is rows[r] when
 // rows is set, else item r / per_item's row ids[r] (clamped to the item).
-// SPLIT: the out row has 2*D columns, the rounded value in [0, D) and what
-// rounding left over in [D, 2D).  One workgroup per row, four columns per
+// SPLIT: the rounded value goes to columns [0, D) and what rounding left
+// over to [lo_off, lo_off + D) of the out row (lo_off = D: a row of 2D
+// columns; the levels of a concatenated row use the offset of its second half).  One workgroup per row, four columns per
 // thread and step (VEC: 16-byte source loads, set when lds, D and src allow).
 template <typename T, bool SPLIT, bool VEC>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restrict__ src, int64_t lds,
                                                           const int *__restrict__ rows, const int *__restrict__ ids,
                                                           int per_item, int src_rows, int D, T *__restrict__ out,
-                                                          int64_t ldo) {
+                                                          int64_t ldo, int64_t lo_off) {
     const int r = blockIdx.x;
     int64_t srow;
     if (rows) {
@@ -83,16 +84,16 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const float *__restric
         for (int i = 0; i < 4 && c + i < D; ++i) {
             const T h = from_f32<T>(v[i]);
             o[c + i] = h;
-            if constexpr (SPLIT) o[D + c + i] = from_f32<T>(v[i] - to_f32(h));
+            if constexpr (SPLIT) o[lo_off + c + i] = from_f32<T>(v[i] - to_f32(h));
         }
     }
 }
 
-// Z row rows[r] = vec, one workgroup per row
-__global__ __launch_bounds__(256) void fill_rows_kernel(const float *__restrict__ vec, const int *__restrict__ rows,
-                                                        int D, float *__restrict__ Z) {
+// Z row rows[r] = vec (+ add), one workgroup per row
+__global__ __launch_bounds__(256) void fill_rows_kernel(const float *__restrict__ vec, const float *__restrict__ add,
+                                                        const int *__restrict__ rows, int D, float *__restrict__ Z) {
     float *z = Z + (int64_t)rows[blockIdx.x] * D;
-    for (int c = threadIdx.x; c < D; c += blockDim.x) z[c] = vec[c];
+    for (int c = threadIdx.x; c < D; c += blockDim.x) z[c] = add ? vec[c] + add[c] : vec[c];
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ x, int64_t n) {
@@ -102,23 +103,24 @@ __global__ __launch_bounds__(256) void zero_kernel(float *__restrict__ x, int64_
 
 template <typename T, bool SPLIT>
 hipError_t launch_gather_t2(const float *src, int64_t lds, const int *rows, const int *ids, int per_item,
-                            int src_rows, int R, int D, T *out, int64_t ldo, hipStream_t s) {
+                            int src_rows, int R, int D, T *out, int64_t ldo, int64_t lo_off, hipStream_t s) {
     const bool vec = D % 4 == 0 && lds % 4 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
     const unsigned threads = (unsigned)std::min<int64_t>(256, std::max<int64_t>(64, cdiv(D, 4) / 64 * 64));
     if (vec)
         hipLaunchKernelGGL((gather_rows_kernel<T, SPLIT, true>), dim3((unsigned)R), dim3(threads), 0, s, src, lds,
-                           rows, ids, per_item, src_rows, D, out, ldo);
+                           rows, ids, per_item, src_rows, D, out, ldo, lo_off);
     else
         hipLaunchKernelGGL((gather_rows_kernel<T, SPLIT, false>), dim3((unsigned)R), dim3(threads), 0, s, src, lds,
-                           rows, ids, per_item, src_rows, D, out, ldo);
+                           rows, ids, per_item, src_rows, D, out, ldo, lo_off);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_gather_t(const float *src, int64_t lds, const int *rows, const int *ids, int per_item,
-                           int src_rows, int R, int D, bool split, T *out, int64_t ldo, hipStream_t s) {
-    if (split) return launch_gather_t2<T, true>(src, lds, rows, ids, per_item, src_rows, R, D, out, ldo, s);
-    return launch_gather_t2<T, false>(src, lds, rows, ids, per_item, src_rows, R, D, out, ldo, s);
+                           int src_rows, int R, int D, bool split, T *out, int64_t ldo, int64_t lo_off,
+                           hipStream_t s) {
+    if (split) return launch_gather_t2<T, true>(src, lds, rows, ids, per_item, src_rows, R, D, out, ldo, lo_off, s);
+    return launch_gather_t2<T, false>(src, lds, rows, ids, per_item, src_rows, R, D, out, ldo, lo_off, s);
 }
 
 } // namespace
@@ -134,26 +136,28 @@ hipError_t launch_pred_order(const int *ctx_ids, int nc, const int *tgt_ids, int
 
 hipError_t launch_gather_rows(int out_dtype, const float *src, int64_t lds, const int *rows, const int *ids,
                               int per_item, int src_rows, int R, int D, bool split, void *out, int64_t ldo,
-                              hipStream_t s) {
+                              hipStream_t s, int64_t lo_off) {
     if (R == 0) return hipSuccess;
+    if (lo_off < 0) lo_off = D;
     switch (out_dtype) {
     case DT_F32:
         if (split) return hipErrorInvalidValue;
         return launch_gather_t<float>(src, lds, rows, ids, per_item, src_rows, R, D, false,
-                                      reinterpret_cast<float *>(out), ldo, s);
+                                      reinterpret_cast<float *>(out), ldo, lo_off, s);
     case DT_BF16:
         return launch_gather_t<bf16_t>(src, lds, rows, ids, per_item, src_rows, R, D, split,
-                                       reinterpret_cast<bf16_t *>(out), ldo, s);
+                                       reinterpret_cast<bf16_t *>(out), ldo, lo_off, s);
     case DT_F16:
         return launch_gather_t<f16_t>(src, lds, rows, ids, per_item, src_rows, R, D, split,
-                                      reinterpret_cast<f16_t *>(out), ldo, s);
+                                      reinterpret_cast<f16_t *>(out), ldo, lo_off, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fill_rows(const float *vec, const int *rows, int R, int D, float *Z, hipStream_t s) {
+hipError_t launch_fill_rows(const float *vec, const float *add, const int *rows, int R, int D, float *Z,
+                            hipStream_t s) {
     if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(fill_rows_kernel, dim3((unsigned)R), dim3(256), 0, s, vec, rows, D, Z);
+    hipLaunchKernelGGL(fill_rows_kernel, dim3((unsigned)R), dim3(256), 0, s, vec, add, rows, D, Z);
     return hipGetLastError();
 }
 

@@ -60,13 +60,15 @@ class Weights(ctypes.Structure):
 class PredHparams(ctypes.Structure):
     _fields_ = [(n, c_i32) for n in ("embed_dim", "enc_dim", "n_layer", "n_head", "ffn_dim", "n_mask_tokens")] + \
                [("ln_eps", c_f32), ("rope_theta", c_f32)] + \
-               [(n, c_i32) for n in ("rope_layout", "grid_t", "grid_h", "grid_w", "dtype")]
+               [(n, c_i32) for n in ("rope_layout", "grid_t", "grid_h", "grid_w", "dtype", "out_dim", "n_hier_in",
+                                     "embed_hidden", "modality_embed", "context_proj")]
 
 
 class PredWeights(ctypes.Structure):
     _fields_ = [("embed_w", c_vp), ("embed_b", c_vp), ("mask_tokens", c_vp),
                 ("blocks", ctypes.POINTER(BlockWeights)), ("norm_w", c_vp), ("norm_b", c_vp),
-                ("proj_w", c_vp), ("proj_b", c_vp)]
+                ("proj_w", c_vp), ("proj_b", c_vp), ("embed2_w", c_vp), ("embed2_b", c_vp),
+                ("mod_embed_img", c_vp), ("mod_embed_video", c_vp), ("proj_ctx_w", c_vp), ("proj_ctx_b", c_vp)]
 
 
 class HeadHparams(ctypes.Structure):
@@ -113,6 +115,8 @@ SIGNATURES = {
     "vitenc_predict_workspace_size": (c_i32, [c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_size)]),
     "vitenc_predict": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_size, c_vp,
                                c_vp]),
+    "vitenc_predict_all": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_i32, c_vp, c_i32, c_i32, c_vp, c_size, c_vp,
+                                   c_vp, c_vp]),
     "vitenc_head_create": (c_i32, [ctypes.POINTER(HeadHparams), ctypes.POINTER(HeadWeights), ctypes.POINTER(c_vp)]),
     "vitenc_head_destroy": (None, [c_vp]),
     "vitenc_head_workspace_size": (c_i32, [c_vp, c_i32, c_i32, ctypes.POINTER(c_size)]),
@@ -323,9 +327,12 @@ class Predictor:
         for i, b in enumerate(blocks):
             for n in BLOCK_FIELDS:
                 setattr(self._bw[i], n, _ptr(b.get(n)))
+        opt = lambda n: _ptr(tensors.get(n))
         self._w = PredWeights(_ptr(tensors["embed_w"]), _ptr(tensors["embed_b"]), _ptr(tensors["mask_tokens"]),
                               ctypes.cast(self._bw, ctypes.POINTER(BlockWeights)), _ptr(tensors["norm_w"]),
-                              _ptr(tensors["norm_b"]), _ptr(tensors["proj_w"]), _ptr(tensors["proj_b"]))
+                              _ptr(tensors["norm_b"]), _ptr(tensors["proj_w"]), _ptr(tensors["proj_b"]),
+                              opt("embed2_w"), opt("embed2_b"), opt("mod_embed_img"), opt("mod_embed_video"),
+                              opt("proj_ctx_w"), opt("proj_ctx_b"))
         h = c_vp()
         check(L.vitenc_predictor_create(ctypes.byref(self._hp), ctypes.byref(self._w), ctypes.byref(h)))
         self.handle = h
@@ -345,6 +352,15 @@ class Predictor:
              "mask_tokens": f32_to_device(w.mask_tokens, device), "norm_w": f32_to_device(w.norm_w, device),
              "norm_b": f32_to_device(w.norm_b, device), "proj_w": to_device(w.store["proj_w"], dt, device),
              "proj_b": f32_to_device(w.proj_b, device)}
+        if w.embed2_w is not None:
+            t["embed2_w"] = to_device(w.store["embed2_w"], dt, device)
+            t["embed2_b"] = f32_to_device(w.embed2_b, device)
+        if w.mod_img is not None:
+            t["mod_embed_img"] = f32_to_device(w.mod_img, device)
+            t["mod_embed_video"] = f32_to_device(w.mod_video, device)
+        if w.proj_ctx_w is not None:
+            t["proj_ctx_w"] = to_device(w.store["proj_ctx_w"], dt, device)
+            t["proj_ctx_b"] = f32_to_device(w.proj_ctx_b, device)
         blocks = []
         for b in w.blocks:
             d = {n: to_device(b.store[n], dt, device) for n in QUANT_MATRICES}
@@ -369,28 +385,39 @@ class Predictor:
         check(lib().vitenc_predict_workspace_size(self.handle, B, n_ctx, n_tgt, ctypes.byref(n)))
         return n.value
 
+    def out_width(self) -> int:
+        return self.hp.get("out_dim") or self.hp["enc_dim"]
+
     def alloc(self, B, n_ctx, n_tgt, device="cuda"):
         import torch
         ws = torch.empty(self.workspace_bytes(B, n_ctx, n_tgt), dtype=torch.uint8, device=device)
-        out = torch.empty((B, n_tgt, self.hp["enc_dim"]), dtype=torch.float32, device=device)
+        out = torch.empty((B, n_tgt, self.out_width()), dtype=torch.float32, device=device)
         return ws, out
 
-    def predict_into(self, enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index=1, stream=None, check_ids=True):
-        """enc_tokens fp32 [B, n_enc, enc_dim], ctx_ids / tgt_ids int32 [B, n]
-        on the device.  check_ids copies the ids to the host (a
-        synchronisation) to check their contract before the call."""
-        B, n_enc, _ = enc_tokens.shape
+    def predict_into(self, enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index=1, stream=None, check_ids=True,
+                     out_ctx=None):
+        """enc_tokens fp32 [B, n_enc, enc_dim] ([n_hier_in, B, n_enc, enc_dim]),
+        ctx_ids / tgt_ids int32 [B, n] on the device.  check_ids copies the ids
+        to the host (a synchronisation) to check their contract before the
+        call.  out_ctx: None, or fp32 [B, n_ctx, out_dim] for the projected
+        context rows."""
+        B, n_enc = enc_tokens.shape[-3], enc_tokens.shape[-2]
         if check_ids:
             check_pred_ids(ctx_ids, tgt_ids, n_enc)
-        check(lib().vitenc_predict(self.handle, enc_tokens.data_ptr(), B, n_enc, ctx_ids.data_ptr(),
-                                   ctx_ids.shape[1], tgt_ids.data_ptr(), tgt_ids.shape[1], mask_index,
-                                   ws.data_ptr(), ws.numel(), out.data_ptr(), _stream(stream)))
+        check(lib().vitenc_predict_all(self.handle, enc_tokens.data_ptr(), B, n_enc, ctx_ids.data_ptr(),
+                                       ctx_ids.shape[1], tgt_ids.data_ptr(), tgt_ids.shape[1], mask_index,
+                                       ws.data_ptr(), ws.numel(), out.data_ptr(), _ptr(out_ctx), _stream(stream)))
 
-    def predict(self, enc_tokens, ctx_ids, tgt_ids, mask_index=1, stream=None):
-        B = enc_tokens.shape[0]
+    def predict(self, enc_tokens, ctx_ids, tgt_ids, mask_index=1, stream=None, return_context=False):
+        import torch
+        B = enc_tokens.shape[-3]
         ws, out = self.alloc(B, ctx_ids.shape[1], tgt_ids.shape[1], device=enc_tokens.device)
-        self.predict_into(enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index, stream)
-        return out
+        out_ctx = None
+        if return_context:
+            out_ctx = torch.empty((B, ctx_ids.shape[1], self.out_width()), dtype=torch.float32,
+                                  device=enc_tokens.device)
+        self.predict_into(enc_tokens, ctx_ids, tgt_ids, ws, out, mask_index, stream, out_ctx=out_ctx)
+        return (out, out_ctx) if return_context else out
 
 
 class Head:

@@ -425,6 +425,14 @@ class PredictorConfig:
     std_w: float = 0.02
     std_tok: float = 0.02
     seed: int = 2000
+    # V-JEPA 2.1 options: output width (0: enc_dim), hierarchical encoder
+    # levels concatenated into a 2-layer embed MLP of embed_hidden units,
+    # modality vectors, and the projection of the context rows
+    out_dim: int = 0
+    n_hier_in: int = 1
+    embed_hidden: int = 0
+    modality_embed: int = 0
+    context_proj: int = 0
 
     @property
     def head_dim(self) -> int:
@@ -447,18 +455,40 @@ class PredictorConfig:
         return dict(embed_dim=self.embed_dim, enc_dim=self.enc_dim, n_layer=self.n_layer, n_head=self.n_head,
                     ffn_dim=self.ffn_dim, n_mask_tokens=self.n_mask_tokens, ln_eps=self.ln_eps,
                     rope_theta=self.rope_theta, rope_layout=self.rope_layout, grid=tuple(self.grid),
-                    dtype=self.dtype)
+                    dtype=self.dtype, out_dim=self.out_width, n_hier_in=self.n_hier_in,
+                    embed_hidden=self.embed_hidden, modality_embed=self.modality_embed,
+                    context_proj=self.context_proj)
+
+    @property
+    def out_width(self) -> int:
+        return self.out_dim or self.enc_dim
 
     def flops(self) -> float:
         M, D, F, De = self.batch * self.n_tokens, self.embed_dim, self.ffn_dim, self.enc_dim
         per_layer = 2.0 * M * D * (3 * D + D + 2 * F) + 4.0 * D * self.batch * self.n_tokens ** 2
-        return (2.0 * self.batch * self.n_ctx * De * D + self.n_layer * per_layer
-                + 2.0 * self.batch * self.n_tgt * D * De)
+        if self.n_hier_in > 1:
+            embed = 2.0 * self.batch * self.n_ctx * (self.n_hier_in * De * self.embed_hidden + self.embed_hidden * D)
+        else:
+            embed = 2.0 * self.batch * self.n_ctx * De * D
+        proj = 2.0 * self.batch * (self.n_tgt + (self.n_ctx if self.context_proj else 0)) * D * self.out_width
+        return embed + self.n_layer * per_layer + proj
 
 
 # V-JEPA 2 ViT-L predictor shape: 12 blocks of width 384, 12 heads of 32, on the
 # 8 x 16 x 16 token grid of a 16-frame 256-px clip, half the tokens as context
 PREDICTOR = PredictorConfig("vjepa2_predictor")
+# V-JEPA 2.1 predictor shapes (8 mask tokens, interleaved RoPE, modality
+# vectors, the projection of the context rows, out_dim the teacher's width):
+# after a ViT-L encoder (one hierarchical level) and after a ViT-g encoder
+# (four levels of width 1408 concatenated into a 2-layer embed MLP), on the
+# 8 x 16 x 16 grid of a 16-frame 256-px clip and the 8 x 24 x 24 grid of a
+# 16-frame 384-px clip
+PREDICTOR_21_L = PredictorConfig("vjepa21_predictor_vit_l", n_mask_tokens=8, rope_layout=LAYOUT_INTERLEAVED,
+                                 out_dim=1664, modality_embed=1, context_proj=1, mask_index=0, seed=2100)
+PREDICTOR_21_G = PredictorConfig("vjepa21_predictor_vit_g", enc_dim=1408, n_mask_tokens=8,
+                                 rope_layout=LAYOUT_INTERLEAVED, out_dim=1664, n_hier_in=4, embed_hidden=1536,
+                                 modality_embed=1, context_proj=1, mask_index=0, grid=(8, 24, 24), n_ctx=1152,
+                                 n_tgt=1152, batch=1, seed=2101)
 
 
 @dataclass
@@ -469,15 +499,23 @@ class PredictorWeights:
     blocks: List[Block]
     norm_w: np.ndarray
     norm_b: np.ndarray
-    proj_w: np.ndarray           # [enc_dim, embed_dim]
+    proj_w: np.ndarray           # [out_dim, embed_dim]
     proj_b: np.ndarray
     store: Dict[str, np.ndarray] = field(default_factory=dict)
+    # V-JEPA 2.1 options (None when off); with n_hier_in > 1, embed_w / embed_b
+    # are the first MLP layer [embed_hidden, n_hier_in * enc_dim]
+    embed2_w: Optional[np.ndarray] = None   # [embed_dim, embed_hidden]
+    embed2_b: Optional[np.ndarray] = None
+    mod_img: Optional[np.ndarray] = None    # [embed_dim]
+    mod_video: Optional[np.ndarray] = None
+    proj_ctx_w: Optional[np.ndarray] = None  # [out_dim, embed_dim]
+    proj_ctx_b: Optional[np.ndarray] = None
 
 
 @dataclass
 class PredictorWorkload:
     cfg: PredictorConfig
-    enc_tokens: np.ndarray       # fp32 [B, n_grid, enc_dim], unit-scale encoder features
+    enc_tokens: np.ndarray       # fp32 [B, n_grid, enc_dim] ([n_hier_in, B, n_grid, enc_dim]), unit scale
     ctx_ids: np.ndarray          # int32 [B, n_ctx], strictly increasing
     tgt_ids: np.ndarray          # int32 [B, n_tgt], strictly increasing, disjoint from ctx_ids
     weights: PredictorWeights
@@ -486,7 +524,11 @@ class PredictorWorkload:
 def make_predictor_workload(cfg: PredictorConfig, seed: Optional[int] = None) -> PredictorWorkload:
     """Draw order: encoder features, per item a permutation of the grid (the
     first n_ctx ids are the context, the next n_tgt the targets), embed
-    weight and bias, mask tokens, the blocks (as the encoder's), proj."""
+    weight and bias, mask tokens, the blocks (as the encoder's), proj; then,
+    for the V-JEPA 2.1 options that are on, the further hierarchical levels of
+    the encoder features, the second embed layer, the image and video
+    modality vectors and the context projection (so that configurations
+    without them draw exactly what they did before the options existed)."""
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     B, Ng, De, D, F = cfg.batch, cfg.n_grid, cfg.enc_dim, cfg.embed_dim, cfg.ffn_dim
     assert cfg.n_ctx + cfg.n_tgt <= Ng
@@ -500,8 +542,9 @@ def make_predictor_workload(cfg: PredictorConfig, seed: Optional[int] = None) ->
     ctx_ids = np.stack(ctx).astype(np.int32).reshape(B, cfg.n_ctx)
     tgt_ids = np.stack(tgt).astype(np.int32).reshape(B, cfg.n_tgt)
     st = {}
-    st["embed_w"], embed_w = quantise(_normal(rng, (D, De), cfg.std_w), dt)
-    embed_b = _normal(rng, (D,), cfg.std_w)
+    Hd = cfg.embed_hidden if cfg.n_hier_in > 1 else D
+    st["embed_w"], embed_w = quantise(_normal(rng, (Hd, cfg.n_hier_in * De), cfg.std_w), dt)
+    embed_b = _normal(rng, (Hd,), cfg.std_w)
     mask_tokens = _normal(rng, (cfg.n_mask_tokens, D), cfg.std_tok)
     ones = np.ones(D, np.float32)
     zeros = np.zeros(D, np.float32)
@@ -518,9 +561,21 @@ def make_predictor_workload(cfg: PredictorConfig, seed: Optional[int] = None) ->
         down_b = _normal(rng, (D,), cfg.std_w)
         blocks.append(Block(qkv_w, qkv_b, out_w, out_b, up_w, up_b, down_w, down_b,
                             ones, zeros, ones, zeros, None, None, bs))
-    st["proj_w"], proj_w = quantise(_normal(rng, (De, D), cfg.std_w), dt)
-    proj_b = _normal(rng, (De,), cfg.std_w)
+    Do = cfg.out_width
+    st["proj_w"], proj_w = quantise(_normal(rng, (Do, D), cfg.std_w), dt)
+    proj_b = _normal(rng, (Do,), cfg.std_w)
     w = PredictorWeights(embed_w, embed_b, mask_tokens, blocks, ones, zeros, proj_w, proj_b, st)
+    if cfg.n_hier_in > 1:
+        more = rng.standard_normal((cfg.n_hier_in - 1, B, Ng, De), dtype=np.float32)
+        enc = np.concatenate([enc[None], more], axis=0)
+        st["embed2_w"], w.embed2_w = quantise(_normal(rng, (D, Hd), cfg.std_w), dt)
+        w.embed2_b = _normal(rng, (D,), cfg.std_w)
+    if cfg.modality_embed:
+        w.mod_img = _normal(rng, (D,), cfg.std_tok)
+        w.mod_video = _normal(rng, (D,), cfg.std_tok)
+    if cfg.context_proj:
+        st["proj_ctx_w"], w.proj_ctx_w = quantise(_normal(rng, (Do, D), cfg.std_w), dt)
+        w.proj_ctx_b = _normal(rng, (Do,), cfg.std_w)
     return PredictorWorkload(cfg, enc, ctx_ids, tgt_ids, w)
 
 
