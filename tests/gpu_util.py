@@ -6,10 +6,15 @@ import numpy as np
 import oracle
 from vision_transformer_amd import workloads as W
 
-# gates: fp32 path max relative error; bf16/f16 path per-token cosine and max abs
+# gates: fp32 path max relative error; bf16/f16 path per-token cosine and max
+# abs.  The max-abs gate of a forward deeper than 24 layers is wider: the bf16
+# recipe by itself (its roundings applied to the float64 oracle, no kernel
+# involved) already reaches 0.020 on a 128-token ViT-g clip at 40 layers
+# (pinned in test_bf16_recipe.py), so 2e-2 would leave the kernels nothing.
 REL_F32 = 1e-4
 COS_BF16 = 0.9999
 ABS_BF16 = 2e-2
+ABS_BF16_DEEP = 3e-2
 
 
 def say(*a):
@@ -29,7 +34,11 @@ def gates_ok(cfg, stats):
         return False
     if cfg.dtype == W.DTYPE_F32:
         return stats["rel"] <= REL_F32
-    return stats["min_cos"] >= COS_BF16 and stats["maxabs"] <= ABS_BF16
+    return stats["min_cos"] >= COS_BF16 and stats["maxabs"] <= abs_gate(cfg.n_layer)
+
+
+def abs_gate(n_layer):
+    return ABS_BF16 if n_layer <= 24 else ABS_BF16_DEEP
 
 
 def run_gpu(wl, device="cuda"):

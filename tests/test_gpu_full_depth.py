@@ -4,7 +4,8 @@ by tests/golden/make_oracle_samples.py, which calls only the oracle).  Every
 token is encoded; the stored sampled token rows (prefix, frame boundaries,
 last row and seeded random rows) and the pooled features are compared at the
 gates: fp32 max relative error <= 1e-4; bf16 per-token cosine >= 0.9999 and
-max abs error <= 2e-2."""
+max abs error <= 2e-2 (3e-2 for the 40-layer ViT-g clip, whose bf16 recipe
+alone comes close to 2e-2; see gpu_util.abs_gate)."""
 import os
 
 import numpy as np

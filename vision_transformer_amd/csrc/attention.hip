@@ -813,9 +813,9 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float *__restric
     const float f1 = h1 ? __builtin_amdgcn_exp2f(ml1.x - M) : 0.0f;
     const float L = (h0 ? ml0.y * f0 : 0.0f) + (h1 ? ml1.y * f1 : 0.0f);
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    const float4 z4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    const float4 a = h0 ? *reinterpret_cast<const float4 *>(p0 + d) : z4;
-    const float4 c = h1 ? *reinterpret_cast<const float4 *>(p1 + d) : z4;
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f), c = a;
+    if (h0) a = *reinterpret_cast<const float4 *>(p0 + d);
+    if (h1) c = *reinterpret_cast<const float4 *>(p1 + d);
     const int b = bh / H, head = bh - b * H;
     T *dst = O + ((int64_t)b * N + q) * H * HD + head * HD + d;
     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(fmaf(a.x, f0, c.x * f1) * inv, fmaf(a.y, f0, c.y * f1) * inv),
