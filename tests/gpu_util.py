@@ -34,7 +34,7 @@ def gates_ok(cfg, stats):
         return False
     if cfg.dtype == W.DTYPE_F32:
         return stats["rel"] <= REL_F32
-    return stats["min_cos"] >= COS_BF16 and stats["maxabs"] <= abs_gate(cfg.n_layer)
+    return stats["min_cos"] >= COS_BF16 and stats["maxabs"] <= abs_gate(getattr(cfg, "n_layer", 0))
 
 
 def abs_gate(n_layer):

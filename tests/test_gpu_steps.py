@@ -210,11 +210,13 @@ def test_pool(gpu_lib, cls, p):
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
-@pytest.mark.parametrize("M,N,K", [(4133, 4096, 256), (4000, 3072, 256)])
+@pytest.mark.parametrize("M,N,K", [(4133, 4096, 256), (4000, 3072, 256), (1990, 2048, 384), (2048, 2040, 320)])
 def test_linear_wide_tiles(gpu_lib, dtype, M, N, K):
     """Shapes with enough tiles for the 256 x 256 direct-to-LDS kernel, with a
-    ragged last row block (M = 4133), and for 1.5 rounds of its 128 x 128
-    tiles (width 3072, the last row block ragged)."""
+    ragged last row block (M = 4133); for 1.5 rounds of its 128 x 128 tiles
+    (width 3072, the last row block ragged); and for one 128 x 128 tile per
+    CU with its deeper slab ring, with ragged rows (M = 1990) or ragged
+    columns (N = 2040)."""
     from vision_transformer_amd import vitenc as V
     say(f"linear wide dtype={dtype} M={M} N={N} K={K}")
     rng = np.random.default_rng(11)

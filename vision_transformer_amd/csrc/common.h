@@ -209,18 +209,20 @@ __device__ __forceinline__ float wave_max(float v) {
 // rational approximation 7.1.26 of Abramowitz & Stegun (Handbook of
 // Mathematical Functions): erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
 // e^{-z^2}, t = 1 / (1 + p z), z >= 0, |error| <= 1.5e-7.  With z = |x| / sqrt 2
-// and q = (x / 2) erfc(z): GELU(x) = x - q for x >= 0 and q for x < 0 (the
-// factor 1/2 is folded into the coefficients).
+// and u = erfc(z) / 2 (the factor 1/2 folded into the coefficients),
+// Phi(x) = 1 - u for x >= 0 and u for x < 0, so GELU(x) = max(x, 0) - |x| u
+// in both cases: one FMA instead of a compare, a select and a subtraction.
 __device__ __forceinline__ float gelu_erf(float x) {
-    const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(x), 0.3275911f * 0.70710678118654752440f, 1.0f));
+    const float ax = fabsf(x);
+    const float t = __builtin_amdgcn_rcpf(fmaf(ax, 0.3275911f * 0.70710678118654752440f, 1.0f));
     float h = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
     h = fmaf(h, t, 0.5f * 1.421413741f);
     h = fmaf(h, t, 0.5f * -0.284496736f);
     h = fmaf(h, t, 0.5f * 0.254829592f);
     // e^{-x^2 / 2} = 2^{-x^2 log2(e) / 2}
     const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170368f) * x);
-    const float q = (x * t) * h * e;
-    return x >= 0.0f ? x - q : q;
+    const float u = (t * h) * e;
+    return fmaf(-ax, u, fmaxf(x, 0.0f));
 }
 
 __host__ __device__ __forceinline__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
