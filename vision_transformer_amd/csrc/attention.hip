@@ -366,6 +366,134 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, Chunk *dst
 }
 __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Prefix (CLS) query rows.  They see every key in both masks (the CLS row is
+// open), and a tile of 32*NWV queries holding a single prefix query would
+// cost as much as a full tile, so the tiled kernels start at the first patch
+// query and the prefix rows are computed here, split over the keys: one
+// workgroup per (prefix row, head, run of kPrefixKeys keys) stores the
+// fp32 scores of its keys (16-byte K row loads) in LDS, turns them into
+// weights against the run's own max, and multiplies them into V (each thread
+// one output dim of one key group, 16-byte runs of V^T); the partial
+// (max, sum, o[HD]) goes to scratch, and a merge kernel combines the runs of
+// a row in order (online-softmax rescaling).  In 16-bit calls these
+// workgroups are the last ones of the tiled kernel's own grid (short jobs
+// that fill the CUs the heavy tiles leave idle at the end), not a launch of
+// their own.
+constexpr int kPrefixThreads = 256;
+constexpr int kPrefixKeys = 256;
+
+// QR query rows of one (item, head) per workgroup (the rows of a row-split
+// call share their K and V^T reads; a prefix call has QR = 1): thread k of the
+// run scores key k against each row, the weights go through LDS, and thread
+// (group, d) accumulates output dim d over its key group for each row.
+// Rows pq0 .. pq0 + nq - 1 of (item, head) bh, keys of run `run` of `runs`;
+// smem: prefix_smem_floats<HD, QR>() floats of LDS.  Every thread of the
+// workgroup (kPrefixThreads) calls it.
+template <int HD, int QR> constexpr int prefix_smem_floats() {
+    return QR * kPrefixKeys + QR * HD + 2 * QR * (kPrefixThreads / 64) + QR * (kPrefixThreads / HD) * HD;
+}
+template <typename T, int HD, int QR>
+__device__ __forceinline__ void prefix_run(const T *__restrict__ Q, const T *__restrict__ K,
+                                           const T *__restrict__ Vt, int N, int ldv, int p, float scale_log2,
+                                           float *__restrict__ part, int bh, int pq0, int nq, int run, int runs,
+                                           float *smem) {
+    constexpr int KPC = Elem<T>::kPerChunk;
+    constexpr int NW = kPrefixThreads / 64;
+    constexpr int G = kPrefixThreads / HD;   // key groups of the PV step
+    constexpr int VE = 16 / (int)sizeof(T);  // keys per 16-byte V^T load
+    static_assert(kPrefixKeys <= kPrefixThreads, "one key per thread");
+    static_assert(QR * HD <= kPrefixThreads, "one query element per thread");
+    float(*ss)[kPrefixKeys] = reinterpret_cast<float(*)[kPrefixKeys]>(smem);
+    float(*sq)[HD] = reinterpret_cast<float(*)[HD]>(smem + QR * kPrefixKeys);
+    float(*red)[QR][NW] = reinterpret_cast<float(*)[QR][NW]>(smem + QR * kPrefixKeys + QR * HD);
+    float(*so)[G][HD] = reinterpret_cast<float(*)[G][HD]>(smem + QR * kPrefixKeys + QR * HD + 2 * QR * NW);
+    const int c0 = run * kPrefixKeys, n = min(kPrefixKeys, N - c0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int d = tid % HD, grp = tid / HD;
+    if (tid < QR * HD) {
+        const int q = tid / HD;
+        sq[q][d] = q < nq ? to_f32(Q[((int64_t)bh * N + pq0 + q) * HD + d]) * scale_log2 : 0.0f;
+    }
+    __syncthreads();
+    float sc[QR];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) sc[q] = -INFINITY;
+    if (tid < n) {
+#pragma unroll
+        for (int q = 0; q < QR; ++q) sc[q] = 0.0f;
+        const T *kr = K + ((int64_t)bh * N + c0 + tid) * HD;
+#pragma unroll
+        for (int c = 0; c < HD / KPC; ++c) {
+            const Chunk ch = load_chunk(kr + c * KPC);
+            const T *e = reinterpret_cast<const T *>(&ch);
+#pragma unroll
+            for (int u = 0; u < KPC; ++u) {
+                const float kv = to_f32(e[u]);
+#pragma unroll
+                for (int q = 0; q < QR; ++q) sc[q] = fmaf(sq[q][c * KPC + u], kv, sc[q]);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < QR; ++q) {
+        const float mw = wave_max(sc[q]);
+        if (lane == 0) red[0][q][wave] = mw;
+    }
+    __syncthreads();
+    float m[QR];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) {
+        m[q] = red[0][q][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m[q] = fmaxf(m[q], red[0][q][w]);
+        const float wgt = tid < n ? __builtin_amdgcn_exp2f(sc[q] - m[q]) : 0.0f;
+        ss[q][tid] = wgt;
+        const float lw = wave_sum(wgt);
+        if (lane == 0) red[1][q][wave] = lw;
+    }
+    __syncthreads();
+    const T *vrow = Vt + ((int64_t)bh * HD + d) * ldv + c0;
+    float acc[QR];
+#pragma unroll
+    for (int q = 0; q < QR; ++q) acc[q] = 0.0f;
+    const int full = n / VE * VE;
+    for (int k = grp * VE; k < full; k += G * VE) {
+        const Chunk ch = load_chunk(vrow + k);
+        const T *e = reinterpret_cast<const T *>(&ch);
+#pragma unroll
+        for (int u = 0; u < VE; ++u) {
+            const float vv = to_f32(e[u]);
+#pragma unroll
+            for (int q = 0; q < QR; ++q) acc[q] = fmaf(ss[q][k + u], vv, acc[q]);
+        }
+    }
+    for (int k = full + grp; k < n; k += G) {
+        const float vv = to_f32(vrow[k]);
+#pragma unroll
+        for (int q = 0; q < QR; ++q) acc[q] = fmaf(ss[q][k], vv, acc[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < QR; ++q) so[q][grp][d] = acc[q];
+    __syncthreads();
+    if (tid < QR * HD) {
+        const int q = tid / HD;
+        if (q < nq) {
+            float t = 0.0f;
+#pragma unroll
+            for (int g2 = 0; g2 < G; ++g2) t += so[q][g2][d];
+            float *out = part + (((int64_t)bh * p + pq0 + q) * runs + run) * (HD + 2);
+            out[2 + d] = t;
+            if (d == 0) {
+                float l = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) l += red[1][q][w];
+                out[0] = m[q];
+                out[1] = l;
+            }
+        }
+    }
+}
+
 // Order in which the workgroups of the direct-to-LDS kernel take the query
 // tiles, and which tiles are computed as two workgroups over halves of their
 // keys.  With the block-causal mask a late frame's query tile sees up to
@@ -374,7 +502,7 @@ __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 
 // When the largest key count is at least twice the smallest, a tile is split
 // in two when its key tiles exceed a third of the largest count: each half
 // writes its unnormalised partial (o, running max, running sum) to scratch and
-// split_merge_kernel combines the two.  Jobs run largest first.  n = 0: no
+// merge_kernel combines the two.  Jobs run largest first.  n = 0: no
 // split, tiles in reverse order (the heaviest last tiles first), one
 // workgroup each.
 constexpr int kMaxJobs = 480;
@@ -392,7 +520,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
                                                                     const T *__restrict__ Vt, int N, int H, int ldv,
                                                                     int causal, int p, int S, int q_begin,
                                                                     float scale_log2, const TileOrder order,
-                                                                    float *__restrict__ part, T *__restrict__ O) {
+                                                                    float *__restrict__ part, int pre_y0,
+                                                                    float *__restrict__ pre_part, T *__restrict__ O) {
     static_assert(sizeof(T) == 2, "16-bit types");
     constexpr int KPC = 8;
     constexpr int QCH = HD / KPC;              // chunks per K row (8 or 4)
@@ -411,12 +540,22 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     __shared__ Chunk sK[STAGES][BKV][QCH];
     __shared__ Chunk sV[STAGES][HD][VCH];
 
+    if ((int)blockIdx.y >= pre_y0) {
+        // a run of keys of one prefix row (rows q_begin of every (item, head))
+        static_assert(kThreadsL == kPrefixThreads && prefix_smem_floats<HD, 1>() * 4 <= (int)sizeof(sK), "prefix job");
+        const int runs = (int)cdiv(N, kPrefixKeys), y = (int)blockIdx.y - pre_y0;
+        const int pq = y / runs;
+        prefix_run<T, HD, 1>(Q, K, Vt, N, ldv, q_begin, scale_log2, pre_part, (int)blockIdx.x, pq, 1, y - pq * runs,
+                             runs, reinterpret_cast<float *>(&sK[0][0][0]));
+        return;
+    }
+
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int bh = blockIdx.x;
     const int b = bh / H, head = bh - b * H;
-    int qt = gridDim.y - 1 - blockIdx.y, piece = 0; // heavy (late-frame) tiles first
+    int qt = pre_y0 - 1 - blockIdx.y, piece = 0; // heavy (late-frame) tiles first
     if (order.n > 0) {
         const int j = order.job[blockIdx.y];
         qt = j & 0x3FFF;
@@ -614,126 +753,18 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     }
 }
 
-// Prefix (CLS) query rows.  They see every key in both masks (the CLS row is
-// open), and a tile of 32*NWV queries holding a single prefix query would
-// cost as much as a full tile, so the tiled kernels start at the first patch
-// query and the prefix rows are computed here, split over the keys: one
-// workgroup per (prefix row, head, run of kPrefixKeys keys) stores the
-// fp32 scores of its keys (16-byte K row loads) in LDS, turns them into
-// weights against the run's own max, and multiplies them into V (each thread
-// one output dim of one key group, 16-byte runs of V^T); the partial
-// (max, sum, o[HD]) goes to scratch, and a second kernel merges the runs of a
-// row in order (online-softmax rescaling).
-constexpr int kPrefixThreads = 256;
-constexpr int kPrefixKeys = 256;
-
-// QR query rows of one (item, head) per workgroup (the rows of a row-split
-// call share their K and V^T reads; a prefix call has QR = 1): thread k of the
-// run scores key k against each row, the weights go through LDS, and thread
-// (group, d) accumulates output dim d over its key group for each row.
+// The fp32 and row-split calls run the prefix rows as a kernel of their own:
+// grid (row groups of every (item, head), runs).
 template <typename T, int HD, int QR>
 __global__ __launch_bounds__(kPrefixThreads) void prefix_partial_kernel(const T *__restrict__ Q,
                                                                         const T *__restrict__ K,
                                                                         const T *__restrict__ Vt, int N, int ldv,
                                                                         int p, float scale_log2,
                                                                         float *__restrict__ part) {
-    constexpr int KPC = Elem<T>::kPerChunk;
-    constexpr int NW = kPrefixThreads / 64;
-    constexpr int G = kPrefixThreads / HD;   // key groups of the PV step
-    constexpr int VE = 16 / (int)sizeof(T);  // keys per 16-byte V^T load
-    static_assert(kPrefixKeys <= kPrefixThreads, "one key per thread");
-    static_assert(QR * HD <= kPrefixThreads, "one query element per thread");
-    __shared__ float ss[QR][kPrefixKeys];
-    __shared__ float sq[QR][HD];
-    __shared__ float red[2][QR][NW];
-    __shared__ float so[QR][G][HD];
+    __shared__ float smem[prefix_smem_floats<HD, QR>()];
     const int gpb = (p + QR - 1) / QR;       // row groups per (item, head)
     const int bh = blockIdx.x / gpb, pq0 = (blockIdx.x - bh * gpb) * QR, nq = min(QR, p - pq0);
-    const int run = blockIdx.y, c0 = run * kPrefixKeys, n = min(kPrefixKeys, N - c0);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int d = tid % HD, grp = tid / HD;
-    if (tid < QR * HD) {
-        const int q = tid / HD;
-        sq[q][d] = q < nq ? to_f32(Q[((int64_t)bh * N + pq0 + q) * HD + d]) * scale_log2 : 0.0f;
-    }
-    __syncthreads();
-    float sc[QR];
-#pragma unroll
-    for (int q = 0; q < QR; ++q) sc[q] = -INFINITY;
-    if (tid < n) {
-#pragma unroll
-        for (int q = 0; q < QR; ++q) sc[q] = 0.0f;
-        const T *kr = K + ((int64_t)bh * N + c0 + tid) * HD;
-#pragma unroll
-        for (int c = 0; c < HD / KPC; ++c) {
-            const Chunk ch = load_chunk(kr + c * KPC);
-            const T *e = reinterpret_cast<const T *>(&ch);
-#pragma unroll
-            for (int u = 0; u < KPC; ++u) {
-                const float kv = to_f32(e[u]);
-#pragma unroll
-                for (int q = 0; q < QR; ++q) sc[q] = fmaf(sq[q][c * KPC + u], kv, sc[q]);
-            }
-        }
-    }
-#pragma unroll
-    for (int q = 0; q < QR; ++q) {
-        const float mw = wave_max(sc[q]);
-        if (lane == 0) red[0][q][wave] = mw;
-    }
-    __syncthreads();
-    float m[QR];
-#pragma unroll
-    for (int q = 0; q < QR; ++q) {
-        m[q] = red[0][q][0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) m[q] = fmaxf(m[q], red[0][q][w]);
-        const float wgt = tid < n ? __builtin_amdgcn_exp2f(sc[q] - m[q]) : 0.0f;
-        ss[q][tid] = wgt;
-        const float lw = wave_sum(wgt);
-        if (lane == 0) red[1][q][wave] = lw;
-    }
-    __syncthreads();
-    const T *vrow = Vt + ((int64_t)bh * HD + d) * ldv + c0;
-    float acc[QR];
-#pragma unroll
-    for (int q = 0; q < QR; ++q) acc[q] = 0.0f;
-    const int full = n / VE * VE;
-    for (int k = grp * VE; k < full; k += G * VE) {
-        const Chunk ch = load_chunk(vrow + k);
-        const T *e = reinterpret_cast<const T *>(&ch);
-#pragma unroll
-        for (int u = 0; u < VE; ++u) {
-            const float vv = to_f32(e[u]);
-#pragma unroll
-            for (int q = 0; q < QR; ++q) acc[q] = fmaf(ss[q][k + u], vv, acc[q]);
-        }
-    }
-    for (int k = full + grp; k < n; k += G) {
-        const float vv = to_f32(vrow[k]);
-#pragma unroll
-        for (int q = 0; q < QR; ++q) acc[q] = fmaf(ss[q][k], vv, acc[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < QR; ++q) so[q][grp][d] = acc[q];
-    __syncthreads();
-    if (tid < QR * HD) {
-        const int q = tid / HD;
-        if (q < nq) {
-            float t = 0.0f;
-#pragma unroll
-            for (int g2 = 0; g2 < G; ++g2) t += so[q][g2][d];
-            float *out = part + (((int64_t)bh * p + pq0 + q) * gridDim.y + run) * (HD + 2);
-            out[2 + d] = t;
-            if (d == 0) {
-                float l = 0.0f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) l += red[1][q][w];
-                out[0] = m[q];
-                out[1] = l;
-            }
-        }
-    }
+    prefix_run<T, HD, QR>(Q, K, Vt, N, ldv, p, scale_log2, part, bh, pq0, nq, blockIdx.y, gridDim.y, smem);
 }
 
 // Merge of the runs of one row: 256 threads, a group of HD threads per share
@@ -743,14 +774,14 @@ __global__ __launch_bounds__(kPrefixThreads) void prefix_partial_kernel(const T 
 constexpr int kMergeThreads = 256;
 
 template <typename T, int HD>
-__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(const float *__restrict__ part, int runs, int N,
-                                                                      int H, int p, T *__restrict__ O) {
+__device__ __forceinline__ void prefix_merge_row(const float *__restrict__ part, int runs, int N, int H, int p,
+                                                 int row, T *__restrict__ O) {
     constexpr int RG = kMergeThreads / HD;  // run groups
     constexpr int NW = kMergeThreads / 64;
     __shared__ float sacc[RG][HD];
     __shared__ float sl[RG];
     __shared__ float smax[NW];
-    const int row = blockIdx.x, bh = row / p, pq = row - bh * p;
+    const int bh = row / p, pq = row - bh * p;
     const int b = bh / H, head = bh - b * H;
     const float *pr = part + (int64_t)row * runs * (HD + 2);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -785,16 +816,21 @@ __global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(const float
     }
 }
 
+template <typename T, int HD>
+__global__ __launch_bounds__(kMergeThreads) void prefix_merge_kernel(const float *__restrict__ part, int runs, int N,
+                                                                      int H, int p, T *__restrict__ O) {
+    prefix_merge_row<T, HD>(part, runs, N, H, p, (int)blockIdx.x, O);
+}
+
 // Combines the two halves of a split query tile (TileOrder): with the running
 // maxima m0, m1 (log2 units) and M = max(m0, m1), o = (o0 2^(m0-M) + o1
 // 2^(m1-M)) / (l0 2^(m0-M) + l1 2^(m1-M)).  One thread per 4 output dims of
 // a row.
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void split_merge_kernel(const float *__restrict__ part, int64_t n, int N, int H,
-                                                          int q_begin, int qs, int nslots, int bq,
-                                                          T *__restrict__ O) {
+__device__ __forceinline__ void split_merge_quad(const float *__restrict__ part, int64_t idx, int64_t n, int N,
+                                                 int H, int q_begin, int qs, int nslots, int bq,
+                                                 T *__restrict__ O) {
     constexpr int G = HD / 4, PS = HD + 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n) return;
     const int64_t row = idx / G;
     const int d = (int)(idx - row * G) * 4;
@@ -820,6 +856,21 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const float *__restric
     T *dst = O + ((int64_t)b * N + q) * H * HD + head * HD + d;
     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack2<T>(fmaf(a.x, f0, c.x * f1) * inv, fmaf(a.y, f0, c.y * f1) * inv),
                                                  pack2<T>(fmaf(a.z, f0, c.z * f1) * inv, fmaf(a.w, f0, c.w * f1) * inv));
+}
+
+// Both merges of a 16-bit call in one launch of kMergeThreads-thread
+// workgroups: the first sblocks combine the split halves (one thread per 4
+// output dims of a row), the rest merge one prefix row each.
+template <typename T, int HD>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ part, int64_t n, int sblocks,
+                                                              int N, int H, int q_begin, int qs, int nslots, int bq,
+                                                              const float *__restrict__ pre_part, int runs,
+                                                              T *__restrict__ O) {
+    if ((int)blockIdx.x < sblocks)
+        split_merge_quad<T, HD>(part, (int64_t)blockIdx.x * kMergeThreads + threadIdx.x, n, N, H, q_begin, qs,
+                                nslots, bq, O);
+    else
+        prefix_merge_row<T, HD>(pre_part, runs, N, H, q_begin, (int)blockIdx.x - sblocks, O);
 }
 
 // the first query row the tiled kernels cover: the prefix rows go to
@@ -932,21 +983,25 @@ hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, 
     TileOrder ord;
     plan_tile_order(B, N, H, causal, p, S, BQL, ord);
     float *part = nullptr;
-    if (ord.n > 0) {
+    if (ord.n > 0 || qb > 0) {
         if (!scratch) return hipErrorInvalidValue;
         part = scratch + cdiv(prefix_scratch_floats(B, N, H, HD, qb), 4) * 4;
     }
-    dim3 grid((unsigned)(B * H), (unsigned)(ord.n > 0 ? ord.n : ntq));
+    // grid y: the query-tile jobs, then (prefix rows x runs of keys) prefix jobs
+    const int jobs = ord.n > 0 ? ord.n : ntq, runs = (int)cdiv(N, kPrefixKeys);
+    dim3 grid((unsigned)(B * H), (unsigned)(jobs + qb * runs));
     hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV>), grid, dim3(64 * NWV), 0, s,
                        reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
-                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part,
-                       reinterpret_cast<T *>(O));
-    if (ord.n > 0) {
-        const int64_t n = (int64_t)B * H * ord.nslots * BQL * (HD / 4);
-        hipLaunchKernelGGL((split_merge_kernel<T, HD>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, part, n, N, H,
-                           qb, ord.qs, ord.nslots, BQL, reinterpret_cast<T *>(O));
-    }
-    return launch_prefix<T, HD>(Q, K, Vt, B, N, H, ldv, qb, scale_log2, scratch, O, s);
+                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part, jobs,
+                       scratch, reinterpret_cast<T *>(O));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = ord.n > 0 ? (int64_t)B * H * ord.nslots * BQL * (HD / 4) : 0;
+    const int sblocks = (int)cdiv(n, kMergeThreads), prows = B * H * qb;
+    if (sblocks + prows > 0)
+        hipLaunchKernelGGL((merge_kernel<T, HD>), dim3((unsigned)(sblocks + prows)), dim3(kMergeThreads), 0, s, part,
+                           n, sblocks, N, H, qb, ord.qs, ord.nslots, BQL, scratch, runs, reinterpret_cast<T *>(O));
+    return hipGetLastError();
 }
 
 template <>
