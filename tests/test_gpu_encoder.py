@@ -98,6 +98,14 @@ def test_sensitised_small_clip(gpu_lib, name):
     _parity(cfg)
 
 
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
+def test_prefix_rows_apart(gpu_lib, dtype):
+    """One clip of CLS + 128 patch tokens (LeVJEPA, 2 frames of 8 x 8): the
+    out, up and down projections compute the 128 patch rows on the tile grid
+    and the CLS row apart."""
+    _parity(W.CONFIGS[4].replace(frames=2, height=128, width=128, n_layer=4, dtype=dtype))
+
+
 def test_layer_scale(gpu_lib):
     _parity(SMALL["vjepa2"].replace(layer_scale=1, n_layer=3))
 

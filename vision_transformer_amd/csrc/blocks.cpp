@@ -23,6 +23,27 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
             return e;                                                                                             \
         }                                                                                                         \
     } while (0)
+    // A one-item call whose prefix (CLS) rows add a row block to the GEMMs
+    // (4097 = 4096 patch tokens + CLS) computes the patch rows of the out, up
+    // and down projections on the tile grid and their prefix rows apart
+    // (launch_gemm_rows).  QKV keeps every row: its transposed V stores need
+    // token runs aligned to 8, and its extra row block costs little (24 more
+    // tiles on top of 768).
+    const int pre = g.B == 1 && g.prefix > 0 && g.prefix <= kGemmRowsMax && g.dtype != DT_F32 && !g.wq &&
+                            (M - g.prefix + 127) / 128 < (M + 127) / 128
+                        ? g.prefix
+                        : 0;
+    const int64_t es = dtype_size(g.dtype);
+    auto gemm = [&](int epi, const void *A, int64_t lda, const void *W, int N, int K, EpiArgs ep) {
+        if (pre == 0) return launch_gemm(g.dtype, epi, A, lda, W, K, M, N, K, ep, s);
+        EpiArgs em = ep;
+        if (em.out) em.out = static_cast<char *>(em.out) + pre * em.ldo * es;
+        if (em.Z) em.Z += pre * em.ldz;
+        hipError_t e2 = launch_gemm(g.dtype, epi, static_cast<const char *>(A) + pre * lda * es, lda, W, K, M - pre,
+                                    N, K, em, s);
+        if (e2 != hipSuccess) return e2;
+        return launch_gemm_rows(g.dtype, epi, A, lda, W, K, pre, N, K, ep, s);
+    };
     STEP(launch_layernorm(g.dtype, b.Z, w.ln1_w, w.ln1_b, g.eps, M, D, b.Y, s), "ln1");
     {
         EpiArgs ep;
@@ -48,7 +69,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.ls = g.layer_scale ? w.ls1 : nullptr;
         if (g.wq) ep.wscale = w.out_s;
         splitk(ep);
-        STEP(launch_gemm(g.dtype, EPI_RESID, b.O, D, w.out_w, D, M, D, D, ep, s), "out GEMM");
+        STEP(gemm(EPI_RESID, b.O, D, w.out_w, D, D, ep), "out GEMM");
     }
     STEP(launch_layernorm(g.dtype, b.Z, w.ln2_w, w.ln2_b, g.eps, M, D, b.Y, s), "ln2");
     {
@@ -56,7 +77,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.bias = w.up_b; ep.out = b.U; ep.ldo = F;
         if (g.wq) ep.wscale = w.up_s;
         splitk(ep);
-        STEP(launch_gemm(g.dtype, EPI_GELU, b.Y, D, w.up_w, D, M, F, D, ep, s), "up GEMM");
+        STEP(gemm(EPI_GELU, b.Y, D, w.up_w, F, D, ep), "up GEMM");
     }
     {
         EpiArgs ep;
@@ -64,7 +85,7 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         ep.ls = g.layer_scale ? w.ls2 : nullptr;
         if (g.wq) ep.wscale = w.down_s;
         splitk(ep);
-        STEP(launch_gemm(g.dtype, EPI_RESID, b.U, F, w.down_w, F, M, D, F, ep, s), "down GEMM");
+        STEP(gemm(EPI_RESID, b.U, F, w.down_w, D, F, ep), "down GEMM");
     }
 #undef STEP
     return hipSuccess;

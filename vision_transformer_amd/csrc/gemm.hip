@@ -1229,6 +1229,90 @@ int64_t gemm_splitk_floats(int dtype, int epi, int M, int N, int K, bool wq) {
     return S > 1 ? (int64_t)S * M * N : 0;
 }
 
+namespace {
+// launch_gemm_rows: one wave per output column.  Its lanes read the
+// column's weight row in 16-byte chunks, 8 chunks per lane in flight at once
+// (1 KB of contiguous weights per load instruction; K = 4096 is one round),
+// with the same chunks of each A row; the wave sum goes to the epilogue.
+// Chunks past K read as zero (buffer range check), so there is no tail.
+constexpr int kRowsWaves = 4, kRowsUnroll = 8;
+__device__ __forceinline__ Chunk buf_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(Chunk, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <typename T, int EPI>
+__global__ __launch_bounds__(64 * kRowsWaves) void gemm_rows_kernel(const T *__restrict__ A, int64_t lda,
+                                                                     const T *__restrict__ W, int64_t ldw, int R,
+                                                                     int N, int K, EpiArgs ep) {
+    constexpr int KPC = Elem<T>::kPerChunk;
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * kRowsWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (n >= N) return;
+    const uint32_t rowb = (uint32_t)(K / KPC) * 16u;
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(W + (int64_t)n * ldw, rowb);
+    float acc[kGemmRowsMax];
+#pragma unroll
+    for (int r = 0; r < kGemmRowsMax; ++r) acc[r] = 0.0f;
+    for (int c0 = 0; c0 < K / KPC; c0 += 64 * kRowsUnroll) {
+        Chunk wc[kRowsUnroll];
+#pragma unroll
+        for (int u = 0; u < kRowsUnroll; ++u) wc[u] = buf_chunk(rw, (uint32_t)(c0 + lane + 64 * u) * 16u);
+#pragma unroll
+        for (int r = 0; r < kGemmRowsMax; ++r) {
+            if (r >= R) break;
+            const __amdgpu_buffer_rsrc_t ra = buf_rsrc(A + r * lda, rowb);
+            Chunk ac[kRowsUnroll];
+#pragma unroll
+            for (int u = 0; u < kRowsUnroll; ++u) ac[u] = buf_chunk(ra, (uint32_t)(c0 + lane + 64 * u) * 16u);
+#pragma unroll
+            for (int u = 0; u < kRowsUnroll; ++u) {
+                const T *we = reinterpret_cast<const T *>(&wc[u]), *ae = reinterpret_cast<const T *>(&ac[u]);
+#pragma unroll
+                for (int e = 0; e < KPC; ++e) acc[r] = fmaf(to_f32(ae[e]), to_f32(we[e]), acc[r]);
+            }
+        }
+    }
+    const float bias = ep.bias ? ep.bias[n] : 0.0f;
+    const float ls = EPI == EPI_RESID && ep.ls ? ep.ls[n] : 1.0f;
+    for (int r = 0; r < R; ++r) {
+        const float v0 = wave_sum(acc[r]) + bias;
+        if (lane != 0) continue;
+        if constexpr (EPI == EPI_STORE || EPI == EPI_GELU) {
+            const float v = EPI == EPI_GELU ? gelu_erf(v0) : v0;
+            reinterpret_cast<T *>(ep.out)[(int64_t)r * ep.ldo + n] = from_f32<T>(v);
+        } else if constexpr (EPI == EPI_RESID) {
+            ep.Z[(int64_t)r * ep.ldz + n] += ep.ls ? v0 * ls : v0;
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_rows_t(int epi, const void *A, int64_t lda, const void *W, int64_t ldw, int R, int N, int K,
+                         const EpiArgs &ep, hipStream_t s) {
+    const dim3 grid((unsigned)cdiv(N, kRowsWaves)), block(64 * kRowsWaves);
+    const T *a = reinterpret_cast<const T *>(A), *w = reinterpret_cast<const T *>(W);
+    switch (epi) {
+    case EPI_STORE: hipLaunchKernelGGL((gemm_rows_kernel<T, EPI_STORE>), grid, block, 0, s, a, lda, w, ldw, R, N, K, ep); break;
+    case EPI_GELU: hipLaunchKernelGGL((gemm_rows_kernel<T, EPI_GELU>), grid, block, 0, s, a, lda, w, ldw, R, N, K, ep); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_rows_kernel<T, EPI_RESID>), grid, block, 0, s, a, lda, w, ldw, R, N, K, ep); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+} // namespace
+
+hipError_t launch_gemm_rows(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw, int R,
+                            int N, int K, const EpiArgs &ep, hipStream_t s) {
+    if (R <= 0 || N <= 0) return hipSuccess;
+    if (R > kGemmRowsMax || K % 8 != 0 || lda % 8 != 0 || ldw % 8 != 0 || ep.wscale || ep.kwrap ||
+        (uintptr_t)A % 16 != 0 || (uintptr_t)W % 16 != 0)
+        return hipErrorInvalidValue;
+    switch (dtype) {
+    case DT_BF16: return launch_rows_t<bf16_t>(epi, A, lda, W, ldw, R, N, K, ep, s);
+    case DT_F16: return launch_rows_t<f16_t>(epi, A, lda, W, ldw, R, N, K, ep, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N,
                        int K, const EpiArgs &ep, hipStream_t s) {
     if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;

@@ -78,6 +78,14 @@ inline int embed_lda(int dtype, int K) {
 hipError_t launch_gemm(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw,
                        int M, int N, int K, const EpiArgs &ep, hipStream_t s);
 
+// The same GEMM and epilogue (STORE, GELU or RESID) for R <= kGemmRowsMax
+// rows, A's rows lda apart: a dot product per output, for the few prefix rows
+// of a one-item call whose patch rows then fill the tile grid of launch_gemm
+// exactly.  16-bit types, K % 8 == 0.
+constexpr int kGemmRowsMax = 4;
+hipError_t launch_gemm_rows(int dtype, int epi, const void *A, int64_t lda, const void *W, int64_t ldw, int R,
+                            int N, int K, const EpiArgs &ep, hipStream_t s);
+
 // codes [rows, cols] E4M3 and scales [cols/64][rows][2] E8M0 of the fp32
 // matrix w [rows, cols] (cols % 64 == 0; w and codes 16-byte aligned)
 hipError_t launch_mxfp8_quantize(const float *w, int rows, int cols, uint8_t *codes, uint8_t *scales,
