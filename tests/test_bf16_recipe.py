@@ -67,3 +67,40 @@ def test_recipe_error_at_vit_g_depth():
     assert abs(st["maxabs"] - 0.0200) <= 1e-4, st["maxabs"]
     assert st["maxabs"] >= 0.95 * ABS_BF16
     assert st["maxabs"] <= 0.7 * abs_gate(cfg.n_layer)
+
+
+@pytest.mark.parametrize("name", ["vjepa2", "vjepa21", "levjepa"])
+def test_sensitised_bf16_gate_sees_planted_mistakes(name):
+    """On the sensitised small clips in bf16 (4 layers) the recipe alone is
+    0.03-0.16 max-abs from the oracle; the GPU test of those clips allows
+    twice that.  A wrong RoPE layout, a missing interpolation or a full mask
+    in place of the block-causal one moves the oracle's output at least five
+    times further than that allowance in max-abs (19-57 times the recipe's
+    own distance) and a hundred times further in per-token cosine."""
+    small = {
+        "vjepa2": W.CONFIGS[2].replace(frames=4, height=48, width=64, batch=2),
+        "vjepa21": W.CONFIGS[3].replace(frames=4, height=64, width=48),
+        "levjepa": W.CONFIGS[4].replace(frames=5, height=48, width=32),
+    }
+    cfg = W.sensitised(small[name].replace(n_layer=4), std_qk=0.1, std_tok=1.0)
+    wl = W.make_workload(cfg)
+    ref, _ = oracle.encoder_forward(cfg, wl.weights, wl.pixels)
+    emu = R.encoder_forward_recipe(cfg, wl.weights, wl.pixels)
+    st = oracle.compare(emu, ref)
+    allow_abs, allow_cos = 2.0 * st["maxabs"] + 2e-3, 2.0 * (1.0 - st["min_cos"]) + 1e-6
+    rp, vis = oracle.rope_and_mask(cfg, wl.pixels.shape)
+
+    def run(c, pos, visible):
+        Z = oracle.embed(c, wl.weights, wl.pixels)
+        for blk in wl.weights.blocks:
+            Z = oracle.encoder_block(Z, blk, c, pos, visible)
+        return oracle.layer_norm(Z, wl.weights.norm_w, wl.weights.norm_b, c.ln_eps)
+
+    planted = [run(cfg.replace(rope_layout=1 - cfg.rope_layout), rp, vis)]
+    if cfg.rope_interpolate:
+        planted.append(run(cfg, oracle.rope_and_mask(cfg.replace(rope_interpolate=0), wl.pixels.shape)[0], vis))
+    if cfg.attn_mode == W.ATTN_BLOCK_CAUSAL:
+        planted.append(run(cfg, rp, oracle.rope_and_mask(cfg.replace(attn_mode=W.ATTN_FULL), wl.pixels.shape)[1]))
+    for bad in planted:
+        sb = oracle.compare(bad, ref)
+        assert sb["maxabs"] > 5 * allow_abs and 1.0 - sb["min_cos"] > 100 * allow_cos, (sb, st)

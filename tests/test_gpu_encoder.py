@@ -98,6 +98,30 @@ def test_sensitised_small_clip(gpu_lib, name):
     _parity(cfg)
 
 
+@pytest.mark.parametrize("name", ["vjepa2", "vjepa21", "levjepa", "hfvit"])
+def test_sensitised_small_clip_bf16(gpu_lib, name):
+    """The sensitised clips on the bf16 path (the direct-to-LDS kernels the
+    bf16 workloads use, with their RoPE, mask, CLS and modality handling).
+    Peaked attention makes the bf16 recipe's own error exceed the 2e-2 gate,
+    so the gate here is derived from it: the CPU emulation of the recipe
+    (tests/bf16_recipe.py) on the same inputs gives the recipe's distance to
+    the oracle, and the kernels may add at most as much again.  A planted
+    RoPE-layout, interpolation or mask mistake moves the output 19-57 times
+    further than the recipe does (test_bf16_recipe.py pins that margin)."""
+    import bf16_recipe as R
+    cfg = W.sensitised(SMALL[name].replace(n_layer=4, dtype=W.DTYPE_BF16), std_qk=0.1, std_tok=1.0)
+    say(f"encode {cfg.name} L={cfg.n_layer} B={cfg.batch} N={cfg.n_tokens} (bf16, sensitised)")
+    wl = W.make_workload(cfg)
+    out, _ = run_gpu(wl)
+    ref, _ = oracle.encoder_forward(cfg, wl.weights, wl.pixels)
+    emu = R.encoder_forward_recipe(cfg, wl.weights, wl.pixels)
+    st_gpu, st_emu = oracle.compare(out, ref), oracle.compare(emu, ref)
+    say(f"  gpu {st_gpu}\n  recipe {st_emu}")
+    assert st_gpu["finite"]
+    assert st_gpu["maxabs"] <= 2.0 * st_emu["maxabs"] + 2e-3, (st_gpu, st_emu)
+    assert 1.0 - st_gpu["min_cos"] <= 2.0 * (1.0 - st_emu["min_cos"]) + 1e-6, (st_gpu, st_emu)
+
+
 @pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
 def test_prefix_rows_apart(gpu_lib, dtype):
     """One clip of CLS + 128 patch tokens (LeVJEPA, 2 frames of 8 x 8): the
