@@ -258,13 +258,16 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[j][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+            mx *= scale_log2;
             // Lazy rescaling: the running max m_run (log2 units) moves only
             // when a score exceeds it by more than kRescale, so most tiles skip
             // the O rescale; exponents stay <= kRescale, and O / l is the same
-            // for any m_run.
-            const bool grow = mx > m_run + kRescale;
-            if (__ballot(grow)) {
+            // for any m_run.  A query's scores sit in a lane pair (l, l ^ 32):
+            // either lane's own maximum decides whether the pair's moves, and
+            // the pair maximum is formed only on the rescaling tiles.
+            if (__ballot(mx > m_run + kRescale)) {
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const bool grow = mx > m_run + kRescale;
                 // lanes that do not grow keep their state (alpha 1): their
                 // m_run may still be -inf, and exp2(-inf - -inf) is NaN
                 const float m_new = grow ? mx : m_run;
@@ -680,13 +683,23 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
                     if (key < lo || key >= hi) sc[j][i] = -INFINITY;
                 }
         }
+        // Each query's scores sit in a lane pair (l, l ^ 32).  The pair's
+        // maximum is needed only when the running max moves, which happens
+        // iff either lane's own maximum exceeds m_run + kRescale: the lane
+        // maxima decide that without the cross-lane exchange, and the pair
+        // maximum is taken only on the (rare) rescaling tiles.
+        {
+            float m0 = sc[0][0], m1 = sc[1][0];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[j][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
-        const bool grow = mx > m_run + kRescale;
-        if (__ballot(grow)) {
+            for (int i = 1; i < 16; ++i) {
+                m0 = fmaxf(m0, sc[0][i]);
+                m1 = fmaxf(m1, sc[1][i]);
+            }
+            mx = fmaxf(m0, m1) * scale_log2;
+        }
+        if (__ballot(mx > m_run + kRescale)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const bool grow = mx > m_run + kRescale;
             // lanes that do not grow keep their state: a lane whose keys in
             // this half of a split tile are all masked still has m_run = -inf,
             // and exp2(-inf - -inf) would be NaN

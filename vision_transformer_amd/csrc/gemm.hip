@@ -747,7 +747,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     constexpr int AI = BM / (RPI * NW), BI = BN / (RPW * NW); // load instructions per wave and slab
     constexpr int SC_CH = WQ ? 64 : 0;                  // scale bytes of a slab: one 1 KB load
     constexpr int STAGE_CH = BM * NCH + BN * WCH + SC_CH; // chunks per LDS stage
-    static_assert(NCH == 4 || NCH == 8, "slab of 64 or 128 bytes per row");
+    static_assert(NCH == 4 || NCH == 8 || NCH == 16, "slab of 64, 128 or 256 bytes per row");
     static_assert(WM % MI == 0 && WN % MI == 0 && AI * RPI * NW == BM && BI * RPW * NW == BN, "tile");
     static_assert(MI == 32 || MI == 16, "MFMA tile");
     static_assert(!WQ || (std::is_same<T, bf16_t>::value && MI == 32 && NCH == 8 && 2 * BN <= 1024),
@@ -777,21 +777,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     // Buffer loads: one resource per operand, a per-lane byte offset and a
     // scalar offset for the slab and the instruction's row block.  Lane l of
     // load instruction j fetches row RPI*j + l/NCH of the wave's share of the
-    // slab; the swizzled chunk of rows RPI*j + r depends on j only through
-    // its parity (8-chunk rows), or not at (4-chunk rows), so two lane
-    // offsets cover every instruction.
+    // slab.  The swizzle repeats every 16 rows and each wave's share starts
+    // on a multiple of 16, so the swizzled chunk of rows RPI*j + r depends on
+    // j only through j mod 16/RPI: one lane offset for 4-chunk rows, two for
+    // 8-chunk rows, four for 16-chunk rows.
     constexpr uint32_t ES = sizeof(T);
     constexpr uint32_t WES = WQ ? 1 : sizeof(T); // bytes per weight
+    constexpr int JA = 16 / RPI, JB = 16 / RPW;  // distinct lane offsets per operand
+    static_assert((BM / NW) % 16 == 0 && (BN / NW) % 16 == 0, "wave shares of whole 16-row blocks");
     const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void *)A, 0, a_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void *)W, 0, b_bytes, 0x00020000);
     const int lrow = lane / NCH, lch = lane % NCH;
-    const int sw0 = swz<NCH>(lrow), sw1 = swz<NCH>(lrow + RPI); // row parity 0 / 1 of 8-row blocks
-    const uint32_t va0 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw0) * KPC) * ES);
-    const uint32_t va1 = (uint32_t)(((int64_t)(m0 + wave * AI * RPI + lrow) * lda + (lch ^ sw1) * KPC) * ES);
+    const int64_t arow = (int64_t)(m0 + wave * AI * RPI + lrow) * lda;
+    uint32_t va[JA];
+#pragma unroll
+    for (int j = 0; j < JA; ++j) va[j] = (uint32_t)((arow + (lch ^ swz<NCH>(j * RPI + lrow)) * KPC) * ES);
     const int wrow = lane / WCH, wch = lane % WCH;
-    const int ws0 = swz<WCH>(wrow), ws1 = swz<WCH>(wrow + RPW);
-    const uint32_t vb0 = (uint32_t)((int64_t)(n0 + wave * BI * RPW + wrow) * ldw * WES + (wch ^ ws0) * 16);
-    const uint32_t vb1 = (uint32_t)((int64_t)(n0 + wave * BI * RPW + wrow) * ldw * WES + (wch ^ ws1) * 16);
+    const int64_t brow = (int64_t)(n0 + wave * BI * RPW + wrow) * ldw * WES;
+    uint32_t vb[JB];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) vb[j] = (uint32_t)(brow + (wch ^ swz<WCH>(j * RPW + wrow)) * 16);
     const int kw = ep.kwrap ? ep.kwrap : K; // W columns
     const __amdgpu_buffer_rsrc_t rss =
         __builtin_amdgcn_make_buffer_rsrc((void *)(WQ ? ep.wscale : nullptr), 0, WQ ? s_bytes : 0, 0x00020000);
@@ -803,14 +808,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
         for (int j = 0; j < AI; ++j) {
             const int row = (wave * AI + j) * RPI;
             const uint32_t soff = (uint32_t)((k0 + (int64_t)j * RPI * lda) * ES);
-            load(rsa, &lA(stage, row, 0), ((row / RPI) & 1) ? va1 : va0, soff);
+            load(rsa, &lA(stage, row, 0), va[j % JA], soff);
         }
         const int kb = k0 >= kw ? k0 - kw : k0; // W column of A column k0
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
             const int row = (wave * BI + j) * RPW;
             const uint32_t soff = (uint32_t)((kb + (int64_t)j * RPW * ldw) * WES);
-            load(rsb, &lW(stage, row, 0), ((row / RPW) & 1) ? vb1 : vb0, soff);
+            load(rsb, &lW(stage, row, 0), vb[j % JB], soff);
         }
         if constexpr (WQ) {
             // scale bytes of rows n0 .. n0 + BN for this slab: [k0/64][n][2]
@@ -1020,7 +1025,9 @@ inline int splits_with(int epi, int64_t tiles, int nk, int per_cu, int min_steps
 }
 // workgroups per CU and minimum K steps per split of each kernel configuration
 constexpr int kRegPerCU = 2, kRegMinSteps = 2, kLdsMinSteps = 8;
-constexpr int lds_per_cu(int BM, int STAGES) { return BM == 64 ? 3 : (BM == 128 && STAGES == 2) ? 2 : 1; }
+constexpr int lds_per_cu(int BM, int NCH, int STAGES) {
+    return NCH == 16 ? 1 : BM == 64 ? 3 : (BM == 128 && STAGES == 2) ? 2 : 1;
+}
 
 // Second half of a split GEMM: v = (partial_0 + ... + partial_{S-1}) + bias,
 // added in split order (the result does not depend on the order in which
@@ -1098,7 +1105,7 @@ hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, in
     const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
     const int64_t wbytes = WQ ? 1 : (int64_t)sizeof(T);
     EpiArgs e = ep;
-    e.splits = splits_with(EPI, (int64_t)tiles_m * tiles_n, K / (NCH * Elem<T>::kPerChunk), lds_per_cu(BM, STAGES),
+    e.splits = splits_with(EPI, (int64_t)tiles_m * tiles_n, K / (NCH * Elem<T>::kPerChunk), lds_per_cu(BM, NCH, STAGES),
                            kLdsMinSteps, M, N, K, ep);
     hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, WQ>),
                        dim3((unsigned)(tiles_m * tiles_n * e.splits)), dim3(64 * WGM * WGN), 0, s,
@@ -1121,7 +1128,10 @@ constexpr int kDeepStages = 3; // LDS ring of the one-tile-per-CU 128 x 128 conf
 
 // With at most one 128 x 128 tile per CU (the N = D projections of one clip)
 // occupancy cannot hide the first touch of the weights in HBM: those tiles
-// keep more slabs in flight instead.
+// keep more slabs in flight instead, and (when K is a multiple of 128) run as
+// 4 waves of 64 x 64 blocks over 128-deep slabs in a two-stage ring, which
+// reads a third fewer fragment bytes from LDS per MFMA than 8 waves of 64 x 32
+// and takes half as many barriers.
 // 256 x 256 tiles are skipped when they would need a nearly empty second
 // round.  When 128 x 128 tiles would leave more than half of the CUs idle (the
 // width-384 projections of the predictor), 64 x 64 tiles of 4 waves spread
@@ -1176,6 +1186,7 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
         case TILE_256x256: return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_128x128: return launch_lds<T, EPI, 128, 128, 2, 4, 8, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_128x128_DEEP:
+            if (K % 128 == 0) return launch_lds<T, EPI, 128, 128, 2, 2, 16, 2, 32>(A, lda, W, ldw, M, N, K, ep, s);
             return launch_lds<T, EPI, 128, 128, 2, 4, 8, kDeepStages, 32>(A, lda, W, ldw, M, N, K, ep, s);
         case TILE_64x64: return launch_lds<T, EPI, 64, 64, 2, 2, 8, 3, 32>(A, lda, W, ldw, M, N, K, ep, s);
         default: break;
@@ -1210,13 +1221,21 @@ int64_t gemm_splitk_floats(int dtype, int epi, int M, int N, int K, bool wq) {
     if (M <= 0 || N <= 0 || K <= 0) return 0;
     int bm, nk, per_cu, min_steps;
     if (dtype != DT_F32 && (K % 64 == 0 || wq)) {
-        switch (pick_tile(M, N, true, false)) {
-        case TILE_256x256: bm = 256; per_cu = lds_per_cu(256, 2); break;
-        case TILE_128x128: bm = 128; per_cu = lds_per_cu(128, 2); break;
-        case TILE_128x128_DEEP: bm = 128; per_cu = lds_per_cu(128, kDeepStages); break;
-        default: bm = 64; per_cu = lds_per_cu(64, 3); break;
-        }
         nk = K / 64;
+        switch (pick_tile(M, N, true, false)) {
+        case TILE_256x256: bm = 256; per_cu = lds_per_cu(256, 8, 2); break;
+        case TILE_128x128: bm = 128; per_cu = lds_per_cu(128, 8, 2); break;
+        case TILE_128x128_DEEP:
+            bm = 128;
+            if (K % 128 == 0 && !wq) {
+                per_cu = lds_per_cu(128, 16, 2);
+                nk = K / 128;
+            } else {
+                per_cu = lds_per_cu(128, 8, kDeepStages);
+            }
+            break;
+        default: bm = 64; per_cu = lds_per_cu(64, 8, 3); break;
+        }
         min_steps = kLdsMinSteps;
     } else {
         bm = reg_small_tiles(M, N) ? 64 : 128;
