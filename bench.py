@@ -10,7 +10,11 @@ video encoder, 2 clips x 16 frames x 3 x 256 x 256 -> 2 x 2048 tokens, 24
 layers, bf16 with fp32 accumulation, synthetic seeded inputs resident in HBM.
 Prints one JSON line.  The roofline object is measured for the dominant
 kernel by timing its step entry point (the same kernel and launch
-configuration encode uses) with HIP events on the stream it is launched on.
+configuration encode uses) with HIP events on the stream it is launched on:
+its launches back to back between one event pair, weights rotating over the
+layers, which is what a rocprofv3 kernel trace of `--only KERNEL` measures
+(`in_layer_ms` is the time of one launch bracketed by its own event pair
+inside the layer sequence, dispatch latency included).
 The line's `predictor` object times the masked-latent predictor that follows
 the encoder (one vitenc_predict call per step) the same way, with its own
 roofline and oracle baseline; `head` does the same for the attentive-pool
@@ -260,7 +264,8 @@ def kernel_breakdown(cfg, enc, reps, stream, busy, only=None):
     did not; the RoPE table is filled once, as encode does.  `busy()` queues a
     few full encode steps first so that the GPU is still working while the
     host queues the layer sequences: each event pair then brackets the kernel
-    alone.  Returns {name: (ms per launch, flops, bytes)}."""
+    alone.  Returns {name: (ms per launch in the layer sequence, flops, bytes,
+    ms per launch alone)}."""
     import torch
     from vision_transformer_amd import vitenc as V
     B, N, D, F, H = cfg.batch, cfg.n_tokens, cfg.embed_dim, cfg.ffn_dim, cfg.n_head
@@ -310,6 +315,7 @@ def kernel_breakdown(cfg, enc, reps, stream, busy, only=None):
 
     seqs = [layer(enc.blocks[r % len(enc.blocks)]) for r in range(reps)]
     if only is not None:
+        busy()
         for seq in seqs:
             for name, fn in seq:
                 if name == only:
@@ -335,6 +341,23 @@ def kernel_breakdown(cfg, enc, reps, stream, busy, only=None):
     log(f"[bench] layer sequence: kernels {sum(acc.values()):.3f} ms of {first.elapsed_time(last):.3f} ms span "
         f"over {reps} layers")
     res = {name: (acc[name] / cnt[name],) + work[name] for name in acc}
+    # Each kernel also alone: its `reps` launches back to back (weights of
+    # layer r mod L, as above) between one event pair, which is what a
+    # rocprofv3 kernel trace of `--only NAME` measures.  The event pairs
+    # around single launches above also hold each launch's dispatch latency.
+    alone = {}
+    for name in res:
+        fns = [fn for seq in seqs for nm, fn in seq if nm == name][:reps]
+        busy()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for fn in fns:
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        alone[name] = a0.elapsed_time(a1) / len(fns)
+    log("[bench] each kernel alone, back to back (ms): " + ", ".join(f"{k}={v:.4f}" for k, v in alone.items()))
+    res = {name: v + (alone[name],) for name, v in res.items()}
     # calibration for the HBM byte counters: a plain device copy of known size
     # (fp32 -> int32 keeps the element size, so torch launches its own copy kernel)
     src = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
@@ -410,10 +433,13 @@ def _oracle_cores():
 
 def roofline_of(bd, workload):
     """The roofline object of the kernel that takes the most time in one
-    forward (layernorm runs twice per block)."""
+    forward (layernorm runs twice per block), timed alone: its launches back
+    to back between one event pair, as a rocprofv3 kernel trace of
+    `bench.py --only KERNEL` measures it; the time of each launch inside the
+    layer sequence (with its dispatch latency) is reported beside it."""
     weight = {"layernorm": 2}
-    dom = max(bd, key=lambda k: bd[k][0] * weight.get(k, 1))
-    d_ms, d_flops, d_bytes = bd[dom]
+    dom = max(bd, key=lambda k: bd[k][3] * weight.get(k, 1))
+    in_layer_ms, d_flops, d_bytes, d_ms = bd[dom]
     if d_flops > 0:
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(d_flops / (d_ms * 1e-3) / 1e12, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
@@ -422,6 +448,8 @@ def roofline_of(bd, workload):
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["avg_launch_ms"] = round(d_ms, 5)
+    roof["timing"] = "launches back to back, weights of layer r mod L"
+    roof["in_layer_ms"] = round(in_layer_ms, 5)
     traffic = read_traffic(dom, workload)
     roof["traffic"] = None if traffic is None else round(traffic / 1e6, 2)
     roof["traffic_unit"] = "MB per launch"
@@ -497,6 +525,7 @@ def bench_predictor(args, stream):
                       "embed_dim": cfg.embed_dim, "enc_dim": cfg.enc_dim, "layers": cfg.n_layer,
                       "heads": cfg.n_head},
            "kernels_ms_per_layer": {k: round(v[0], 5) for k, v in bd.items()},
+           "kernels_ms_alone": {k: round(v[3], 5) for k, v in bd.items()},
            "roofline": roofline_of(bd, cfg.name), "cpu_baseline": None}
     if not args.no_cpu_baseline:
         log("[bench] predictor cpu baseline (oracle) ...")
@@ -590,6 +619,7 @@ def bench_head(args, stream):
            "config": {"global_batch": cfg.batch, "tokens_per_item": cfg.n_tokens, "embed_dim": cfg.embed_dim,
                       "pool_layers": cfg.n_pool_layers, "heads": cfg.n_head, "classes": cfg.n_classes},
            "kernels_ms_per_layer": {k: round(v[0], 5) for k, v in bd.items()},
+           "kernels_ms_alone": {k: round(v[3], 5) for k, v in bd.items()},
            "roofline": roofline_of(bd, cfg.name), "xattn_roofline": xroof, "cpu_baseline": None}
     if not args.no_cpu_baseline:
         log("[bench] head cpu baseline (oracle) ...")
@@ -817,7 +847,14 @@ def main():
     wl = W.make_workload(cfg)
     enc = V.Encoder.from_workload(wl)
     if args.only:
-        kernel_breakdown(cfg, enc, args.kernel_reps, stream, lambda: None, only=args.only)
+        def warm():
+            # library GEMMs (kernels of other names) queued ahead, so that the
+            # kernel's launches run on a busy GPU, as in the layer-sequence timing
+            a = torch.randn((4096, 4096), device="cuda", dtype=torch.bfloat16)
+            for _ in range(100):
+                torch.matmul(a, a)
+
+        kernel_breakdown(cfg, enc, args.kernel_reps, stream, warm, only=args.only)
         print(json.dumps({"only": args.only, "launches": args.kernel_reps}), flush=True)
         return
     px = torch.from_numpy(wl.pixels).cuda()
@@ -876,6 +913,7 @@ def main():
                    "embed_dim": cfg.embed_dim, "layers": cfg.n_layer, "heads": cfg.n_head,
                    "graph": bool(args.graph)},
         "kernels_ms_per_layer": {k: round(v, 5) for k, v in per_layer.items()},
+        "kernels_ms_alone": {k: round(v[3], 5) for k, v in bd.items()},
         "roofline": roof,
         "cpu_baseline": cpu,
         "predictor": pred,
