@@ -183,6 +183,37 @@ template <int EPI> __device__ __forceinline__ float epi_act(float v) {
 // outputs are then 16-byte, row-contiguous vectors instead of per-element
 // accesses.  The V part of the QKV projection is read back transposed (8
 // consecutive rows of one column) because V is stored transposed per head.
+// The residual rows the RESID epilogue updates when they were not prefetched
+// at kernel start (NZ == 0): ZD row blocks of the wave's tile in flight, each
+// lane holding its 8 columns of NPASS rows per block.  request(f) asks for
+// row block f into slot f % ZD with branch-free range-checked loads (see
+// buf_rsrc) from the wave's first row.
+template <int EPI, int NZ, int FM, int MI, int WN> struct ZRows {
+    using RP = RowPath<MI, WN>;
+    static constexpr bool kOn = EPI == EPI_RESID && NZ == 0;
+    static constexpr int NZB = kOn ? RP::NPASS : 1;
+    static constexpr int ZD = FM < 2 ? FM : 2; // blocks in flight
+    float4 q[ZD][NZB][2];
+    __device__ __forceinline__ void request(int f, int m0, int woff_m, int n0, int woff_n, int M, const EpiArgs &ep,
+                                            bool to_part) {
+        if constexpr (kOn) {
+            const int lane = threadIdx.x & 63;
+            const int col0 = n0 + woff_n + (lane % RP::CPR) * 8;
+            const int64_t zr0 = m0 + woff_m;
+            const int64_t zbytes = !to_part && zr0 < M ? (int64_t)(M - zr0) * ep.ldz * 4 : 0;
+            const __amdgpu_buffer_rsrc_t rzb =
+                buf_rsrc(ep.Z + zr0 * ep.ldz, (uint32_t)(zbytes < 0xFFFFFFF0ll ? zbytes : 0xFFFFFFF0ll));
+#pragma unroll
+            for (int p = 0; p < RP::NPASS; ++p) {
+                const int r = f * MI + p * RP::RPP + lane / RP::CPR;
+                const uint32_t off = (uint32_t)(((int64_t)r * ep.ldz + col0) * 4);
+                q[f % ZD][p][0] = buf_f32x4(rzb, off);
+                q[f % ZD][p][1] = buf_f32x4(rzb, off + 16u);
+            }
+        }
+    }
+};
+
 // Everything the epilogue reads from global memory besides the accumulators
 // was requested at kernel start (epi_prefetch), except for the residual rows
 // of tiles too wide to hold them in registers: those are requested one row
@@ -194,7 +225,7 @@ template <typename T, int BM, int FM, int FN, int EPI, int NT, int MI, int WN, b
 __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], const EpiPre<NZ, NTAB> &pre, RowInfo *ri,
                                               float *stage, float2 *lds_tab, int lds_tab_cap, int m0, int n0,
                                               int woff_m, int woff_n, int M, int N, const EpiArgs &ep,
-                                              float *part = nullptr) {
+                                              float *part, ZRows<EPI, NZ, FM, MI, WN> &zr, bool z_requested) {
     using RP = RowPath<MI, WN>;
     constexpr int NV = MI == 32 ? 16 : 4; // accumulator values per lane per block
     constexpr int LD = WN + 4;            // staging row stride (floats), 16-byte aligned
@@ -336,29 +367,14 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], const EpiPre<
 
     // residual rows (when not prefetched at kernel start): the values of row
     // blocks fm and fm + 1 are requested before block fm is processed, so one
-    // round trip to memory serves two blocks
-    constexpr bool kZBlock = EPI == EPI_RESID && NZ == 0;
-    constexpr int NZB = kZBlock ? NPASS : 1;
-    constexpr int ZD = FM < 2 ? FM : 2; // blocks in flight
-    float4 zq[ZD][NZB][2];
-    // branch-free range-checked loads (see buf_rsrc) from the wave's first row
-    const int64_t zr0 = m0 + woff_m;
-    const int64_t zbytes = kZBlock && !part && zr0 < M ? (int64_t)(M - zr0) * ep.ldz * 4 : 0;
-    const __amdgpu_buffer_rsrc_t rzb =
-        buf_rsrc(kZBlock ? ep.Z + zr0 * ep.ldz : nullptr, (uint32_t)(zbytes < 0xFFFFFFF0ll ? zbytes : 0xFFFFFFF0ll));
-    auto load_zblock = [&](float4 (&dst)[NZB][2], int fm) {
-        if constexpr (kZBlock) {
+    // round trip to memory serves two blocks (the first ZD blocks may have been
+    // requested by the caller already, under its last K step)
+    constexpr int ZD = ZRows<EPI, NZ, FM, MI, WN>::ZD;
+    auto &zq = zr.q;
+    if (!z_requested) {
 #pragma unroll
-            for (int p = 0; p < NPASS; ++p) {
-                const int r = fm * MI + p * RPP + lane / CPR;
-                const uint32_t off = (uint32_t)(((int64_t)r * ep.ldz + col0) * 4);
-                dst[p][0] = buf_f32x4(rzb, off);
-                dst[p][1] = buf_f32x4(rzb, off + 16u);
-            }
-        }
-    };
-#pragma unroll
-    for (int f = 0; f < ZD; ++f) load_zblock(zq[f], f);
+        for (int f = 0; f < ZD; ++f) zr.request(f, m0, woff_m, n0, woff_n, M, ep, part != nullptr);
+    }
 
     auto row_path = [&](int rt, int zi, int p, int zslot, const float (&x)[8]) {
         const int row = m0 + rt;
@@ -493,7 +509,7 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[FM][FN], const EpiPre<
             }
         }
         // the slot of block fm is free: request block fm + ZD into it
-        if (fm + ZD < FM) load_zblock(zq[fm % ZD], fm + ZD);
+        if (fm + ZD < FM) zr.request(fm + ZD, m0, woff_m, n0, woff_n, M, ep, part != nullptr);
         if constexpr (EPI == EPI_QKV) {
             // V columns: lane -> (column, 8 consecutive rows), stored along tokens
             static_assert(64 % WN == 0, "one V column per lane");
@@ -680,9 +696,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(const T *__restrict__
     float *stage = reinterpret_cast<float *>(sbase + kRiBytes) + wave * 32 * (WN + 4);
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(smem) - kRiBytes - kStageBytes) / 8;
+    ZRows<EPI, kNZ, FM, 32, WN> zr;
     gemm_epilogue<T, BM, FM, FN, EPI, kThreads, 32, WN, false>(
         acc, pre, ri, stage, ltab, kTabCap, m0, n0, wm * WM, wn * WN, M, N, ep,
-        ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
+        ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr, zr, false);
 }
 
 
@@ -947,9 +964,23 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     frags(a0, b0, 0, 0);
     expand(b0, 0);
     int stage = 0;
+    // RESID: the first residual row blocks are requested at the start of the
+    // last K step, after its slab has landed (no slab load is issued after
+    // them), so that their round trip hides under that step's MFMAs.  Not in
+    // the configurations whose registers are full already: 256-row tiles
+    // (the values would spill) and the 128 x 128 two-stage tiles that need
+    // 128 registers or fewer for two workgroups per CU.
+    ZRows<EPI, kNZ, FM, MI, WN> zr;
+    constexpr bool kZEarly =
+        ZRows<EPI, kNZ, FM, MI, WN>::kOn && BM <= 128 && !(BM == 128 && NW == 8 && STAGES == 2);
     for (int kt = 0; kt < nk; ++kt) {
         int nstage = stage + 1;
         if (nstage == STAGES) nstage = 0;
+        if (kZEarly && kt == nk - 1) {
+#pragma unroll
+            for (int f = 0; f < ZRows<EPI, kNZ, FM, MI, WN>::ZD; ++f)
+                zr.request(f, m0, wm * WM, n0, wn * WN, M, ep, ep.splits > 1);
+        }
 #pragma unroll
         for (int s = 0; s < KSUB; ++s) {
             Chunk *ca = (s & 1) ? a1 : a0, *cb = (s & 1) ? b1 : b0;
@@ -993,8 +1024,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     float2 *ltab = reinterpret_cast<float2 *>(sbase + kRiBytes + kStageBytes);
     constexpr int kTabCap = ((int)sizeof(lds) - kRiBytes - kStageBytes) / 8;
     gemm_epilogue<T, BM, FM, FN, EPI, NT, MI, WN, MI == 32>(acc, pre, ri, estage, ltab, kTabCap, m0, n0, wm * WM,
-                                                            wn * WN, M, N,
-                                                  ep, ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr);
+                                                            wn * WN, M, N, ep,
+                                                            ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr,
+                                                            zr, kZEarly && nk > 0);
 }
 
 // Split-K where the output tiles fill at most half of the per_cu workgroup
