@@ -43,6 +43,15 @@ def test_full_token_count_two_layers(gpu_lib, idx):
     _parity(W.CONFIGS[idx], n_layer=2)
 
 
+def test_one_clip_split_k_deep_tiles(gpu_lib):
+    """One 16-frame ViT-L clip (2048 tokens): its out and down projections
+    have one 128 x 128 tile per CU for half of the CUs, so they run the
+    4-wave 128-deep-slab tiles, and the down projection (K 4096) also splits
+    K over two workgroups per tile (partials through the workspace, then the
+    reduction applies the residual epilogue)."""
+    _parity(W.CONFIGS[2].replace(batch=1), n_layer=2)
+
+
 def test_vit_g_video_one_layer_sampled_rows(gpu_lib):
     """18432 tokens, D 1408, 22 heads, interleaved RoPE with interpolation and
     the modality vector: one full-size layer, checked on sampled tokens."""
