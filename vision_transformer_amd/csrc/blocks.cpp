@@ -39,10 +39,12 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         EpiArgs em = ep;
         if (em.out) em.out = static_cast<char *>(em.out) + pre * em.ldo * es;
         if (em.Z) em.Z += pre * em.ldz;
-        hipError_t e2 = launch_gemm(g.dtype, epi, static_cast<const char *>(A) + pre * lda * es, lda, W, K, M - pre,
-                                    N, K, em, s);
+        // the prefix rows first: their kernel reads the whole weight matrix
+        // once, which leaves it in the last-level cache for the tile grid
+        hipError_t e2 = launch_gemm_rows(g.dtype, epi, A, lda, W, K, pre, N, K, ep, s);
         if (e2 != hipSuccess) return e2;
-        return launch_gemm_rows(g.dtype, epi, A, lda, W, K, pre, N, K, ep, s);
+        return launch_gemm(g.dtype, epi, static_cast<const char *>(A) + pre * lda * es, lda, W, K, M - pre, N, K, em,
+                           s);
     };
     STEP(launch_layernorm(g.dtype, b.Z, w.ln1_w, w.ln1_b, g.eps, M, D, b.Y, s), "ln1");
     {
