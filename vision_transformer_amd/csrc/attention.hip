@@ -637,6 +637,18 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
+    // Row sums: with hd 64 a lane adds its rounded weights with packed dot
+    // products (VALU); with hd 32, where the softmax's VALU work outweighs
+    // the MFMAs twice over, an MFMA of the weights against a block of ones
+    // forms them (every accumulator slot of a lane then holds its query's
+    // sum over all the keys of both lane groups).
+    constexpr bool kMfmaSum = HD == 32;
+    f32x16 lsum;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lsum[i] = 0.0f;
+    Chunk ones;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ones.w[i] = pack2<T>(1.0f, 1.0f);
 
 #pragma unroll
     for (int s2 = 0; s2 < STAGES - 1; ++s2)
@@ -707,6 +719,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
             const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
             m_run = m_new;
             l_run *= alpha;
+            if constexpr (kMfmaSum) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) lsum[i] *= alpha;
+            }
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -725,18 +741,19 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
                     const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[j][8 * st + 2 * e], scale_log2, neg_m));
                     const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[j][8 * st + 2 * e + 1], scale_log2, neg_m));
                     pb.w[e] = pack2<T>(p0, p1);
-                    l_run = sum2<T>(pb.w[e], l_run); // the rounded weights the MFMA uses
+                    if constexpr (!kMfmaSum) l_run = sum2<T>(pb.w[e], l_run); // the rounded weights
                 }
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const int r = db * 32 + l32;
                     mfma_chunk<T>(o[db], sV[stg][r][(2 * (2 * j + st) + g) ^ swz<VCH>(r)], pb);
                 }
+                if constexpr (kMfmaSum) mfma_chunk<T>(lsum, ones, pb);
             }
         }
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = kMfmaSum ? lsum[0] : l_run + __shfl_xor(l_run, 32, 64);
     if (piece) {
         // half of the keys: the unnormalised partial, [HD] o then (max, sum)
         if (qrow < N) {
