@@ -146,27 +146,30 @@ def sources_hash(files):
     return h.hexdigest()[:16]
 
 
-# kernels that share one device instantiation: (index, count) of each one's dispatches in the
-# repeating launch order (every layer launches the out projection, then the down projection)
-SHARED_DISPATCH = {"out_gemm": (0, 2), "down_gemm": (1, 2)}
+# kernels that share one device instantiation: the kernel whose dispatch comes right before each
+# of theirs (copies aside) in a layer: the out projection follows attention, the down projection
+# follows the up projection (dispatches after anything else, such as the back-to-back launches
+# of one kernel alone, are left out)
+SHARED_DISPATCH = {"out_gemm": r"attention_lds_kernel", "down_gemm": r"gemm_lds_kernel.*Li1ELb0EEEv"}
 
 
-def counter_means(path, counter, share=None):
+def counter_means(path, counter, follows=None):
     """{kernel name: (mean counter value, dispatches)} from a rocprofv3 counter csv; with
-    share = (index, count) only every count-th dispatch of a kernel, starting at index."""
-    rows = {}
+    `follows` (a pattern) only the dispatches whose preceding dispatch, copies aside, is of a
+    kernel matching it."""
+    seq = []
     with open(path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] == counter:
-                rows.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
-    out = {}
-    for k, vals in rows.items():
-        vals.sort()
-        if share is not None:
-            vals = vals[share[0]::share[1]]
-        if vals:
-            out[k] = (sum(v for _, v in vals) / len(vals), len(vals))
-    return out
+                seq.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    seq.sort()
+    out, prev = {}, None
+    for _, k, v in seq:
+        if follows is None or (prev is not None and re.search(follows, prev.split("(")[0])):
+            out.setdefault(k, []).append(v)
+        if "copy" not in k.split("(")[0].lower():
+            prev = k
+    return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
 
 
 SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU",
@@ -234,10 +237,11 @@ def write_counters(dominant, fetch_csv, write_csv, out_txt):
     print("\n".join(lines))
 
 
-def read_traffic(dominant, workload):
+def read_traffic(dominant, workload, path=None):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if there is none or the kernel changed since."""
-    path = os.path.join(ROOT, "profiles", f"{dominant}_{workload}_counters.txt")
+    summary (or the summary at `path`), or None if there is none or the
+    kernel changed since."""
+    path = path or os.path.join(ROOT, "profiles", f"{dominant}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
