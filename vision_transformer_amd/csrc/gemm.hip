@@ -176,13 +176,6 @@ template <int EPI> __device__ __forceinline__ float epi_act(float v) {
     else return v;
 }
 
-// Epilogue of one workgroup tile: v = accumulator + bias, then the EPI
-// operation.  Each wave stages one MI-row block of its accumulators at a time
-// through a private LDS area (MI x (WN + 4) fp32) and reads it back so that
-// every lane owns 8 consecutive columns of one row: loads and stores of the
-// outputs are then 16-byte, row-contiguous vectors instead of per-element
-// accesses.  The V part of the QKV projection is read back transposed (8
-// consecutive rows of one column) because V is stored transposed per head.
 // The residual rows the RESID epilogue updates when they were not prefetched
 // at kernel start (NZ == 0): ZD row blocks of the wave's tile in flight, each
 // lane holding its 8 columns of NPASS rows per block.  request(f) asks for
@@ -214,6 +207,13 @@ template <int EPI, int NZ, int FM, int MI, int WN> struct ZRows {
     }
 };
 
+// Epilogue of one workgroup tile: v = accumulator + bias, then the EPI
+// operation.  Each wave stages one MI-row block of its accumulators at a time
+// through a private LDS area (MI x (WN + 4) fp32) and reads it back so that
+// every lane owns 8 consecutive columns of one row: loads and stores of the
+// outputs are then 16-byte, row-contiguous vectors instead of per-element
+// accesses.  The V part of the QKV projection is read back transposed (8
+// consecutive rows of one column) because V is stored transposed per head.
 // Everything the epilogue reads from global memory besides the accumulators
 // was requested at kernel start (epi_prefetch), except for the residual rows
 // of tiles too wide to hold them in registers: those are requested one row
