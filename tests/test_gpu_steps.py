@@ -173,6 +173,22 @@ def test_qkv_rope(gpu_lib, dtype, case):
     dict(B=1, H=2, N=1 + 4 * 300, hd=32, mode=1, p=1, S=300),
 ])
 def test_attention(gpu_lib, dtype, case):
+    _attention_case(dtype, case)
+
+
+@pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=2, N=1 + 16 * 256, hd=64, mode=1, p=1, S=256),
+    dict(B=1, H=1, N=4096, hd=32, mode=0, p=0, S=0),
+])
+def test_attention_long_keys(gpu_lib, dtype, case):
+    """From 4096 keys on, the 16-bit kernel issues its tile loads from
+    inline assembly: a block-causal 4097-token clip with its CLS row (split
+    halves, prefix runs) and a full-attention hd-32 case."""
+    _attention_case(dtype, case)
+
+
+def _attention_case(dtype, case):
     from vision_transformer_amd import vitenc as V
     say(f"attention dtype={dtype} {case}")
     rng = np.random.default_rng(case["N"])

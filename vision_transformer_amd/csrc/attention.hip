@@ -39,6 +39,7 @@ constexpr int BQ = 128;   // queries per workgroup
 constexpr int BKV = 64;   // keys per tile
 constexpr float kRescale = 8.0f; // log2 headroom before the running max moves
 constexpr int kStages = 4;  // LDS ring depth of the direct-to-LDS kernel
+constexpr int kDeepKeys = 4096; // key count from which the tile loads come from inline assembly
 constexpr int kLdsWaves = 4; // waves (32 queries each) per workgroup, hd 64
 
 // acc + lo + hi of a dword holding two 16-bit values (one packed dot product
@@ -367,6 +368,20 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(const T *__restr
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, Chunk *dst, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, voff, soff, 0, 0);
 }
+// The same load from inline assembly (M0 carries the LDS address; nothing
+// else in the kernel keeps a value in M0).  The compiler does not count
+// these loads: with them and a compiler-visible wait for the Q fragments
+// before the key loop, the loop carries no wait of the compiler's own, only
+// the kernel's vm_wait for the tile it is about to read.  (With the builtin
+// the compiler cannot tell the ring stages apart and waits for every load in
+// flight, the newest tile's included, before each tile's first fragment
+// reads.)
+__device__ __forceinline__ void load_lds16_asm(__amdgpu_buffer_rsrc_t rs, Chunk *dst, uint32_t voff, uint32_t soff) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(const lds_void_t *)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff), "s"(rs),
+                 "s"(soff)
+                 : "memory");
+}
 __device__ __forceinline__ int key_perm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // Prefix (CLS) query rows.  They see every key in both masks (the CLS row is
@@ -518,7 +533,9 @@ struct TileOrder {
     uint16_t job[kMaxJobs]; // bits 0-13 query tile; bits 14-15: 0 all keys, 1 first half, 2 second half
 };
 
-template <typename T, int HD, int STAGES, int NWV>
+// DEEP: the tile loads from inline assembly (load_lds16_asm), for long key
+// sequences, where the ring then keeps STAGES - 1 tiles in flight.
+template <typename T, int HD, int STAGES, int NWV, bool DEEP>
 __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                     const T *__restrict__ Vt, int N, int H, int ldv,
                                                                     int causal, int p, int S, int q_begin,
@@ -600,6 +617,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
 #pragma unroll
     for (int s2 = 0; s2 < QCH / 2; ++s2)
         qf[s2] = qrow < N ? load_chunk(Qb + (int64_t)qrow * HD + (2 * s2 + g) * KPC) : zero_chunk();
+    if constexpr (DEEP) __builtin_amdgcn_s_waitcnt(0xF70); // vmcnt(0): the Q fragments have landed
 
     // per-lane byte offsets of the tile loads (the tile's key offset goes in
     // the scalar offset)
@@ -618,11 +636,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
         const uint32_t koff = (uint32_t)(kt * BKV) * HD * (uint32_t)sizeof(T);
         const uint32_t voff = (uint32_t)(kt * BKV) * (uint32_t)sizeof(T);
 #pragma unroll
-        for (int j = 0; j < K_INST; ++j)
-            load_lds16(rsk, &sK[stage][(wave * K_INST + j) * KRI][0], vk[j], koff);
+        for (int j = 0; j < K_INST; ++j) {
+            if constexpr (DEEP) load_lds16_asm(rsk, &sK[stage][(wave * K_INST + j) * KRI][0], vk[j], koff);
+            else load_lds16(rsk, &sK[stage][(wave * K_INST + j) * KRI][0], vk[j], koff);
+        }
 #pragma unroll
-        for (int j = 0; j < V_INST; ++j)
-            load_lds16(rsv, &sV[stage][(wave * V_INST + j) * VRI][0], vv[j], voff);
+        for (int j = 0; j < V_INST; ++j) {
+            if constexpr (DEEP) load_lds16_asm(rsv, &sV[stage][(wave * V_INST + j) * VRI][0], vv[j], voff);
+            else load_lds16(rsv, &sV[stage][(wave * V_INST + j) * VRI][0], vv[j], voff);
+        }
     };
     auto wait_tile = [&](int later) {
         if (later >= 2) vm_wait<(STAGES > 3 ? 2 * PER : 0)>();
@@ -1020,10 +1042,19 @@ hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, 
     // grid y: the query-tile jobs, then (prefix rows x runs of keys) prefix jobs
     const int jobs = ord.n > 0 ? ord.n : ntq, runs = (int)cdiv(N, kPrefixKeys);
     dim3 grid((unsigned)(B * H), (unsigned)(jobs + qb * runs));
-    hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV>), grid, dim3(64 * NWV), 0, s,
-                       reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
-                       reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part, jobs,
-                       scratch, reinterpret_cast<T *>(O));
+    // measured: the inline-assembly tile loads pay from about 4096 keys on (a
+    // 4097-token clip 0.4 % faster per encode, an 18432-token one 3.5-6 %) and
+    // cost 1 % per encode at 2048 keys
+    if (N >= kDeepKeys)
+        hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV, true>), grid, dim3(64 * NWV), 0, s,
+                           reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
+                           reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part, jobs,
+                           scratch, reinterpret_cast<T *>(O));
+    else
+        hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages, NWV, false>), grid, dim3(64 * NWV), 0, s,
+                           reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
+                           reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part, jobs,
+                           scratch, reinterpret_cast<T *>(O));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = ord.n > 0 ? (int64_t)B * H * ord.nslots * BQL * (HD / 4) : 0;
