@@ -525,11 +525,14 @@ __device__ __forceinline__ void prefix_run(const T *__restrict__ Q, const T *__r
 // When the largest key count is at least twice the smallest, a tile is split
 // in two when its key tiles exceed a third of the largest count: each half
 // writes its unnormalised partial (o, running max, running sum) to scratch and
-// merge_kernel combines the two.  Jobs run largest first.  n = 0: no
-// split, tiles in reverse order (the heaviest last tiles first), one
-// workgroup each.
+// merge_kernel combines the two.  Tiles of equal cost (no mask, or a single
+// frame) split the same way when their grid leaves a last round of
+// workgroups less than half full: the last tiles of every (item, head) then
+// run as halves, so the last round holds half tiles.  Jobs run largest
+// first.  n = 0: no split, tiles in reverse order (the heaviest last tiles
+// first), one workgroup each.
 constexpr int kMaxJobs = 480;
-constexpr int kSplitMaxWorkgroups = 1024; // above this the dispatcher balances the tiles by itself
+constexpr int kSplitMaxWorkgroups = 1024; // block-causal: above this the dispatcher balances the tiles by itself
 constexpr int kSplitMinKeyTiles = 8;
 struct TileOrder {
     int n;      // jobs (the grid's y extent), 0 when nothing is split
@@ -950,25 +953,46 @@ inline int tile_key_tiles(int q0, int bq, int N, int causal, int p, int S) {
     return (int)(cdiv(hi, BKV) - lo / BKV);
 }
 
+// Workgroups of the direct-to-LDS kernel resident at once: 256 CUs, three
+// per CU at hd 64 (48 KB of LDS, 156 VGPRs) and at hd 32 (32 KB, 130 VGPRs).
+// A constant, so that the scratch size a call is planned with never depends
+// on the device it is asked on.
+constexpr int kLdsSlots = 256 * 3;
+
 // The TileOrder of a 16-bit attention call (bq queries per tile); returns
-// false (ord.n = 0) when no tile is split.
+// false (ord.n = 0) when no tile is split.  Two cases split tiles:
+//  - block-causal, grid of at most kSplitMaxWorkgroups: the late tiles
+//    (above a third of the largest key count) run as two halves each;
+//  - tiles of equal cost whose grid exceeds the resident slots and leaves
+//    its last round less than half full (the 18432-token clip: 3168
+//    workgroups on 768 slots, a last round of 96): the last k tiles of every
+//    (item, head) run as halves, k the fewest that move every whole tile
+//    into the full rounds, so the last round holds half tiles only.
 inline bool plan_tile_order(int B, int N, int H, int causal, int p, int S, int bq, TileOrder &ord) {
     ord.n = 0;
     ord.qs = ord.nslots = 0;
     const int qb = query_begin(N, p), T = (int)cdiv(N - qb, bq);
-    if (!causal || T < 4 || (int64_t)B * H * T > kSplitMaxWorkgroups) return false;
+    const int64_t tiles = (int64_t)B * H * T;
     int cnt[kMaxJobs];
-    if (T > kMaxJobs) return false;
+    if (T < 4 || T > kMaxJobs) return false;
     int maxn = 0, minn = 1 << 30;
     for (int qt = 0; qt < T; ++qt) {
         cnt[qt] = tile_key_tiles(qb + qt * bq, bq, N, causal, p, S);
         maxn = cnt[qt] > maxn ? cnt[qt] : maxn;
         minn = cnt[qt] < minn ? cnt[qt] : minn;
     }
-    if (maxn < 2 * minn) return false; // tiles of alike cost (a single frame): nothing to balance
-    int qs = T; // split: the run of last tiles above the threshold (block-causal counts never fall)
-    while (qs > 0 && cnt[qs - 1] >= kSplitMinKeyTiles && 3 * cnt[qs - 1] > maxn) --qs;
-    if (qs == T || T + (T - qs) > kMaxJobs) return false;
+    int qs = T; // split: the tiles qs .. T-1
+    if (causal) {
+        if (tiles > kSplitMaxWorkgroups) return false;
+        if (maxn < 2 * minn) return false; // tiles of alike cost (a single frame): nothing to balance
+        // the run of last tiles above the threshold (block-causal counts never fall)
+        while (qs > 0 && cnt[qs - 1] >= kSplitMinKeyTiles && 3 * cnt[qs - 1] > maxn) --qs;
+    } else {
+        const int64_t rem = tiles % kLdsSlots;
+        if (tiles <= kLdsSlots || rem == 0 || 2 * rem >= kLdsSlots || minn < kSplitMinKeyTiles) return false;
+        qs = T - (int)cdiv(rem, (int64_t)B * H);
+    }
+    if (qs <= 0 || qs == T || T + (T - qs) > kMaxJobs) return false;
     // jobs with their key-tile counts, sorted largest first (ties: later tile first)
     int njob = 0, size[kMaxJobs];
     for (int qt = T - 1; qt >= 0; --qt) {
