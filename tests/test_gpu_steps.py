@@ -189,16 +189,19 @@ def test_attention_long_keys(gpu_lib, dtype, case):
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
-@pytest.mark.parametrize("B,H,N,hd", [(1, 49, 2048, 64), (1, 49, 2048, 32), (1, 25, 4096, 64)])
-def test_attention_last_round_split(gpu_lib, dtype, B, H, N, hd):
+@pytest.mark.parametrize("B,H,N,hd,p", [(1, 49, 2048, 64, 0), (1, 49, 2048, 32, 0), (1, 25, 4096, 64, 0),
+                                          (1, 25, 4097, 64, 1)])
+def test_attention_last_round_split(gpu_lib, dtype, B, H, N, hd, p):
     """Full attention whose grid of equal-cost query tiles exceeds the 768
     resident workgroups by a nearly empty last round (49 heads x 16 tiles =
     784, 25 x 32 = 800): the last tile or two of every head run as two
     halves over the keys and are merged.  Every row of the last two query
     tiles of each head and a sample of the other rows against the oracle;
-    the 4096-key case takes the inline-assembly tile loads."""
+    the 4096-key cases take the inline-assembly tile loads, and the
+    4097-token one has a CLS row, whose runs of keys the same merge launch
+    combines."""
     from vision_transformer_amd import vitenc as V
-    say(f"attention last-round split dtype={dtype} B={B} H={H} N={N} hd={hd}")
+    say(f"attention last-round split dtype={dtype} B={B} H={H} N={N} hd={hd} p={p}")
     rng = np.random.default_rng(N + H)
     q = rng.standard_normal((B, H, N, hd)).astype(np.float32)
     k = rng.standard_normal((B, H, N, hd)).astype(np.float32)
@@ -206,12 +209,13 @@ def test_attention_last_round_split(gpu_lib, dtype, B, H, N, hd):
     ldv = (N + 63) // 64 * 64
     vt = np.zeros((B, H, hd, ldv), np.float32)
     vt[..., :N] = v.transpose(0, 1, 3, 2)
-    O = V.op_attention(dtype, dev(q, dtype), dev(k, dtype), dev(vt, dtype), attn_mode=0, n_prefix=0,
+    O = V.op_attention(dtype, dev(q, dtype), dev(k, dtype), dev(vt, dtype), attn_mode=0, n_prefix=p,
                        tokens_per_frame=0)
     torch.cuda.synchronize()
     g = to_np(O)
     qe, ke, ve = exact(q, dtype), exact(k, dtype), exact(v, dtype)
-    rows = np.concatenate([np.sort(rng.choice(N - 256, 48, replace=False)), np.arange(N - 256, N)])
+    rows = np.concatenate([np.arange(p), np.sort(p + rng.choice(N - 256 - p, 48, replace=False)),
+                           np.arange(N - 256, N)])
     tol = {W.DTYPE_BF16: 1.5e-2, W.DTYPE_F16: 2e-3}[dtype]
     for b in range(B):
         for h in range(H):
