@@ -135,8 +135,18 @@ def test_sensitised_small_clip_bf16(gpu_lib, name):
 def test_prefix_rows_apart(gpu_lib, dtype):
     """One clip of CLS + 128 patch tokens (LeVJEPA, 2 frames of 8 x 8): the
     out, up and down projections compute the 128 patch rows on the tile grid
-    and the CLS row apart."""
+    and the CLS row with the row kernel (the tile configuration of 128 rows
+    has no prefix-row path)."""
     _parity(W.CONFIGS[4].replace(frames=2, height=128, width=128, n_layer=4, dtype=dtype))
+
+
+def test_prefix_row_in_tile_kernel_f16(gpu_lib):
+    """The 4097-token block-causal clip (CLS + 4096 patches) in fp16, two
+    layers: the CLS row of the out, up and down projections rides along in
+    their tile kernels (each workgroup adds its share of the columns from the
+    weight slabs it holds), which the bf16 case of the full token count
+    covers as well."""
+    _parity(W.CONFIGS[4].replace(dtype=W.DTYPE_F16), n_layer=2)
 
 
 def test_layer_scale(gpu_lib):

@@ -39,6 +39,18 @@ hipError_t run_block(const BlockGeom &g, const BlockBufs &b, const vitenc_block_
         EpiArgs em = ep;
         if (em.out) em.out = static_cast<char *>(em.out) + pre * em.ldo * es;
         if (em.Z) em.Z += pre * em.ldz;
+        if (pre == 1) {
+            // a single prefix row rides along in the tile kernel, which holds
+            // every weight slab in LDS anyway (where its configuration has that
+            // path; otherwise the row kernel below)
+            EpiArgs ef = em;
+            ef.pre_a = A;
+            ef.pre_out = ep.out;
+            ef.pre_z = ep.Z;
+            const hipError_t e1 = launch_gemm(g.dtype, epi, static_cast<const char *>(A) + lda * es, lda, W, K,
+                                              M - 1, N, K, ef, s);
+            if (e1 != hipErrorNotSupported) return e1;
+        }
         // the prefix rows first: their kernel reads the whole weight matrix
         // once, which leaves it in the last-level cache for the tile grid
         hipError_t e2 = launch_gemm_rows(g.dtype, epi, A, lda, W, K, pre, N, K, ep, s);

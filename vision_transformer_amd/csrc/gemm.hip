@@ -746,11 +746,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void *dst
                  : "memory");
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI, bool WQ>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
-                                                                     const void *__restrict__ W, int64_t ldw, int M,
-                                                                     int N, int K, int tiles_n, int a_bytes,
-                                                                     int b_bytes, int s_bytes, EpiArgs ep) {
+// Longest prefix row (K) the tile kernel takes beside its grid (EpiArgs::pre_a)
+constexpr int kPreMaxK = 4096;
+
+template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI, bool WQ, bool PRE>
+__device__ __forceinline__ void gemm_lds_body(const T *__restrict__ A, int64_t lda, const void *__restrict__ W,
+                                              int64_t ldw, int M, int N, int K, int tiles_n, int a_bytes,
+                                              int b_bytes, int s_bytes, const EpiArgs &ep) {
     constexpr int KPC = Elem<T>::kPerChunk;
     constexpr int BK = NCH * KPC;
     constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -770,7 +772,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     static_assert(!WQ || (std::is_same<T, bf16_t>::value && MI == 32 && NCH == 8 && 2 * BN <= 1024),
                   "8-bit weights: bf16 activations, 32x32 MFMAs, 64-k slabs");
 
-    __shared__ Chunk lds[STAGES * STAGE_CH];
+    // PRE: the prefix row of A, K values, after the ring
+    constexpr int kPreOff = STAGES * STAGE_CH, kPreChunks = PRE ? kPreMaxK / KPC : 0;
+    static_assert(!PRE || ((EPI == EPI_RESID || EPI == EPI_GELU) && !WQ && MI == 32), "prefix row: RESID / GELU");
+    __shared__ Chunk lds[STAGES * STAGE_CH + kPreChunks];
     auto lA = [&](int stage, int r, int c) -> Chunk & { return lds[stage * STAGE_CH + r * NCH + c]; };
     auto lW = [&](int stage, int r, int c) -> Chunk & { return lds[stage * STAGE_CH + BM * NCH + r * WCH + c]; };
     auto lS = [&](int stage) { return reinterpret_cast<const uint16_t *>(&lds[stage * STAGE_CH + BM * NCH + BN * WCH]); };
@@ -956,6 +961,43 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     const int kb0 = (int)((int64_t)split * nk_all / ep.splits);
     const int nk = (int)((int64_t)(split + 1) * nk_all / ep.splits) - kb0;
     const int kbase = kb0 * BK;
+    // PRE: this workgroup's share of the prefix row's N columns is cpw
+    // columns from n0 + tm * cpw (the tiles of one column block split its BN
+    // columns; the launcher checks that they divide evenly), cpw / NW per
+    // wave; lane l takes column l / NCH of its wave's share and, in every
+    // slab, chunk l % NCH of that column's weights and of the prefix row.
+    // The row itself is fetched into LDS before the first slab, so the first
+    // slab wait covers it.
+    float pre_acc = 0.0f;
+    int pre_r = 0;
+    bool pre_live = false;
+    if constexpr (PRE) {
+        const int tiles_m = (M + BM - 1) / BM, cpw = BN / tiles_m, cpwv = cpw / NW;
+        const int j = lane / NCH;
+        pre_live = j < cpwv;
+        pre_r = tm * cpw + wave * cpwv + (pre_live ? j : 0);
+        const __amdgpu_buffer_rsrc_t rsp =
+            __builtin_amdgcn_make_buffer_rsrc((void *)ep.pre_a, 0, K * (int)sizeof(T), 0x00020000);
+        for (int b = wave; b * 64 < K / KPC; b += NW)
+            dma16(rsp, &lds[kPreOff + b * 64], (uint32_t)lane * 16u, (uint32_t)b * 1024u);
+    }
+    // (read at the top of a slab's K step, added at its end, so that the LDS
+    // round trip hides under the step's MFMAs)
+    Chunk pre_w, pre_a;
+    auto pre_read = [&](int stg, int kt) {
+        if constexpr (PRE) {
+            const int c = lane % NCH;
+            pre_w = lW(stg, pre_r, c ^ swz<NCH>(pre_r));
+            pre_a = lds[kPreOff + (kbase / KPC) + kt * NCH + c];
+        }
+    };
+    auto pre_add = [&]() {
+        if constexpr (PRE) {
+            const T *we = reinterpret_cast<const T *>(&pre_w), *ae = reinterpret_cast<const T *>(&pre_a);
+#pragma unroll
+            for (int e = 0; e < KPC; ++e) pre_acc = fmaf(to_f32(ae[e]), to_f32(we[e]), pre_acc);
+        }
+    };
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
         if (s < nk) issue(s, kbase + s * BK);
@@ -976,6 +1018,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
     for (int kt = 0; kt < nk; ++kt) {
         int nstage = stage + 1;
         if (nstage == STAGES) nstage = 0;
+        pre_read(stage, kt);
         if (kZEarly && kt == nk - 1) {
 #pragma unroll
             for (int f = 0; f < ZRows<EPI, kNZ, FM, MI, WN>::ZD; ++f)
@@ -1004,6 +1047,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
                 }
             }
         }
+        pre_add();
         stage = nstage;
         if (KSUB & 1) {
             // odd sub-step count: the next slab's first fragments sit in the
@@ -1012,6 +1056,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
             for (int fm = 0; fm < FM; ++fm) { Chunk t = a0[fm]; a0[fm] = a1[fm]; a1[fm] = t; }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) { Chunk t = b0[fn]; b0[fn] = b1[fn]; b1[fn] = t; }
+        }
+    }
+    if constexpr (PRE) {
+        // sum over the NCH lanes of each column, then the epilogue of the row
+#pragma unroll
+        for (int o = NCH / 2; o >= 1; o >>= 1) pre_acc += __shfl_xor(pre_acc, o, 64);
+        const int col = n0 + pre_r;
+        if (pre_live && lane % NCH == 0 && col < N) {
+            const float v = pre_acc + (ep.bias ? ep.bias[col] : 0.0f);
+            if constexpr (EPI == EPI_RESID) ep.pre_z[col] += ep.ls ? ep.ls[col] * v : v;
+            else reinterpret_cast<T *>(ep.pre_out)[col] = from_f32<T>(gelu_erf(v));
         }
     }
     __syncthreads();
@@ -1027,6 +1082,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__
                                                             wn * WN, M, N, ep,
                                                             ep.splits > 1 ? ep.sk_part + (int64_t)split * M * N : nullptr,
                                                             zr, kZEarly && nk > 0);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI, bool WQ>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_kernel(const T *__restrict__ A, int64_t lda,
+                                                                     const void *__restrict__ W, int64_t ldw, int M,
+                                                                     int N, int K, int tiles_n, int a_bytes,
+                                                                     int b_bytes, int s_bytes, EpiArgs ep) {
+    gemm_lds_body<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, WQ, false>(A, lda, W, ldw, M, N, K, tiles_n, a_bytes,
+                                                                        b_bytes, s_bytes, ep);
+}
+// the same with one prefix row beside the tile grid (EpiArgs::pre_a)
+template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_lds_pre_kernel(const T *__restrict__ A, int64_t lda,
+                                                                         const void *__restrict__ W, int64_t ldw,
+                                                                         int M, int N, int K, int tiles_n,
+                                                                         int a_bytes, int b_bytes, EpiArgs ep) {
+    gemm_lds_body<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, false, true>(A, lda, W, ldw, M, N, K, tiles_n, a_bytes,
+                                                                          b_bytes, 0, ep);
 }
 
 // Split-K where the output tiles fill at most half of the per_cu workgroup
@@ -1131,7 +1204,8 @@ hipError_t launch_t(const void *A, int64_t lda, const void *W, int64_t ldw, int 
     return launch_reduce<T, EPI>(e.splits, M, N, e, s);
 }
 
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, bool WQ = false>
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, bool WQ = false,
+          bool PRE = false>
 hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K, const EpiArgs &ep,
                       hipStream_t s) {
     const int tiles_n = (int)cdiv(N, BN), tiles_m = (int)cdiv(M, BM);
@@ -1139,11 +1213,26 @@ hipError_t launch_lds(const void *A, int64_t lda, const void *W, int64_t ldw, in
     EpiArgs e = ep;
     e.splits = splits_with(EPI, (int64_t)tiles_m * tiles_n, K / (NCH * Elem<T>::kPerChunk), lds_per_cu(BM, NCH, STAGES),
                            kLdsMinSteps, M, N, K, ep);
-    hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, WQ>),
-                       dim3((unsigned)(tiles_m * tiles_n * e.splits)), dim3(64 * WGM * WGN), 0, s,
-                       reinterpret_cast<const T *>(A), lda, W, ldw, M, N, K, tiles_n,
-                       (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * wbytes),
-                       WQ ? (int)((int64_t)(K / 64) * N * 2) : 0, e);
+    if constexpr (PRE) {
+        // the tiles of a column block split its BN columns evenly, each wave's
+        // share fits its lanes, and the K range is whole
+        constexpr int NW = WGM * WGN;
+        const int cpw = tiles_m > 0 && BN % tiles_m == 0 ? BN / tiles_m : 0;
+        if (e.splits != 1 || K > kPreMaxK || cpw == 0 || cpw % NW != 0 || (cpw / NW) * NCH > 64 ||
+            (uintptr_t)ep.pre_a % 16 != 0 || (EPI == EPI_RESID ? !ep.pre_z : !ep.pre_out))
+            return hipErrorNotSupported;
+    }
+    if constexpr (PRE)
+        hipLaunchKernelGGL((gemm_lds_pre_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI>),
+                           dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WGM * WGN), 0, s,
+                           reinterpret_cast<const T *>(A), lda, W, ldw, M, N, K, tiles_n,
+                           (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * wbytes), e);
+    else
+        hipLaunchKernelGGL((gemm_lds_kernel<T, BM, BN, WGM, WGN, NCH, STAGES, MI, EPI, WQ>),
+                           dim3((unsigned)(tiles_m * tiles_n * e.splits)), dim3(64 * WGM * WGN), 0, s,
+                           reinterpret_cast<const T *>(A), lda, W, ldw, M, N, K, tiles_n,
+                           (int)((int64_t)M * lda * sizeof(T)), (int)((int64_t)N * ldw * wbytes),
+                           WQ ? (int)((int64_t)(K / 64) * N * 2) : 0, e);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess || e.splits == 1) return err;
     return launch_reduce<T, EPI>(e.splits, M, N, e, s);
@@ -1195,6 +1284,23 @@ hipError_t launch_align(const void *A, int64_t lda, const void *W, int64_t ldw, 
     // tile of overhang) below 2 GiB
     const bool small = ((int64_t)M + 256) * lda * (int64_t)sizeof(T) < INT32_MAX &&
                        ((int64_t)N + 256) * ldw * (int64_t)sizeof(T) < INT32_MAX;
+    if (ep.pre_a) {
+        if constexpr (!std::is_same<T, float>::value && (EPI == EPI_RESID || EPI == EPI_GELU)) {
+            if (fast && small && !ep.wscale && !ep.kwrap) {
+                switch (pick_tile(M, N, true, false)) {
+                case TILE_256x256:
+                    return launch_lds<T, EPI, 256, 256, 2, 4, 8, 2, 32, false, true>(A, lda, W, ldw, M, N, K, ep, s);
+                case TILE_128x128_DEEP:
+                    if (K % 128 == 0)
+                        return launch_lds<T, EPI, 128, 128, 2, 2, 16, 2, 32, false, true>(A, lda, W, ldw, M, N, K,
+                                                                                          ep, s);
+                    break;
+                default: break;
+                }
+            }
+        }
+        return hipErrorNotSupported;
+    }
     if constexpr (std::is_same<T, bf16_t>::value) {
         if (ep.wscale) {
             // 8-bit weights: the direct-to-LDS kernel only (conditions checked by the caller)

@@ -59,6 +59,17 @@ struct EpiArgs {
     float *sk_part = nullptr;
     int64_t sk_part_floats = 0;
     int splits = 1; // set by the launcher
+    // One prefix row (a CLS token) beside the tile grid: when pre_a is set,
+    // the tile kernel also forms pre_a [K] times W^T.  Its workgroups split
+    // the N columns, each adding its share from the weight slabs it holds in
+    // LDS anyway, and the row goes through the same GELU / residual epilogue
+    // into pre_out / pre_z (the output / residual row of the prefix token).
+    // RESID and GELU only, on the 256 x 256 and the 128-deep 128 x 128
+    // configurations, unsplit, K <= 4096; otherwise the launcher returns
+    // hipErrorNotSupported and launches nothing.
+    const void *pre_a = nullptr;
+    void *pre_out = nullptr;
+    float *pre_z = nullptr;
 };
 
 // Split-K scratch floats a GEMM of this shape can use (0: it does not split;
