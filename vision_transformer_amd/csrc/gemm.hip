@@ -748,6 +748,16 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const void *dst
 
 // Longest prefix row (K) the tile kernel takes beside its grid (EpiArgs::pre_a)
 constexpr int kPreMaxK = 4096;
+// acc + a.lo * b.lo + a.hi * b.hi for dwords holding two 16-bit values
+// (one packed dot product, fp32 accumulation)
+template <typename T> __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc);
+template <> __device__ __forceinline__ float dot2_acc<bf16_t>(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                           false);
+}
+template <> __device__ __forceinline__ float dot2_acc<f16_t>(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), acc, false);
+}
 
 template <typename T, int BM, int BN, int WGM, int WGN, int NCH, int STAGES, int MI, int EPI, bool WQ, bool PRE>
 __device__ __forceinline__ void gemm_lds_body(const T *__restrict__ A, int64_t lda, const void *__restrict__ W,
@@ -993,9 +1003,8 @@ __device__ __forceinline__ void gemm_lds_body(const T *__restrict__ A, int64_t l
     };
     auto pre_add = [&]() {
         if constexpr (PRE) {
-            const T *we = reinterpret_cast<const T *>(&pre_w), *ae = reinterpret_cast<const T *>(&pre_a);
 #pragma unroll
-            for (int e = 0; e < KPC; ++e) pre_acc = fmaf(to_f32(ae[e]), to_f32(we[e]), pre_acc);
+            for (int e = 0; e < 4; ++e) pre_acc = dot2_acc<T>(pre_a.w[e], pre_w.w[e], pre_acc);
         }
     };
 #pragma unroll
