@@ -282,6 +282,17 @@ def test_step_entry_point_refusals():
     # 3 heads: the prefix area (3 x 17 x 66 = 3366 floats) is padded to 3368
     assert S(1, 1, 4097, 3, 64, 1, 1, 256) == 3368 + 3 * 22 * 128 * 2 * 68
     assert S(1, 1, 4097, 16, 64, 1, 1, 4096) == pre                 # one frame: nothing to balance
+    # full attention beyond the 768 resident workgroups with a last round less
+    # than half full: the last k query tiles of every head run as halves, k the
+    # fewest that leave only halves in the last round
+    assert S(1, 1, 2048, 49, 64, 0, 0, 0) == 49 * 1 * 128 * 2 * 68       # 784 tiles: 16 over, k = 1
+    assert S(1, 1, 2048, 49, 32, 0, 0, 0) == 49 * 1 * 128 * 2 * 36       # hd 32 alike
+    assert S(1, 1, 18432, 22, 64, 0, 0, 0) == 22 * 5 * 128 * 2 * 68      # 3168 tiles: 96 over, k = 5
+    assert S(1, 1, 2048, 48, 64, 0, 0, 0) == 0                           # 768 tiles: whole rounds
+    assert S(1, 1, 2048, 73, 64, 0, 0, 0) == 0                           # 1168: last round 400 of 768
+    assert S(1, 2, 2048, 16, 64, 0, 0, 0) == 0                           # the headline: one round
+    # with a CLS row: the prefix area (25 x 17 x 66 = 28050 floats, padded to 28052), then the halves
+    assert S(1, 1, 4097, 25, 64, 0, 1, 0) == 28052 + 25 * 2 * 128 * 2 * 68
     assert S(7, 1, 64, 1, 64, 0, 0, 0) == -1 and S(1, 1, 64, 1, 64, 2, 0, 0) == -1
     assert S(1, 1, 64, 1, 64, 1, 0, 0) == -1
     assert L.vitenc_op_attention(1, FAKE, FAKE, FAKE, 1, 257, 2, 64, 0, 1, 0, None, FAKE, None) == 3
