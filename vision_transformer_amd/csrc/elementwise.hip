@@ -376,7 +376,18 @@ __global__ __launch_bounds__(1024) void pool_kernel(const float *__restrict__ X,
         if (cls) {
             s = rg == 0 ? xb[d] : 0.0f;
         } else {
-            for (int n = n_prefix + rg; n < N; n += 64) s += xb[(int64_t)n * D + d];
+            // four independent partial sums, so that four row loads are in
+            // flight per step (fixed order: deterministic)
+            float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+            int n = n_prefix + rg;
+            for (; n + 192 < N; n += 256) {
+                s0 += xb[(int64_t)n * D + d];
+                s1 += xb[(int64_t)(n + 64) * D + d];
+                s2 += xb[(int64_t)(n + 128) * D + d];
+                s3 += xb[(int64_t)(n + 192) * D + d];
+            }
+            for (; n < N; n += 64) s0 += xb[(int64_t)n * D + d];
+            s = (s0 + s1) + (s2 + s3);
         }
     }
     part[rg][cx] = s;
