@@ -190,16 +190,17 @@ def test_attention_long_keys(gpu_lib, dtype, case):
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_BF16, W.DTYPE_F16])
 @pytest.mark.parametrize("B,H,N,hd,p", [(1, 49, 2048, 64, 0), (1, 49, 2048, 32, 0), (1, 25, 4096, 64, 0),
-                                          (1, 25, 4097, 64, 1)])
+                                          (1, 25, 4097, 64, 1), (2, 25, 2048, 64, 0)])
 def test_attention_last_round_split(gpu_lib, dtype, B, H, N, hd, p):
     """Full attention whose grid of equal-cost query tiles exceeds the 768
     resident workgroups by a nearly empty last round (49 heads x 16 tiles =
     784, 25 x 32 = 800): the last tile or two of every head run as two
     halves over the keys and are merged.  Every row of the last two query
     tiles of each head and a sample of the other rows against the oracle;
-    the 4096-key cases take the inline-assembly tile loads, and the
-    4097-token one has a CLS row, whose runs of keys the same merge launch
-    combines."""
+    the 4096-key cases take the inline-assembly tile loads, the 4097-token
+    one has a CLS row, whose runs of keys the same merge launch combines, and
+    the two-item one (2 x 25 x 16 = 800 tiles) splits the last tile of every
+    (item, head)."""
     from vision_transformer_amd import vitenc as V
     say(f"attention last-round split dtype={dtype} B={B} H={H} N={N} hd={hd} p={p}")
     rng = np.random.default_rng(N + H)
