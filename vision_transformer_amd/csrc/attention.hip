@@ -684,13 +684,33 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
     for (int s2 = 0; s2 < STAGES - 1; ++s2)
         if (s2 < ntiles) issue(s2, kt_begin + s2);
 
-    for (int t = 0; t < ntiles; ++t) {
+    // Lane byte offsets of the fragment reads within a stage (the swizzle
+    // depends on the row's low 4 bits only, so rows 32 apart share it); with
+    // the loop unrolled over the ring, the stage and the 32-row block are
+    // immediate offsets of the reads.  They pass through an empty asm once per
+    // tile, so that the compiler keeps one register per offset instead of a
+    // sum per stage.
+    uint32_t kofs[QCH / 2], vofs[4];
+#pragma unroll
+    for (int s2 = 0; s2 < QCH / 2; ++s2)
+        kofs[s2] = (uint32_t)(l32 * QCH + ((2 * s2 + g) ^ swz<QCH>(l32))) * (uint32_t)sizeof(Chunk);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        vofs[c] = (uint32_t)(l32 * VCH + ((2 * c + g) ^ swz<VCH>(l32))) * (uint32_t)sizeof(Chunk);
+    auto lds_chunk = [](const void *base, uint32_t off) __attribute__((always_inline)) {
+        return *reinterpret_cast<const Chunk *>(reinterpret_cast<const char *>(base) + off);
+    };
+    auto tile_step = [&](auto pos, int t) __attribute__((always_inline)) {
+        constexpr int stg = decltype(pos)::value;
         const int kt = kt_begin + t, kb = kt * BKV;
-        const int stg = t % STAGES;
+#pragma unroll
+        for (int i = 0; i < QCH / 2; ++i) asm("" : "+v"(kofs[i]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm("" : "+v"(vofs[i]));
         // tiles issued so far: 0 .. min(t + STAGES - 2, ntiles - 1)
         wait_tile(min(t + STAGES - 2, ntiles - 1) - t);
         // every wave is past tile t-1, so its stage can be refilled
-        if (t + STAGES - 1 < ntiles) issue((t + STAGES - 1) % STAGES, kt + STAGES - 1);
+        if (t + STAGES - 1 < ntiles) issue((stg + STAGES - 1) % STAGES, kt + STAGES - 1);
         if (kb + BKV > N) {
             // ragged last tile: V^T columns of keys >= N hold whatever follows
             // the last token in memory; make them zero
@@ -703,7 +723,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
             }
             __syncthreads();
         }
-        if (!(kb < w_hi && kb + BKV > w_lo)) continue;
+        if (!(kb < w_hi && kb + BKV > w_lo)) return;
         const bool need_mask = !(kb >= w_full_lo && kb + BKV <= w_full_hi);
 
         f32x16 sc[2];
@@ -713,7 +733,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
             for (int i = 0; i < 16; ++i) sc[j][i] = 0.0f;
             const int r = 32 * j + l32;
 #pragma unroll
-            for (int s2 = 0; s2 < QCH / 2; ++s2) mfma_chunk<T>(sc[j], sK[stg][r][(2 * s2 + g) ^ swz<QCH>(r)], qf[s2]);
+            for (int s2 = 0; s2 < QCH / 2; ++s2)
+                mfma_chunk<T>(sc[j], lds_chunk(&sK[stg][32 * j][0], kofs[s2]), qf[s2]);
         }
         float mx = -INFINITY;
         if (need_mask) {
@@ -774,12 +795,22 @@ __global__ __launch_bounds__(64 * NWV, 2) void attention_lds_kernel(const T *__r
                     if constexpr (!kMfmaSum) l_run = sum2<T>(pb.w[e], l_run); // the rounded weights
                 }
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const int r = db * 32 + l32;
-                    mfma_chunk<T>(o[db], sV[stg][r][(2 * (2 * j + st) + g) ^ swz<VCH>(r)], pb);
-                }
+                for (int db = 0; db < NDB; ++db)
+                    mfma_chunk<T>(o[db], lds_chunk(&sV[stg][32 * db][0], vofs[2 * j + st]), pb);
                 if constexpr (kMfmaSum) mfma_chunk<T>(lsum, ones, pb);
             }
+        }
+    };
+    static_assert(STAGES == 3 || STAGES == 4, "one copy of the tile step per ring stage");
+    for (int t = 0; t < ntiles; t += STAGES) {
+        tile_step(std::integral_constant<int, 0>{}, t);
+        if (t + 1 >= ntiles) break;
+        tile_step(std::integral_constant<int, 1>{}, t + 1);
+        if (t + 2 >= ntiles) break;
+        tile_step(std::integral_constant<int, 2>{}, t + 2);
+        if constexpr (STAGES == 4) {
+            if (t + 3 >= ntiles) break;
+            tile_step(std::integral_constant<int, 3 % STAGES>{}, t + 3);
         }
     }
 
