@@ -44,7 +44,10 @@ constexpr float kRescale = 8.0f; // log2 headroom before the running max moves
 // 0.3 % on 2 x 2048 tokens against four stages), at hd 32 four (the 8 KB
 // stages never limit occupancy; three measured 1.2 % slower per predictor call)
 template <int HD> constexpr int kStages = HD == 64 ? 3 : 4;
-constexpr int kDeepKeys = 4096; // key count from which the tile loads come from inline assembly
+// key count from which the tile loads come from inline assembly: at hd 64 from
+// 4096 keys (below that the builtin loads measured 1 % faster per encode), at
+// hd 32 always (the predictor's 2048-key calls 0.7 % faster per call)
+template <int HD> constexpr int kDeepKeys = HD == 64 ? 4096 : 0;
 constexpr int kLdsWaves = 4; // waves (32 queries each) per workgroup, hd 64
 
 // acc + lo + hi of a dword holding two 16-bit values (one packed dot product
@@ -1102,10 +1105,11 @@ hipError_t launch_t(const void *Q, const void *K, const void *Vt, int B, int N, 
     // grid y: the query-tile jobs, then (prefix rows x runs of keys) prefix jobs
     const int jobs = ord.n > 0 ? ord.n : ntq, runs = (int)cdiv(N, kPrefixKeys);
     dim3 grid((unsigned)(B * H), (unsigned)(jobs + qb * runs));
-    // measured: the inline-assembly tile loads pay from about 4096 keys on (a
-    // 4097-token clip 0.4 % faster per encode, an 18432-token one 3.5-6 %) and
-    // cost 1 % per encode at 2048 keys
-    if (N >= kDeepKeys)
+    // measured at hd 64: the inline-assembly tile loads pay from about 4096
+    // keys on (a 4097-token clip 0.4 % faster per encode, an 18432-token one
+    // 3.5-6 %) and cost 1 % per encode at 2048 keys; at hd 32 they pay at
+    // 2048 keys already
+    if (N >= kDeepKeys<HD>)
         hipLaunchKernelGGL((attention_lds_kernel<T, HD, kStages<HD>, NWV, true>), grid, dim3(64 * NWV), 0, s,
                            reinterpret_cast<const T *>(Q), reinterpret_cast<const T *>(K),
                            reinterpret_cast<const T *>(Vt), N, H, ldv, causal, p, S, qb, scale_log2, ord, part, jobs,
